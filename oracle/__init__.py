@@ -1,0 +1,9 @@
+"""CPU oracle for the Prox two-stage sparse SwiGLU FFN step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It is independent of
+the HIP library: the two share no code, and neither imports the other.
+"""
+from .prox_oracle import (Layer, build, dense, dequantize, forward,  # noqa: F401
+                          forward_batch, input_mask, proxy, quantize,
+                          rmsnorm, round_bf16, stack_forward, stage2, topk)
