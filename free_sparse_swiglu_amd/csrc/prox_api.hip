@@ -1,0 +1,370 @@
+// C ABI of libprox (declared in include/prox.h): argument checks, buffer
+// layout and the launch sequence of the Prox FFN step.
+//
+// Method: "Prox: Training-Free FFN Activation Sparsity via Approximate
+// Intermediate-Channel Salience in LLMs" (arXiv 2607.27591).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/prox.h"
+#include "prox_internal.h"
+
+struct prox_layer {
+  prox::Plan plan;
+  prox::Bufs bufs;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+prox_status fail(prox_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+prox_status fail(prox_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+prox_status hip_fail(hipError_t e, const char *what) {
+  return fail(PROX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+prox_status check_shape(const prox_shape *sh) {
+  if (!sh) return fail(PROX_EINVAL, "shape is NULL");
+  if (sh->d_model <= 0 || sh->d_ff <= 0 || sh->group_size <= 0 || sh->max_batch <= 0)
+    return fail(PROX_EINVAL, "shape sizes must be positive (d_model=%d d_ff=%d G=%d max_batch=%d)",
+                sh->d_model, sh->d_ff, sh->group_size, sh->max_batch);
+  if (sh->dtype != PROX_F32 && sh->dtype != PROX_BF16)
+    return fail(PROX_EINVAL, "unknown dtype %d", sh->dtype);
+  if (sh->d_model % sh->group_size != 0)
+    return fail(PROX_EINVAL, "d_model (%d) is not a multiple of group_size (%d)",
+                sh->d_model, sh->group_size);
+  if (sh->group_size != 64 && sh->group_size != 128 && sh->group_size != 256)
+    return fail(PROX_EUNSUPPORTED, "group_size must be 64, 128 or 256 (got %d)", sh->group_size);
+  const int dm_mult = sh->dtype == PROX_BF16 ? 512 : 256;
+  if (sh->d_model % dm_mult != 0)
+    return fail(PROX_EUNSUPPORTED, "d_model must be a multiple of %d for this dtype (got %d)",
+                dm_mult, sh->d_model);
+  if (sh->d_model > prox::kMaxDmodel)
+    return fail(PROX_EUNSUPPORTED, "d_model above %d is not supported (got %d)",
+                prox::kMaxDmodel, sh->d_model);
+  if (sh->d_ff > prox::kMaxDff)
+    return fail(PROX_EUNSUPPORTED, "d_ff above %d is not supported (got %d)", prox::kMaxDff,
+                sh->d_ff);
+  if (sh->max_batch > prox::kMaxBatch)
+    return fail(PROX_EUNSUPPORTED, "max_batch above %d is not supported (got %d)",
+                prox::kMaxBatch, sh->max_batch);
+  // Byte offsets inside the weight buffers are 32-bit.
+  const size_t esz = sh->dtype == PROX_BF16 ? 2 : 4;
+  if ((size_t)sh->d_ff * 2 * sh->d_model * esz >= (1ull << 32))
+    return fail(PROX_EUNSUPPORTED, "up/gate weights above 4 GiB are not supported");
+  return PROX_OK;
+}
+
+}  // namespace
+
+namespace prox {
+
+Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch) {
+  Plan p{};
+  p.d_model = d_model;
+  p.d_ff = d_ff;
+  p.G = G;
+  p.bf16 = bf16;
+  p.max_batch = max_batch;
+  p.esz = bf16 ? 2 : 4;
+  p.ngroups = d_model / G;
+  p.ntile = (d_ff + kTile - 1) / kTile;
+  p.nchunk = (p.ngroups + 3) / 4;
+  p.ncol = d_model / kDownCols;
+  int nrc = 512 / p.ncol;
+  if (nrc < 1) nrc = 1;
+  if (nrc > 64) nrc = 64;
+  p.nrc = nrc;
+  p.upgate_cap = 4096;
+  return p;
+}
+
+Layout make_layout(const Plan &p) {
+  Layout L{};
+  const size_t B = (size_t)p.max_batch;
+  const size_t wug = (size_t)p.d_ff * 2 * p.d_model * p.esz;
+  L.o_wd = align256(wug);
+  L.weights = align256(L.o_wd + (size_t)p.d_ff * p.d_model * p.esz);
+  const size_t pq = (size_t)p.ntile * p.d_model * kTileBytes;
+  L.o_psc = align256(pq);
+  L.proxy = align256(L.o_psc + (size_t)p.ntile * p.ngroups * 512 * sizeof(float));
+  size_t o = 0;
+  L.o_part = o;      o = align256(o + (size_t)p.ntile * p.nchunk * B * 512 * sizeof(float));
+  L.o_tile_cnt = o;  o = align256(o + (size_t)p.ntile * sizeof(unsigned));
+  L.o_sabs = o;      o = align256(o + B * p.d_ff * sizeof(float));
+  L.o_sel = o;       o = align256(o + B * p.d_ff * sizeof(int));
+  L.o_ssp = o;       o = align256(o + B * p.d_ff * sizeof(float));
+  L.o_uni = o;       o = align256(o + (size_t)p.d_ff * sizeof(int));
+  L.o_nuni = o;      o = align256(o + sizeof(int));
+  L.o_umask = o;     o = align256(o + (size_t)p.d_ff);
+  L.o_ypart = o;     o = align256(o + (size_t)p.nrc * B * p.d_model * sizeof(float));
+  L.o_col_cnt = o;   o = align256(o + (size_t)p.ncol * sizeof(unsigned));
+  L.o_xbuf = o;      o = align256(o + B * p.d_model * p.esz);
+  L.o_ybuf = o;      o = align256(o + B * p.d_model * p.esz);
+  L.workspace = o;
+  return L;
+}
+
+}  // namespace prox
+
+namespace {
+
+// Stage 1, top-k and Stage 2 for `batch` tokens; writes y.
+prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau,
+                        int k, void *y, float *resid, hipStream_t s) {
+  const prox::Plan &p = L->plan;
+  const prox::Bufs &b = L->bufs;
+  hipError_t e;
+  if (k == 0) {
+    e = prox::launch_zero_y(p, y, batch, s);
+    if (e != hipSuccess) return hip_fail(e, "zero output");
+    return PROX_OK;  // y = 0 adds nothing to the residual
+  }
+  if ((e = prox::launch_proxy(p, b, x, batch, tau, s)) != hipSuccess)
+    return hip_fail(e, "stage 1 proxy kernel");
+  if ((e = prox::launch_topk(p, b, batch, k, s)) != hipSuccess)
+    return hip_fail(e, "top-k kernel");
+  const int mode = batch == 1 ? 0 : 1;
+  if (mode == 1 && (e = prox::launch_union(p, b, batch, k, s)) != hipSuccess)
+    return hip_fail(e, "mask union kernel");
+  if ((e = prox::launch_upgate(p, b, x, batch, mode, k, s)) != hipSuccess)
+    return hip_fail(e, "stage 2 up/gate kernel");
+  if ((e = prox::launch_down(p, b, batch, mode, k, y, resid, s)) != hipSuccess)
+    return hip_fail(e, "stage 2 down kernel");
+  return PROX_OK;
+}
+
+prox_status run_dense(const prox_layer *L, const void *x, int batch, void *y,
+                      float *resid, hipStream_t s) {
+  const prox::Plan &p = L->plan;
+  hipError_t e;
+  if ((e = prox::launch_upgate(p, L->bufs, x, batch, 2, p.d_ff, s)) != hipSuccess)
+    return hip_fail(e, "dense up/gate kernel");
+  if ((e = prox::launch_down(p, L->bufs, batch, 2, p.d_ff, y, resid, s)) != hipSuccess)
+    return hip_fail(e, "dense down kernel");
+  return PROX_OK;
+}
+
+prox_status check_forward_args(const prox_layer *L, const void *x, int batch,
+                               float tau, int k, const void *y) {
+  if (!L) return fail(PROX_EINVAL, "layer is NULL");
+  if (!x || !y) return fail(PROX_EINVAL, "x and y must be non-NULL device pointers");
+  if (!aligned(x, 16) || !aligned(y, 16))
+    return fail(PROX_EINVAL, "x and y must be 16-byte aligned");
+  if (batch < 1 || batch > L->plan.max_batch)
+    return fail(PROX_EINVAL, "batch %d outside [1, max_batch=%d]", batch, L->plan.max_batch);
+  if (isnan(tau)) return fail(PROX_EINVAL, "threshold is NaN");
+  if ((size_t)batch * L->plan.d_model * L->plan.esz > prox::kMaxLds)
+    return fail(PROX_EUNSUPPORTED, "batch * d_model activations exceed the %zu-byte LDS budget",
+                prox::kMaxLds);
+  if (k < 0 || k > L->plan.d_ff)
+    return fail(PROX_EINVAL, "k=%d outside [0, d_ff=%d]", k, L->plan.d_ff);
+  return PROX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *prox_last_error(void) { return g_err.c_str(); }
+
+prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
+                             size_t *proxy_bytes, size_t *workspace_bytes) {
+  g_err.clear();
+  prox_status st = check_shape(shape);
+  if (st != PROX_OK) return st;
+  if (!weights_bytes || !proxy_bytes || !workspace_bytes)
+    return fail(PROX_EINVAL, "output size pointers must be non-NULL");
+  const prox::Plan p = prox::make_plan(shape->d_model, shape->d_ff, shape->group_size,
+                                       shape->dtype == PROX_BF16, shape->max_batch);
+  const prox::Layout L = prox::make_layout(p);
+  *weights_bytes = L.weights;
+  *proxy_bytes = L.proxy;
+  *workspace_bytes = L.workspace;
+  return PROX_OK;
+}
+
+prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
+                               const void *w_gate, const void *w_down,
+                               void *weights_buf, void *proxy_buf,
+                               void *workspace_buf, void *stream,
+                               prox_layer **out) {
+  g_err.clear();
+  prox_status st = check_shape(shape);
+  if (st != PROX_OK) return st;
+  if (!out) return fail(PROX_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!w_up || !w_gate || !w_down || !weights_buf || !proxy_buf || !workspace_buf)
+    return fail(PROX_EINVAL, "weight and buffer pointers must be non-NULL");
+  if (!aligned(weights_buf, 256) || !aligned(proxy_buf, 256) || !aligned(workspace_buf, 256))
+    return fail(PROX_EINVAL, "weights/proxy/workspace buffers must be 256-byte aligned");
+  const size_t ea = shape->dtype == PROX_BF16 ? 2 : 4;
+  if (!aligned(w_up, ea) || !aligned(w_gate, ea) || !aligned(w_down, ea))
+    return fail(PROX_EINVAL, "source weights must be aligned to their element size");
+  prox_layer *L = new (std::nothrow) prox_layer;
+  if (!L) return fail(PROX_EINVAL, "out of host memory");
+  L->plan = prox::make_plan(shape->d_model, shape->d_ff, shape->group_size,
+                            shape->dtype == PROX_BF16, shape->max_batch);
+  const prox::Layout lay = prox::make_layout(L->plan);
+  char *wb = (char *)weights_buf, *pb = (char *)proxy_buf, *ws = (char *)workspace_buf;
+  prox::Bufs &b = L->bufs;
+  b.wug = wb;
+  b.wd = wb + lay.o_wd;
+  b.pq = (uint8_t *)pb;
+  b.psc = (float *)(pb + lay.o_psc);
+  b.part = (float *)(ws + lay.o_part);
+  b.tile_cnt = (unsigned *)(ws + lay.o_tile_cnt);
+  b.sabs = (float *)(ws + lay.o_sabs);
+  b.sel = (int *)(ws + lay.o_sel);
+  b.ssp = (float *)(ws + lay.o_ssp);
+  b.uni = (int *)(ws + lay.o_uni);
+  b.nuni = (int *)(ws + lay.o_nuni);
+  b.umask = (uint8_t *)(ws + lay.o_umask);
+  b.ypart = (float *)(ws + lay.o_ypart);
+  b.col_cnt = (unsigned *)(ws + lay.o_col_cnt);
+  b.xbuf = ws + lay.o_xbuf;
+  b.ybuf = ws + lay.o_ybuf;
+  hipError_t e = prox::launch_prepare(L->plan, b, w_up, w_gate, w_down, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    delete L;
+    return hip_fail(e, "prepare kernels");
+  }
+  *out = L;
+  return PROX_OK;
+}
+
+prox_status prox_export_proxy(const prox_layer *layer, int matrix, int8_t *codes,
+                              float *scales, void *stream) {
+  g_err.clear();
+  if (!layer || !codes || !scales) return fail(PROX_EINVAL, "NULL argument");
+  if (matrix != 0 && matrix != 1) return fail(PROX_EINVAL, "matrix must be 0 (up) or 1 (gate)");
+  hipError_t e = prox::launch_export_proxy(layer->plan, layer->bufs, matrix, codes, scales,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "export kernel");
+  return PROX_OK;
+}
+
+prox_status prox_ffn_forward(const prox_layer *layer, const void *x, float threshold,
+                             int k, void *y, void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, 1, threshold, k, y);
+  if (st != PROX_OK) return st;
+  return run_forward(layer, x, 1, threshold, k, y, nullptr, (hipStream_t)stream);
+}
+
+prox_status prox_ffn_forward_batch(const prox_layer *layer, const void *x, int batch,
+                                   float threshold, int k, void *y, void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, batch, threshold, k, y);
+  if (st != PROX_OK) return st;
+  return run_forward(layer, x, batch, threshold, k, y, nullptr, (hipStream_t)stream);
+}
+
+prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int batch,
+                                   float threshold, int k, void *y, const prox_debug *dbg,
+                                   void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, batch, threshold, k, y);
+  if (st != PROX_OK) return st;
+  if (!dbg) return fail(PROX_EINVAL, "dbg is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  st = run_forward(layer, x, batch, threshold, k, y, nullptr, s);
+  if (st != PROX_OK) return st;
+  const prox::Plan &p = layer->plan;
+  const prox::Bufs &b = layer->bufs;
+  hipError_t e = hipSuccess;
+  if (dbg->n1 || dbg->idx) {
+    if (!dbg->n1 || !dbg->idx) return fail(PROX_EINVAL, "n1 and idx must be given together");
+    e = prox::launch_compact_debug(p, x, batch, threshold, dbg->n1, dbg->idx, s);
+    if (e != hipSuccess) return hip_fail(e, "compaction debug kernel");
+  }
+  const size_t nf = (size_t)batch * p.d_ff;
+  if (k > 0) {
+    if (dbg->s_abs &&
+        (e = hipMemcpyAsync(dbg->s_abs, b.sabs, nf * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "copy |s~|");
+    if (dbg->sel &&
+        (e = hipMemcpyAsync(dbg->sel, b.sel, nf * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "copy sel");
+    if (batch == 1 && dbg->s_sel &&
+        (e = hipMemcpyAsync(dbg->s_sel, b.ssp, nf * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "copy s");
+    if (batch > 1) {
+      if (dbg->n_union &&
+          (e = hipMemcpyAsync(dbg->n_union, b.nuni, 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "copy union size");
+      if (dbg->union_idx &&
+          (e = hipMemcpyAsync(dbg->union_idx, b.uni, (size_t)p.d_ff * 4,
+                              hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "copy union");
+      if (dbg->s_sel &&
+          (e = hipMemcpyAsync(dbg->s_sel, b.ssp, nf * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "copy s");
+    }
+  }
+  return PROX_OK;
+}
+
+prox_status prox_dense_ffn_forward(const prox_layer *layer, const void *x, int batch,
+                                   void *y, void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, batch, 0.0f, 0, y);
+  if (st != PROX_OK) return st;
+  return run_dense(layer, x, batch, y, nullptr, (hipStream_t)stream);
+}
+
+prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
+                               const float *thresholds, int k, float *resid, int batch,
+                               float eps, void *stream) {
+  g_err.clear();
+  if (!layers || n_layers <= 0 || !resid)
+    return fail(PROX_EINVAL, "layers, n_layers > 0 and resid are required");
+  if (k >= 0 && !thresholds) return fail(PROX_EINVAL, "thresholds are required when k >= 0");
+  if (!(eps >= 0.0f)) return fail(PROX_EINVAL, "eps must be >= 0");
+  if (!aligned(resid, 16)) return fail(PROX_EINVAL, "resid must be 16-byte aligned");
+  const prox::Plan &p0 = layers[0] ? layers[0]->plan : prox::Plan{};
+  for (int l = 0; l < n_layers; ++l) {
+    const prox_layer *L = layers[l];
+    if (!L) return fail(PROX_EINVAL, "layer %d is NULL", l);
+    if (L->plan.d_model != p0.d_model || L->plan.bf16 != p0.bf16)
+      return fail(PROX_EINVAL, "layer %d has a different d_model or dtype", l);
+    if (batch < 1 || batch > L->plan.max_batch)
+      return fail(PROX_EINVAL, "batch %d outside [1, max_batch] of layer %d", batch, l);
+    if (k > L->plan.d_ff) return fail(PROX_EINVAL, "k=%d above d_ff of layer %d", k, l);
+    if (k >= 0 && isnan(thresholds[l])) return fail(PROX_EINVAL, "threshold %d is NaN", l);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    const prox_layer *L = layers[l];
+    hipError_t e = prox::launch_rmsnorm(L->plan, resid, batch, eps, L->bufs.xbuf, s);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel");
+    prox_status st = (k < 0) ? run_dense(L, L->bufs.xbuf, batch, L->bufs.ybuf, resid, s)
+                             : run_forward(L, L->bufs.xbuf, batch, thresholds[l], k,
+                                           L->bufs.ybuf, resid, s);
+    if (st != PROX_OK) return st;
+  }
+  return PROX_OK;
+}
+
+void prox_destroy_layer(prox_layer *layer) { delete layer; }
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Internal declarations shared by the kernel and ABI translation units of
+// libprox.  Not part of the public interface (include/prox.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace prox {
+
+// Proxy (Stage 1) column tile: 256 intermediate channels.  For one tile and
+// one input row the INT4 codes of W_up (128 bytes) and W_gate (128 bytes) sit
+// side by side, so a surviving row is one contiguous 256-byte read and a
+// pruned row is skipped whole.
+constexpr int kTile = 256;
+constexpr int kTileBytes = 256;
+// Output columns handled by one down-projection work-group.
+constexpr int kDownCols = 256;
+constexpr int kMaxBatch = 8;
+constexpr int kMaxDff = 32768;
+constexpr int kMaxDmodel = 16384;
+// LDS a work-group may hold (gfx950: 160 KiB per compute unit).
+constexpr size_t kMaxLds = 160 * 1024;
+
+// Device buffers of one layer (all owned by the caller).
+struct Bufs {
+  // weights_buf
+  void *wug;       // [d_ff][2][d_model] dtype: channel j's up row, then gate row
+  void *wd;        // [d_ff][d_model]    dtype: W_down as given
+  // proxy_buf
+  uint8_t *pq;     // [ntile][d_model][256] bytes: (code + 8) nibbles, up | gate
+  float *psc;      // [ntile][ngroups][2][256] float32 scales
+  // workspace_buf
+  float *part;     // [ntile][nchunk][batch][512]   Stage 1 partial sums
+  unsigned *tile_cnt;  // [ntile]                  Stage 1 arrival counters
+  float *sabs;     // [batch][d_ff]                 |s~|
+  int *sel;        // [batch][d_ff]                 top-k channels, ascending
+  float *ssp;      // [batch][d_ff]                 exact s by list position
+  int *uni;        // [d_ff]                        union of the masks
+  int *nuni;       // [1]
+  uint8_t *umask;  // [d_ff]                        token bits per union entry
+  float *ypart;    // [nrc][batch][d_model]         Stage 2 down partial sums
+  unsigned *col_cnt;  // [ncol]                    Stage 2 arrival counters
+  void *xbuf;      // [batch][d_model] dtype         stack: normalized input
+  void *ybuf;      // [batch][d_model] dtype         stack: layer output
+};
+
+struct Plan {
+  int d_model, d_ff, G, bf16, max_batch;
+  int esz;          // bytes per element
+  int ngroups;      // d_model / G
+  int ntile;        // ceil(d_ff / 256)
+  int nchunk;       // ceil(ngroups / 4): proxy work-groups per tile
+  int ncol;         // d_model / 256
+  int nrc;          // row chunks of the down projection
+  int upgate_cap;   // max work-groups of the up/gate kernel
+};
+
+struct Layout {
+  size_t weights, proxy, workspace;
+  size_t o_wd, o_psc;
+  size_t o_part, o_tile_cnt, o_sabs, o_sel, o_ssp, o_uni, o_nuni, o_umask,
+      o_ypart, o_col_cnt, o_xbuf, o_ybuf;
+};
+
+Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch);
+Layout make_layout(const Plan &p);
+
+// Kernel launchers (prox_kernels.hip).  Each returns hipSuccess or the launch
+// error.  `batch` is the number of tokens (1..kMaxBatch).
+hipError_t launch_prepare(const Plan &p, const Bufs &b, const void *w_up,
+                          const void *w_gate, const void *w_down,
+                          hipStream_t s);
+hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
+                               int8_t *codes, float *scales, hipStream_t s);
+hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
+                        float tau, hipStream_t s);
+hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k,
+                       hipStream_t s);
+hipError_t launch_union(const Plan &p, const Bufs &b, int batch, int k,
+                        hipStream_t s);
+// mode: 0 = one token over sel, 1 = batch over the union, 2 = dense
+hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
+                         int mode, int n, hipStream_t s);
+hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
+                       void *y, float *resid, hipStream_t s);
+hipError_t launch_compact_debug(const Plan &p, const void *x, int batch,
+                                float tau, int *n1, int *idx, hipStream_t s);
+hipError_t launch_rmsnorm(const Plan &p, const float *resid, int batch,
+                          float eps, void *x, hipStream_t s);
+hipError_t launch_zero_y(const Plan &p, void *y, int batch, hipStream_t s);
+
+}  // namespace prox

@@ -1,0 +1,1028 @@
+// HIP kernels of libprox for CDNA4 (gfx950): the Prox two-stage sparse
+// SwiGLU FFN decode step.
+//
+// Method: "Prox: Training-Free FFN Activation Sparsity via Approximate
+// Intermediate-Channel Salience in LLMs" (arXiv 2607.27591), Sec. 4.1
+// (two-stage inference), Sec. 4.3 (INT4 proxy, fused kernels), App. A.6
+// (top-k mask).
+//
+// Batch-1 decode is a chain of matrix-vector products, so every kernel here
+// is bound by HBM bandwidth, not by arithmetic: no MFMA.  The weight layouts
+// make each read a long contiguous run (see prox_internal.h), reads go
+// through buffer loads with scalar row offsets, and every reduction across
+// work-groups is deterministic (partials + last-arriving work-group, fixed
+// summation order).
+#include "prox_internal.h"
+
+#include <math.h>
+
+namespace prox {
+
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// float32 -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float ld_elem(const void *p, size_t i) {
+  if constexpr (BF16)
+    return bf16_to_f32(((const uint16_t *)p)[i]);
+  else
+    return ((const float *)p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void st_elem(void *p, size_t i, float v) {
+  if constexpr (BF16)
+    ((uint16_t *)p)[i] = f32_to_bf16(v);
+  else
+    ((float *)p)[i] = v;
+}
+
+// Value as stored in the layer dtype (what a caller reads back).
+template <bool BF16>
+__device__ __forceinline__ float round_elem(float v) {
+  if constexpr (BF16)
+    return bf16_to_f32(f32_to_bf16(v));
+  else
+    return v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
+                                                            uint32_t bytes) {
+  // raw buffer: stride 0, num_records = bytes; out-of-range reads return 0.
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Sum over the 64 lanes of a wave, returned uniform: DPP within each row of
+// 16 lanes (quad swaps, then row rotations by 4 and 8), then the four row
+// sums in a fixed order.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int r;
+  switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, true); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, true); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, true); break;
+    default: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, true); break;
+  }
+  return v + __int_as_float(r);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add(v, 0);  // quad_perm [1,0,3,2]
+  v = dpp_add(v, 1);  // quad_perm [2,3,0,1]
+  v = dpp_add(v, 2);  // row_ror:4
+  v = dpp_add(v, 3);  // row_ror:8
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Reinterpret 32 bits as two bf16 lanes.  (Written with memcpy: a
+// __builtin_bit_cast of a single element of a 4 x u32 vector was folded back
+// to element 0 by the optimizer in this toolchain.)
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned v) {
+  bf16x2 r;
+  __builtin_memcpy(&r, &v, 4);
+  return r;
+}
+
+// Dot product of 16 bytes of weights with 16 bytes of activations.
+template <bool BF16>
+__device__ __forceinline__ float dot16(u4 w, u4 x, float acc) {
+  if constexpr (BF16) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), acc, false);
+    return acc;
+  } else {
+    acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+    acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+    acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+    acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+    return acc;
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    unsigned t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a work-group of NWAVES waves; also returns the
+// total.  wsum: NWAVES words of LDS.  Contains two barriers.
+template <int NWAVES>
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned *wsum,
+                                                    unsigned &total) {
+  const unsigned inc = wave_incl_scan(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) wsum[w] = inc;
+  __syncthreads();
+  unsigned off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    const unsigned s = wsum[i];
+    off += (i < w) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return off + inc - v;
+}
+
+// Stage 1 input mask for one 64-row slice (Sec. 4.1, m_x equation): each lane
+// tests its own row, |x_i| >= tau keeps it; the wave gets the 64-bit mask.
+// Shared by the proxy kernel and the compaction debug kernel, so the
+// survivors checked by the tests are the ones the proxy uses.
+template <bool BF16>
+__device__ __forceinline__ uint64_t slice_mask(const void *x, size_t row0,
+                                               float tau, float &xl) {
+  xl = ld_elem<BF16>(x, row0 + (threadIdx.x & 63));
+  return __ballot(fabsf(xl) >= tau);
+}
+
+// ---------------------------------------------------------------------------
+// Prepare: relayout and INT4 quantization (Sec. 4.3)
+// ---------------------------------------------------------------------------
+
+// W [d_model][d_ff] (paper layout) -> wug[j][m][i], m = 0 up, 1 gate.
+template <bool BF16>
+__global__ __launch_bounds__(256) void transpose_kernel(const void *w_up,
+                                                        const void *w_gate,
+                                                        void *wug, int d_model,
+                                                        int d_ff) {
+  typedef typename std::conditional<BF16, uint16_t, float>::type E;
+  __shared__ E tile[64][65];
+  const int m = blockIdx.z;
+  const E *src = (const E *)(m ? w_gate : w_up);
+  E *dst = (E *)wug;
+  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int i = i0 + r, j = j0 + tx;
+    if (i < d_model && j < d_ff) tile[r][tx] = src[(size_t)i * d_ff + j];
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int j = j0 + r, i = i0 + tx;
+    if (i < d_model && j < d_ff)
+      dst[((size_t)j * 2 + m) * d_model + i] = tile[tx][r];
+  }
+}
+
+// One thread per proxy column of a tile, one work-group per (group, tile,
+// matrix).  scale = absmax / 7, code = clamp(rint(w / scale), -7, 7), both
+// divisions correctly rounded float32; stored as (code + 8) nibbles, two
+// columns per byte (low nibble = even column).
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_kernel(const void *w_up,
+                                                       const void *w_gate,
+                                                       uint8_t *pq, float *psc,
+                                                       int d_model, int d_ff,
+                                                       int G, int ngroups) {
+  const int g = blockIdx.x, t = blockIdx.y, m = blockIdx.z;
+  const int c = threadIdx.x;
+  const int j = t * kTile + c;
+  const void *W = m ? w_gate : w_up;
+  const bool live = j < d_ff;
+  float a = 0.0f;
+  if (live)
+    for (int i = g * G; i < (g + 1) * G; ++i)
+      a = fmaxf(a, fabsf(ld_elem<BF16>(W, (size_t)i * d_ff + j)));
+  const float sc = live ? __fdiv_rn(a, 7.0f) : 0.0f;
+  psc[((size_t)t * ngroups + g) * 512 + m * 256 + c] = sc;
+  for (int i = g * G; i < (g + 1) * G; ++i) {
+    int code = 0;
+    if (live && a > 0.0f) {
+      float r = rintf(__fdiv_rn(ld_elem<BF16>(W, (size_t)i * d_ff + j), sc));
+      r = fminf(fmaxf(r, -7.0f), 7.0f);
+      code = (int)r;
+    }
+    const unsigned nib = (unsigned)(code + 8);
+    const unsigned odd = __shfl_xor(nib, 1, 64);
+    if ((c & 1) == 0)
+      pq[((size_t)t * d_model + i) * kTileBytes + m * 128 + (c >> 1)] =
+          (uint8_t)(nib | (odd << 4));
+  }
+}
+
+// Unpack a prepared proxy back to int8 codes [d_model][d_ff] and scales
+// [ngroups][d_ff] (paper layout), for inspection.
+__global__ __launch_bounds__(256) void export_proxy_kernel(
+    const uint8_t *pq, const float *psc, int matrix, int d_model, int d_ff,
+    int G, int ngroups, int8_t *codes, float *scales) {
+  const int i = blockIdx.x, t = blockIdx.y, c = threadIdx.x;
+  const int j = t * kTile + c;
+  if (j >= d_ff) return;
+  const uint8_t byte =
+      pq[((size_t)t * d_model + i) * kTileBytes + matrix * 128 + (c >> 1)];
+  const int nib = (c & 1) ? (byte >> 4) : (byte & 15);
+  codes[(size_t)i * d_ff + j] = (int8_t)(nib - 8);
+  if (i % G == 0)
+    scales[(size_t)(i / G) * d_ff + j] =
+        psc[((size_t)t * ngroups + i / G) * 512 + matrix * 256 + c];
+}
+
+// ---------------------------------------------------------------------------
+// K-c  Stage 1: threshold + compact + INT4 proxy up/gate GEMV + SwiGLU
+//      (Sec. 4.1, m_x and u~/h~ equations; Sec. 4.3, fused Stage 1 kernel)
+// ---------------------------------------------------------------------------
+// Grid (nchunk, ntile), 4 waves.  Wave w of chunk c handles scale group
+// g = 4c + w of column tile t.  It finds the group's surviving rows with one
+// ballot per 64-row slice (the compaction never leaves registers), parks the
+// masked x values of the group in LDS, then streams only the surviving rows'
+// 256-byte code runs, 16 rows in flight while the previous 16 are consumed.
+// Lane l covers 8 consecutive columns: lanes 0-31 the up proxy, lanes 32-63
+// the gate proxy of the same columns.  Since
+//   sum_i x_i * code_i = sum_i x_i * nib_i - 8 * sum_i x_i,
+// each code costs one byte->float conversion and one FMA per token, and the
+// -8 offset and the group scale are applied once per group.
+// The last work-group to finish a tile adds the partials of all chunks in a
+// fixed order and writes |s~| = |u~ * SiLU(g~)| for the tile's columns.
+struct ProxyArgs {
+  const uint8_t *pq;
+  const float *psc;
+  const void *x;
+  float tau;
+  int d_model, d_ff, G, ngroups, nchunk;
+  float *part;
+  unsigned *tile_cnt;
+  float *sabs;
+};
+
+template <int NB, bool BF16, int NSL>
+__global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
+  constexpr int U = 16;            // rows per pipeline stage
+  constexpr int GR = NSL * 64;     // rows per group
+  constexpr int LL = GR + 3 * U;   // list length incl. padding for prefetch
+  __shared__ float red[4][512];
+  __shared__ __attribute__((aligned(16))) int rl[4][LL];      // surviving rows of the group
+  __shared__ __attribute__((aligned(16))) float xc[4][NB][LL]; // their x (0 where a token drops them)
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int chunk = blockIdx.x, t = blockIdx.y;
+  const int g = chunk * 4 + wv;
+
+  float acc[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[b][c] = 0.0f;
+
+  if (g < a.ngroups) {
+    // Input mask of the group's rows (Sec. 4.1, m_x), compacted in LDS: the
+    // union over tokens decides which rows are read; each token keeps its
+    // own x or 0.
+    float xsum[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xsum[b] = 0.0f;
+    int cnt = 0;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      float xm[NB];
+      uint64_t un = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float xl;
+        const uint64_t mk =
+            slice_mask<BF16>(a.x, (size_t)b * a.d_model + g * GR + sl * 64, a.tau, xl);
+        xm[b] = ((mk >> lane) & 1ull) ? xl : 0.0f;
+        xsum[b] += wave_sum(xm[b]);
+        un |= mk;
+      }
+      if ((un >> lane) & 1ull) {
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                  (unsigned)(un >> 32),
+                                  __builtin_amdgcn_mbcnt_lo((unsigned)un, 0u));
+        rl[wv][pos] = sl * 64 + lane;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xc[wv][b][pos] = xm[b];
+      }
+      cnt += (int)__popcll(un);
+    }
+    // Padding: row 0 of the group (a valid address) with x = 0.
+    if (lane < 3 * U) {
+      rl[wv][cnt + lane] = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xc[wv][b][cnt + lane] = 0.0f;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(a.pq + (size_t)t * a.d_model * kTileBytes,
+                  (uint32_t)a.d_model * kTileBytes);
+    const uint32_t voff = (uint32_t)lane * 4u;
+    const uint32_t gbase = (uint32_t)g * GR * kTileBytes;
+
+    // Stage `base`: 16 row indices (uniform) and their code words.
+    auto fetch = [&](int base, uint32_t (&w)[U]) {
+#pragma unroll
+      for (int q = 0; q < U / 4; ++q) {
+        const int4 r4 = *(const int4 *)&rl[wv][base + 4 * q];
+        const int rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(rr[e]);
+          w[4 * q + e] = __builtin_amdgcn_raw_buffer_load_b32(
+              rs, voff, gbase + row * kTileBytes, 0);
+        }
+      }
+    };
+    // 0x0f0f0f0f kept opaque to the optimizer: with a visible constant it
+    // fuses mask + shift into one bit-field extract per nibble, while this
+    // way one AND serves four byte->float conversions (v_cvt_f32_ubyte0..3).
+    uint32_t nib_mask;
+    asm volatile("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(nib_mask));
+    // Consume one stage: 16 rows, per token one FMA per code.
+    auto consume = [&](int base, const uint32_t (&w)[U]) {
+#pragma unroll
+      for (int q = 0; q < U / 4; ++q) {
+        float4 x4[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) x4[b] = *(const float4 *)&xc[wv][b][base + 4 * q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wcur = w[4 * q + e];
+          const uint32_t lo = wcur & nib_mask;
+          const uint32_t hi = (wcur >> 4) & nib_mask;
+          float n[8];
+          n[0] = (float)(lo & 0xffu);
+          n[1] = (float)(hi & 0xffu);
+          n[2] = (float)((lo >> 8) & 0xffu);
+          n[3] = (float)((hi >> 8) & 0xffu);
+          n[4] = (float)((lo >> 16) & 0xffu);
+          n[5] = (float)((hi >> 16) & 0xffu);
+          n[6] = (float)(lo >> 24);
+          n[7] = (float)(hi >> 24);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const float xv = e == 0 ? x4[b].x : e == 1 ? x4[b].y : e == 2 ? x4[b].z : x4[b].w;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[b][c] = fmaf(xv, n[c], acc[b][c]);
+          }
+        }
+      }
+    };
+    // Two buffers in turn: while one stage is consumed the next is in flight.
+    uint32_t wa[U], wb[U];
+    fetch(0, wa);
+    for (int base = 0; base < cnt; base += 2 * U) {
+      fetch(base + U, wb);
+      consume(base, wa);
+      fetch(base + 2 * U, wa);
+      if (base + U < cnt) consume(base + U, wb);
+    }
+    // Apply the group scale: u~ contribution = scale * (sum x*nib - 8 sum x).
+    const float4 *sp = (const float4 *)(a.psc +
+                                        ((size_t)t * a.ngroups + g) * 512 +
+                                        (size_t)lane * 8);
+    const float4 s0 = sp[0], s1 = sp[1];
+    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[b][c] = sc[c] * (acc[b][c] - 8.0f * xsum[b]);
+  }
+
+  // Sum the four waves (fixed order) and publish this chunk's partials.
+  float *part = a.part + ((size_t)t * a.nchunk + chunk) * NB * 512;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float4 *rp = (float4 *)&red[wv][lane * 8];
+    rp[0] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    rp[1] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+    __syncthreads();
+    for (int e = threadIdx.x; e < 512; e += 256)
+      part[b * 512 + e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+    __syncthreads();
+  }
+
+  // Release this work-group's partials (every thread), then count arrival.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = (atomicAdd(&a.tile_cnt[t], 1u) == (unsigned)(a.nchunk - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // Tile epilogue: u~, g~ for 256 columns per token, then |s~|.
+  const float *tp = a.part + (size_t)t * a.nchunk * NB * 512;
+  for (int e = threadIdx.x; e < NB * 256; e += 256) {
+    const int b = e >> 8, col = e & 255;
+    float u = 0.0f, gg = 0.0f;
+    for (int ch = 0; ch < a.nchunk; ++ch) {
+      u += tp[((size_t)ch * NB + b) * 512 + col];
+      gg += tp[((size_t)ch * NB + b) * 512 + 256 + col];
+    }
+    const int j = t * kTile + col;
+    if (j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(u * silu(gg));
+  }
+  if (threadIdx.x == 0) a.tile_cnt[t] = 0u;  // ready for the next call
+}
+
+// ---------------------------------------------------------------------------
+// K-d  Top-k channel mask (App. A.6, top-k equation), ties to the lower index
+// ---------------------------------------------------------------------------
+// One 1024-thread work-group per token.  |s~| >= 0, so its float32 bit
+// pattern orders like the value; a three-pass most-significant-digit radix
+// select (11, 11, 10 bits) finds the k-th largest key T and how many keys
+// equal to T are taken.  Thread t owns the contiguous channels
+// [t*PER, (t+1)*PER) in registers, so one exclusive scan gives each thread
+// its output position and the list comes out ascending; keys equal to T are
+// taken lowest index first.
+template <int PER>
+__global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
+                                                    int k, int *sel) {
+  __shared__ unsigned hist[2048];
+  __shared__ unsigned wsum[16];
+  __shared__ unsigned s_bin, s_kk;
+  const int b = blockIdx.x;
+  if (k <= 0) return;
+  const float *z = sabs + (size_t)b * d_ff;
+  int *out = sel + (size_t)b * d_ff;
+  const int tid = threadIdx.x;
+  const int j0 = tid * PER;
+
+  unsigned key[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = j0 + e;
+    key[e] = (j < d_ff) ? __float_as_uint(z[j]) : 0u;
+  }
+
+  unsigned prefix = 0u, pmask = 0u, kk = (unsigned)k;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const unsigned nb = pass == 2 ? 1024u : 2048u;
+    for (int i = tid; i < 2048; i += 1024) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (j0 + e < d_ff && (key[e] & pmask) == prefix)
+        atomicAdd(&hist[(key[e] >> sh) & (nb - 1u)], 1u);
+    __syncthreads();
+    // Thread t owns bins [t*bpt, (t+1)*bpt); count of keys in higher bins.
+    const int bpt = (int)(nb >> 10);
+    unsigned c1 = hist[tid * bpt];
+    unsigned c2 = (bpt == 2) ? hist[tid * bpt + 1] : 0u;
+    unsigned total;
+    const unsigned below = block_excl_scan<16>(c1 + c2, wsum, total);
+    const unsigned above = total - below - (c1 + c2);
+    if (bpt == 2) {
+      if (above < kk && above + c2 >= kk) {
+        s_bin = (unsigned)(tid * 2 + 1);
+        s_kk = kk - above;
+      } else if (above + c2 < kk && above + c2 + c1 >= kk) {
+        s_bin = (unsigned)(tid * 2);
+        s_kk = kk - above - c2;
+      }
+    } else if (above < kk && above + c1 >= kk) {
+      s_bin = (unsigned)tid;
+      s_kk = kk - above;
+    }
+    __syncthreads();
+    prefix |= s_bin << sh;
+    pmask |= (nb - 1u) << sh;
+    kk = s_kk;
+    __syncthreads();
+  }
+
+  // Compaction: keys > T all go, keys == T go while fewer than kk taken.
+  unsigned gt = 0u, eq = 0u;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (j0 + e < d_ff) {
+      gt += key[e] > prefix;
+      eq += key[e] == prefix;
+    }
+  unsigned total;
+  const unsigned before = block_excl_scan<16>((eq << 16) | gt, wsum, total);
+  unsigned eq_seen = before >> 16;
+  unsigned pos = (before & 0xffffu) + min(eq_seen, kk);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = j0 + e;
+    if (j < d_ff) {
+      if (key[e] > prefix) {
+        out[pos++] = j;
+      } else if (key[e] == prefix) {
+        if (eq_seen < kk) out[pos++] = j;
+        ++eq_seen;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Union of the per-token masks (batch path): U ascending, plus for each entry
+// the bit set of tokens whose mask holds it.  One 1024-thread work-group.
+// ---------------------------------------------------------------------------
+template <int PER>
+__global__ __launch_bounds__(1024) void union_kernel(const int *sel, int d_ff,
+                                                     int k, int nb, int *uni,
+                                                     int *nuni, uint8_t *umask) {
+  __shared__ unsigned bits[kMaxBatch][kMaxDff / 32];
+  __shared__ unsigned wsum[16];
+  const int tid = threadIdx.x;
+  const int words = (d_ff + 31) >> 5;
+  for (int b = 0; b < nb; ++b)
+    for (int i = tid; i < words; i += 1024) bits[b][i] = 0u;
+  __syncthreads();
+  for (int b = 0; b < nb; ++b)
+    for (int i = tid; i < k; i += 1024) {
+      const int j = sel[(size_t)b * d_ff + i];
+      if ((unsigned)j < (unsigned)d_ff) atomicOr(&bits[b][j >> 5], 1u << (j & 31));
+    }
+  __syncthreads();
+  const int j0 = tid * PER;
+  unsigned tm[PER];
+  unsigned cnt = 0u;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = j0 + e;
+    unsigned m = 0u;
+    if (j < d_ff)
+      for (int b = 0; b < nb; ++b) m |= ((bits[b][j >> 5] >> (j & 31)) & 1u) << b;
+    tm[e] = m;
+    cnt += (m != 0u);
+  }
+  unsigned total;
+  unsigned pos = block_excl_scan<16>(cnt, wsum, total);
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (tm[e]) {
+      uni[pos] = j0 + e;
+      umask[pos] = (uint8_t)tm[e];
+      ++pos;
+    }
+  if (tid == 0) *nuni = (int)total;
+}
+
+// ---------------------------------------------------------------------------
+// K-e  Stage 2a: exact gathered up/gate GEMV fused with SiLU and the product
+//      (Sec. 4.1, Stage 2 equations: u_sp, h_sp, s_sp over the full x)
+// ---------------------------------------------------------------------------
+// One wave per selected channel j (grid-stride over list positions).  The
+// channel's up row and gate row are one contiguous run of 2*d_model elements
+// (channel-major layout), read 16 bytes per lane per step; x sits in LDS.
+// mode 0: position p -> channel sel[p] (one token); mode 1: channel uni[p],
+// s zeroed for tokens whose own mask lacks it; mode 2: dense, channel p.
+struct UpGateArgs {
+  const void *wug;
+  uint32_t wug_bytes;
+  const void *x;
+  int d_model, d_ff, n;
+  const int *n_ptr;
+  const int *list;
+  const uint8_t *umask;
+  float *ssp;
+};
+
+template <int NB, bool BF16, int MODE>
+__global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
+  extern __shared__ u4 xs[];
+  constexpr int EPL = BF16 ? 8 : 4;   // elements per 16-byte load
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int MU = 8;               // 16-byte steps in flight per matrix
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row16 = a.d_model / EPL;  // 16-byte units per row
+  for (int i = threadIdx.x; i < NB * row16; i += 256) xs[i] = ((const u4 *)a.x)[i];
+  __syncthreads();
+
+  const int n = a.n_ptr ? *a.n_ptr : a.n;
+  const int nsteps = row16 / 64;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
+  const int W = gridDim.x * 4;
+  for (int p = blockIdx.x * 4 + wv; p < n; p += W) {
+    const int j = (MODE == 2) ? p : a.list[p];
+    const uint32_t ubase = (uint32_t)j * 2u * (uint32_t)a.d_model * ESZ;
+    const uint32_t gbase = ubase + (uint32_t)a.d_model * ESZ;
+    float au[NB], ag[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) au[b] = ag[b] = 0.0f;
+    for (int m0 = 0; m0 < nsteps; m0 += MU) {
+      u4 wu[MU], wg[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const uint32_t off = (uint32_t)((m0 + u) * 64 + lane) * 16u;
+        if (m0 + u < nsteps) {
+          wu[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase, 0);
+          wg[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, gbase, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        if (m0 + u < nsteps) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const u4 xv = xs[b * row16 + (m0 + u) * 64 + lane];
+            au[b] = dot16<BF16>(wu[u], xv, au[b]);
+            ag[b] = dot16<BF16>(wg[u], xv, ag[b]);
+          }
+        }
+      }
+    }
+    unsigned tok = 0xffu;
+    if (MODE == 1) tok = a.umask[p];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float u = wave_sum(au[b]);
+      const float g = wave_sum(ag[b]);
+      if (lane == 0)
+        a.ssp[(size_t)b * a.d_ff + p] = ((tok >> b) & 1u) ? u * silu(g) : 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K-f  Stage 2b: input-sparse down projection y = s_sp W_down[sel, :]
+//      (Sec. 4.1, Stage 2 equations; Sec. 3.1, weighted-sum view)
+// ---------------------------------------------------------------------------
+// Grid (ncol, nrc), 4 waves.  Work-group (c, r) covers output columns
+// [256c, 256c + 256) and list positions [rR, rR + R); lane l owns 4 columns
+// and walks its wave's rows (8 bytes bf16 / 16 bytes f32 per row), with the
+// row index and s value uniform across the wave.  The last work-group of a
+// column chunk adds the nrc partials in order, casts y to the layer dtype
+// and, for the stack, adds it to the float32 residual.
+struct DownArgs {
+  const void *wd;
+  uint32_t wd_bytes;
+  int d_model, d_ff, n, nrc;
+  const int *n_ptr;
+  const int *list;
+  const float *ssp;
+  float *ypart;
+  unsigned *col_cnt;
+  void *y;
+  float *resid;
+};
+
+template <int NB, bool BF16, int MODE>
+__global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
+  constexpr int U = 16;  // rows in flight per wave
+  constexpr int ESZ = BF16 ? 2 : 4;
+  __shared__ float red[4][NB][kDownCols];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cc = blockIdx.x, rc = blockIdx.y;
+  const int n = a.n_ptr ? *a.n_ptr : a.n;
+  const int R = (n + a.nrc - 1) / a.nrc;
+  const int p0 = rc * R;
+  const int p1 = min(n, p0 + R);
+  const int col = cc * kDownCols + lane * 4;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wd, a.wd_bytes);
+  const uint32_t voff = (uint32_t)col * ESZ;
+
+  float acc[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[b][c] = 0.0f;
+
+  // Rows p0+wv, p0+wv+4, ... of this chunk; an out-of-range slot re-reads a
+  // valid row and gets s = 0, so the loop body has no branches.
+  for (int p = p0 + wv; p < p1; p += 4 * U) {
+    float wf[U][4];
+    float sv[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pp = p + 4 * u;
+      const bool ok = pp < p1;
+      const int ppc = ok ? pp : p;
+      const int j = (MODE == 2) ? ppc : a.list[ppc];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sv[u][b] = ok ? a.ssp[(size_t)b * a.d_ff + ppc] : 0.0f;
+      const uint32_t rowoff = (uint32_t)j * (uint32_t)a.d_model * ESZ;
+      if constexpr (BF16) {
+        const u2 w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, rowoff, 0);
+        wf[u][0] = bf16_to_f32(w.x & 0xffffu);
+        wf[u][1] = bf16_to_f32(w.x >> 16);
+        wf[u][2] = bf16_to_f32(w.y & 0xffffu);
+        wf[u][3] = bf16_to_f32(w.y >> 16);
+      } else {
+        const u4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, 0);
+        wf[u][0] = __uint_as_float(w.x);
+        wf[u][1] = __uint_as_float(w.y);
+        wf[u][2] = __uint_as_float(w.z);
+        wf[u][3] = __uint_as_float(w.w);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[b][c] = fmaf(sv[u][b], wf[u][c], acc[b][c]);
+  }
+
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    *(float4 *)&red[wv][b][lane * 4] =
+        make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+  __syncthreads();
+  float *yp = a.ypart + (size_t)rc * NB * a.d_model;
+  for (int e = threadIdx.x; e < NB * kDownCols; e += 256) {
+    const int b = e / kDownCols, c = e % kDownCols;
+    yp[(size_t)b * a.d_model + cc * kDownCols + c] =
+        ((red[0][b][c] + red[1][b][c]) + red[2][b][c]) + red[3][b][c];
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = (atomicAdd(&a.col_cnt[cc], 1u) == (unsigned)(a.nrc - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int e = threadIdx.x; e < NB * kDownCols; e += 256) {
+    const int b = e / kDownCols, c = cc * kDownCols + e % kDownCols;
+    float v = 0.0f;
+    for (int r = 0; r < a.nrc; ++r) v += a.ypart[((size_t)r * NB + b) * a.d_model + c];
+    const size_t o = (size_t)b * a.d_model + c;
+    st_elem<BF16>(a.y, o, v);
+    if (a.resid) a.resid[o] += round_elem<BF16>(v);
+  }
+  if (threadIdx.x == 0) a.col_cnt[cc] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Verification helper: the Stage 1 survivors as an ascending list, built
+// with the same slice_mask() the proxy kernel uses.  One work-group per token.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(1024) void compact_debug_kernel(const void *x,
+                                                             int d_model,
+                                                             float tau, int *n1,
+                                                             int *idx) {
+  __shared__ int cnt[kMaxDff / 64];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nslices = d_model / 64;
+  const void *xb = (const char *)x + (size_t)b * d_model * (BF16 ? 2 : 4);
+  for (int s = wv; s < nslices; s += 16) {
+    float xl;
+    const uint64_t m = slice_mask<BF16>(xb, (size_t)s * 64, tau, xl);
+    if (lane == 0) cnt[s] = __popcll(m);
+  }
+  __syncthreads();
+  for (int s = wv; s < nslices; s += 16) {
+    float xl;
+    const uint64_t m = slice_mask<BF16>(xb, (size_t)s * 64, tau, xl);
+    int off = 0;
+    for (int q = 0; q < s; ++q) off += cnt[q];
+    if ((m >> lane) & 1ull)
+      idx[(size_t)b * d_model + off + __popcll(m & ((1ull << lane) - 1ull))] =
+          s * 64 + lane;
+  }
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int q = 0; q < nslices; ++q) tot += cnt[q];
+    n1[b] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stack glue: x = cast(r / sqrt(mean(r^2) + eps)), unit gain.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *resid,
+                                                      int d_model, float eps,
+                                                      void *x) {
+  __shared__ float ws[4];
+  const int b = blockIdx.x;
+  const float *r = resid + (size_t)b * d_model;
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < d_model; i += 256) ss = fmaf(r[i], r[i], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d_model + eps);
+  for (int i = threadIdx.x; i < d_model; i += 256)
+    st_elem<BF16>(x, (size_t)b * d_model + i, r[i] * inv);
+}
+
+template <bool BF16>
+__global__ void zero_kernel(void *y, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) st_elem<BF16>(y, i, 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+#define PROX_DISPATCH_NB(NBVAR, BODY)                  \
+  switch (NBVAR) {                                     \
+    case 1: { constexpr int NB = 1; BODY; } break;     \
+    case 2: { constexpr int NB = 2; BODY; } break;     \
+    case 3: { constexpr int NB = 3; BODY; } break;     \
+    case 4: { constexpr int NB = 4; BODY; } break;     \
+    case 5: { constexpr int NB = 5; BODY; } break;     \
+    case 6: { constexpr int NB = 6; BODY; } break;     \
+    case 7: { constexpr int NB = 7; BODY; } break;     \
+    case 8: { constexpr int NB = 8; BODY; } break;     \
+    default: return hipErrorInvalidValue;              \
+  }
+
+hipError_t launch_prepare(const Plan &p, const Bufs &b, const void *w_up,
+                          const void *w_gate, const void *w_down,
+                          hipStream_t s) {
+  dim3 tg((p.d_ff + 63) / 64, (p.d_model + 63) / 64, 2);
+  if (p.bf16)
+    transpose_kernel<true><<<tg, 256, 0, s>>>(w_up, w_gate, b.wug, p.d_model, p.d_ff);
+  else
+    transpose_kernel<false><<<tg, 256, 0, s>>>(w_up, w_gate, b.wug, p.d_model, p.d_ff);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(b.wd, w_down, (size_t)p.d_ff * p.d_model * p.esz,
+                     hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  // Padding columns of the last tile keep code 0 (nibble 8) and scale 0.
+  e = hipMemsetAsync(b.pq, 0x88, (size_t)p.ntile * p.d_model * kTileBytes, s);
+  if (e != hipSuccess) return e;
+  dim3 qg(p.ngroups, p.ntile, 2);
+  if (p.bf16)
+    quantize_kernel<true><<<qg, 256, 0, s>>>(w_up, w_gate, b.pq, b.psc, p.d_model,
+                                             p.d_ff, p.G, p.ngroups);
+  else
+    quantize_kernel<false><<<qg, 256, 0, s>>>(w_up, w_gate, b.pq, b.psc, p.d_model,
+                                              p.d_ff, p.G, p.ngroups);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipMemsetAsync(b.tile_cnt, 0, sizeof(unsigned) * p.ntile, s);
+  if (e != hipSuccess) return e;
+  return hipMemsetAsync(b.col_cnt, 0, sizeof(unsigned) * p.ncol, s);
+}
+
+hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
+                               int8_t *codes, float *scales, hipStream_t s) {
+  dim3 g(p.d_model, p.ntile);
+  export_proxy_kernel<<<g, 256, 0, s>>>(b.pq, b.psc, matrix, p.d_model, p.d_ff,
+                                        p.G, p.ngroups, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
+                        float tau, hipStream_t s) {
+  ProxyArgs a{b.pq, b.psc, x, tau, p.d_model, p.d_ff, p.G, p.ngroups,
+              p.nchunk, b.part, b.tile_cnt, b.sabs};
+  dim3 g(p.nchunk, p.ntile);
+  const int nsl = p.G / 64;
+  if (p.bf16) {
+    if (nsl == 1) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true, 1><<<g, 256, 0, s>>>(a))); }
+    else if (nsl == 2) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true, 2><<<g, 256, 0, s>>>(a))); }
+    else if (nsl == 4) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true, 4><<<g, 256, 0, s>>>(a))); }
+    else return hipErrorInvalidValue;
+  } else {
+    if (nsl == 1) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false, 1><<<g, 256, 0, s>>>(a))); }
+    else if (nsl == 2) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false, 2><<<g, 256, 0, s>>>(a))); }
+    else if (nsl == 4) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false, 4><<<g, 256, 0, s>>>(a))); }
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int PER>
+static void topk_launch(const Plan &p, const Bufs &b, int batch, int k, hipStream_t s) {
+  topk_kernel<PER><<<batch, 1024, 0, s>>>(b.sabs, p.d_ff, k, b.sel);
+}
+
+hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, hipStream_t s) {
+  const int per = (p.d_ff + 1023) / 1024;
+  if (per <= 1) topk_launch<1>(p, b, batch, k, s);
+  else if (per <= 4) topk_launch<4>(p, b, batch, k, s);
+  else if (per <= 8) topk_launch<8>(p, b, batch, k, s);
+  else if (per <= 16) topk_launch<16>(p, b, batch, k, s);
+  else if (per <= 32) topk_launch<32>(p, b, batch, k, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const Plan &p, const Bufs &b, int batch, int k, hipStream_t s) {
+  const int per = (p.d_ff + 1023) / 1024;
+  if (per <= 8)
+    union_kernel<8><<<1, 1024, 0, s>>>(b.sel, p.d_ff, k, batch, b.uni, b.nuni, b.umask);
+  else if (per <= 16)
+    union_kernel<16><<<1, 1024, 0, s>>>(b.sel, p.d_ff, k, batch, b.uni, b.nuni, b.umask);
+  else if (per <= 32)
+    union_kernel<32><<<1, 1024, 0, s>>>(b.sel, p.d_ff, k, batch, b.uni, b.nuni, b.umask);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int NB, bool BF16, int MODE>
+static hipError_t upgate_go(const UpGateArgs &a, int grid, size_t lds, hipStream_t s) {
+  auto fn = upgate_kernel<NB, BF16, MODE>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void *)fn,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  fn<<<grid, 256, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
+                         int mode, int n, hipStream_t s) {
+  UpGateArgs a{b.wug, (uint32_t)((size_t)p.d_ff * 2 * p.d_model * p.esz), x,
+               p.d_model, p.d_ff, n, nullptr,
+               mode == 0 ? b.sel : b.uni, b.umask, b.ssp};
+  if (mode == 1) a.n_ptr = b.nuni;
+  const int maxn = (mode == 1) ? p.d_ff : n;
+  if (maxn <= 0) return hipSuccess;
+  int grid = (maxn + 3) / 4;
+  if (grid > p.upgate_cap) grid = p.upgate_cap;
+  const size_t lds = (size_t)batch * p.d_model * p.esz;
+  hipError_t e = hipErrorInvalidValue;
+  if (p.bf16) {
+    if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 0>(a, grid, lds, s))); }
+    else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 1>(a, grid, lds, s))); }
+    else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 2>(a, grid, lds, s))); }
+  } else {
+    if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 0>(a, grid, lds, s))); }
+    else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 1>(a, grid, lds, s))); }
+    else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 2>(a, grid, lds, s))); }
+  }
+  return e;
+}
+
+hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
+                       void *y, float *resid, hipStream_t s) {
+  DownArgs a{b.wd, (uint32_t)((size_t)p.d_ff * p.d_model * p.esz), p.d_model,
+             p.d_ff, n, p.nrc, nullptr, mode == 0 ? b.sel : b.uni, b.ssp,
+             b.ypart, b.col_cnt, y, resid};
+  if (mode == 1) a.n_ptr = b.nuni;
+  dim3 g(p.ncol, p.nrc);
+  if (p.bf16) {
+    if (mode == 0) { PROX_DISPATCH_NB(batch, (down_kernel<NB, true, 0><<<g, 256, 0, s>>>(a))); }
+    else if (mode == 1) { PROX_DISPATCH_NB(batch, (down_kernel<NB, true, 1><<<g, 256, 0, s>>>(a))); }
+    else { PROX_DISPATCH_NB(batch, (down_kernel<NB, true, 2><<<g, 256, 0, s>>>(a))); }
+  } else {
+    if (mode == 0) { PROX_DISPATCH_NB(batch, (down_kernel<NB, false, 0><<<g, 256, 0, s>>>(a))); }
+    else if (mode == 1) { PROX_DISPATCH_NB(batch, (down_kernel<NB, false, 1><<<g, 256, 0, s>>>(a))); }
+    else { PROX_DISPATCH_NB(batch, (down_kernel<NB, false, 2><<<g, 256, 0, s>>>(a))); }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_debug(const Plan &p, const void *x, int batch,
+                                float tau, int *n1, int *idx, hipStream_t s) {
+  if (p.bf16)
+    compact_debug_kernel<true><<<batch, 1024, 0, s>>>(x, p.d_model, tau, n1, idx);
+  else
+    compact_debug_kernel<false><<<batch, 1024, 0, s>>>(x, p.d_model, tau, n1, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const Plan &p, const float *resid, int batch,
+                          float eps, void *x, hipStream_t s) {
+  if (p.bf16)
+    rmsnorm_kernel<true><<<batch, 256, 0, s>>>(resid, p.d_model, eps, x);
+  else
+    rmsnorm_kernel<false><<<batch, 256, 0, s>>>(resid, p.d_model, eps, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_y(const Plan &p, void *y, int batch, hipStream_t s) {
+  const size_t n = (size_t)batch * p.d_model;
+  const int blocks = (int)((n + 255) / 256);
+  if (p.bf16)
+    zero_kernel<true><<<blocks, 256, 0, s>>>(y, n);
+  else
+    zero_kernel<false><<<blocks, 256, 0, s>>>(y, n);
+  return hipGetLastError();
+}
+
+}  // namespace prox

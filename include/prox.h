@@ -1,0 +1,165 @@
+/*
+ * prox.h -- C ABI of libprox, the MI355X (gfx950) implementation of the Prox
+ * two-stage sparse SwiGLU FFN decode step.
+ *
+ * Method: "Prox: Training-Free FFN Activation Sparsity via Approximate
+ * Intermediate-Channel Salience in LLMs" (arXiv 2607.27591).
+ *   Stage 1 (Sec. 4.1, m_x and u~/h~ equations): keep the inputs with
+ *     |x_i| >= threshold, run the INT4 proxy up/gate projections over those
+ *     rows only, and form s~ = (x W~up) . SiLU(x W~gate).
+ *   Mask (App. A.6, top-k equation): the k channels of largest |s~|, ties to
+ *     the lower index, shared by all three projections.
+ *   Stage 2 (Sec. 4.1, Stage 2 equations): exact up/gate over the selected
+ *     channels with the full x, s = u . SiLU(g), then y = s W_down over the
+ *     selected rows.
+ *
+ * Conventions shared by every call:
+ *  - All pointers to tensors are DEVICE pointers owned by the caller; the
+ *    library allocates no device memory.  `stream` is a hipStream_t (NULL =
+ *    the null stream); every call only enqueues work on it and never
+ *    synchronizes the host.
+ *  - Element type of weights, x and y is the layer's dtype (PROX_F32 or
+ *    PROX_BF16, bf16 = IEEE-754 binary32 truncated to its top 16 bits).
+ *  - Weights are given in the paper's x.W layout (Sec. 2.1):
+ *      w_up, w_gate: [d_model][d_ff] row-major; w_down: [d_ff][d_model].
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    rejected call enqueues nothing.  Errors: PROX_EINVAL (bad argument),
+ *    PROX_EUNSUPPORTED (valid but unsupported shape), PROX_EHIP (a HIP call
+ *    or launch failed).  prox_last_error() describes the last failure of the
+ *    calling thread.
+ *  - A layer's workspace is reused by every call on that layer: calls that
+ *    share a layer (or a workspace) must be ordered on one stream.
+ */
+#ifndef PROX_H_
+#define PROX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PROX_OK = 0,
+  PROX_EINVAL = -1,
+  PROX_EUNSUPPORTED = -2,
+  PROX_EHIP = -3
+} prox_status;
+
+typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
+
+/* Shape of one FFN layer.
+ *   d_model     input/output width, at most 16384, a multiple of group_size
+ *               and of 512 (bf16) or 256 (f32); batch * d_model activations
+ *               must fit in 160 KiB
+ *   d_ff        intermediate width, 1..32768
+ *   group_size  G, rows per INT4 proxy scale group: 64, 128 or 256
+ *   dtype       prox_dtype of weights, x and y
+ *   max_batch   largest batch a forward call may pass, 1..8            */
+typedef struct {
+  int d_model;
+  int d_ff;
+  int group_size;
+  int dtype;
+  int max_batch;
+} prox_shape;
+
+/* Opaque host-side handle: shape, launch plan and the caller's buffers. */
+typedef struct prox_layer prox_layer;
+
+/* Bytes the caller must allocate (device memory, 256-byte aligned) for:
+ *   weights_bytes   relaid exact weights (up/gate channel-major, down row-major)
+ *   proxy_bytes     packed INT4 proxy codes and their float32 scales
+ *   workspace_bytes per-call scratch: partial sums, counters, masks, s values
+ * Pure host function.  PROX_EINVAL on a null pointer or an invalid shape,
+ * PROX_EUNSUPPORTED on a shape outside the limits above.                    */
+prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
+                             size_t *proxy_bytes, size_t *workspace_bytes);
+
+/* Build a layer (Sec. 4.3: the INT4 proxy of W_up and W_gate is computed once
+ * and stays resident).  Enqueues on `stream`:
+ *   - relayout: W_up and W_gate transposed to channel-major rows (channel j's
+ *     up row followed by its gate row), W_down copied row-major;
+ *   - quantization: per group g of G input rows and per column j,
+ *     scale = max|W[i][j]| / 7 (float32), code = clamp(rint(W / scale), -7, 7)
+ *     (float32 divide, ties to even; an all-zero group has scale 0, codes 0),
+ *     stored as 4-bit (code + 8), packed along j per input row;
+ *   - zeroing of the workspace counters.
+ * Source weights must stay valid until the stream has run these kernels.
+ * The three buffers belong to the caller and must outlive the layer.
+ * On success *out receives a handle to free with prox_destroy_layer.        */
+prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
+                               const void *w_gate, const void *w_down,
+                               void *weights_buf, void *proxy_buf,
+                               void *workspace_buf, void *stream,
+                               prox_layer **out);
+
+/* Read back a prepared layer's INT4 codes (as signed int8 [d_model][d_ff], in
+ * the paper's layout) and scales (float32 [d_model/G][d_ff]) into caller
+ * device buffers.  Inspection only (used to check the quantizer bit for bit). */
+prox_status prox_export_proxy(const prox_layer *layer, int matrix /*0 up, 1 gate*/,
+                              int8_t *codes, float *scales, void *stream);
+
+/* One token: y = Prox-FFN(x) (batch 1, the decode hot path).
+ *   x          [d_model] layer dtype
+ *   threshold  tau of the Stage 1 input mask; an input survives iff
+ *              |x_i| >= threshold (so threshold <= 0 keeps every input and
+ *              +inf keeps none); NaN -> PROX_EINVAL
+ *   k          channels kept by the Stage 2 mask, 0 <= k <= d_ff (k = 0
+ *              gives y = 0, k = d_ff the dense result)
+ *   y          [d_model] layer dtype (written, never read)                  */
+prox_status prox_ffn_forward(const prox_layer *layer, const void *x,
+                             float threshold, int k, void *y, void *stream);
+
+/* `batch` independent tokens (1 <= batch <= max_batch), x and y [batch][d_model].
+ * Each token gets its own input mask and its own top-k mask; the union of
+ * the masks decides which weight rows are streamed, and every token's s is
+ * zero outside its own mask, so the result equals `batch` batch-1 calls.   */
+prox_status prox_ffn_forward_batch(const prox_layer *layer, const void *x,
+                                   int batch, float threshold, int k, void *y,
+                                   void *stream);
+
+/* Intermediate results of a forward call, for verification.  Every pointer
+ * is a caller device buffer or NULL (not written).                           */
+typedef struct {
+  int32_t *n1;       /* [batch]            surviving inputs per token          */
+  int32_t *idx;      /* [batch][d_model]   survivors, ascending               */
+  float *s_abs;      /* [batch][d_ff]      |s~| of the INT4 proxy             */
+  int32_t *sel;      /* [batch][d_ff]      selected channels, ascending (k used) */
+  float *s_sel;      /* [batch][d_ff]      exact s of sel[b][t] at t (k used) */
+  int32_t *n_union;  /* [1]                size of the union of the masks     */
+  int32_t *union_idx;/* [d_ff]             the union, ascending               */
+} prox_debug;
+
+/* prox_ffn_forward_batch plus a copy of its intermediate results into `dbg`. */
+prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x,
+                                   int batch, float threshold, int k, void *y,
+                                   const prox_debug *dbg, void *stream);
+
+/* Dense SwiGLU FFN on the same relaid weights (Sec. 2.1), the baseline:
+ * y = (x W_up . SiLU(x W_gate)) W_down for `batch` tokens.                   */
+prox_status prox_dense_ffn_forward(const prox_layer *layer, const void *x,
+                                   int batch, void *y, void *stream);
+
+/* A decode stack of n_layers FFN layers of one shape on a float32 residual
+ * stream r [batch][d_model] (updated in place): for each layer l,
+ *   x = cast(r / sqrt(mean(r^2) + eps)) (RMSNorm with unit gain),
+ *   y = Prox-FFN_l(x, thresholds[l], k) (or the dense FFN when k < 0),
+ *   r = r + y.
+ * thresholds is a HOST array [n_layers].  The layers may share one workspace. */
+prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
+                               const float *thresholds, int k, float *resid,
+                               int batch, float eps, void *stream);
+
+/* Release a handle (host memory only; the caller's buffers are untouched). */
+void prox_destroy_layer(prox_layer *layer);
+
+/* Text of the calling thread's last error ("" if none). */
+const char *prox_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROX_H_ */

@@ -1,0 +1,103 @@
+"""The C ABI library without a GPU: it loads, exports every function
+include/prox.h declares, and rejects bad arguments on the host before any
+HIP call (no kernel is launched by these tests)."""
+import ctypes
+import math
+
+import pytest
+
+from free_sparse_swiglu_amd import prox
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return prox.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = prox.header_symbols()
+    for want in ("prox_query_sizes", "prox_prepare_layer", "prox_ffn_forward",
+                 "prox_ffn_forward_batch", "prox_ffn_forward_debug",
+                 "prox_dense_ffn_forward", "prox_stack_forward", "prox_export_proxy",
+                 "prox_destroy_layer", "prox_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in prox.header_symbols():
+        assert hasattr(lib, name), f"{name} declared in prox.h but not exported"
+
+
+def _q(d_model, d_ff, G, dtype, mb=1):
+    sh = prox.prox_shape(d_model, d_ff, G, dtype, mb)
+    w, p, ws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = prox.load_library().prox_query_sizes(ctypes.byref(sh), ctypes.byref(w),
+                                              ctypes.byref(p), ctypes.byref(ws))
+    return st, w.value, p.value, ws.value
+
+
+def test_query_sizes_values(lib):
+    st, w, p, ws = _q(4096, 14336, 128, prox.PROX_BF16)
+    assert st == prox.PROX_OK
+    assert w >= 3 * 4096 * 14336 * 2
+    # packed codes (one byte per input row per column pair, up+gate) + fp32 scales
+    assert p >= 4096 * 14336 + 2 * (4096 // 128) * 14336 * 4
+    assert ws > 0
+    st, w1, p1, ws1 = _q(256, 688, 64, prox.PROX_F32)
+    assert st == prox.PROX_OK and w1 >= 3 * 256 * 688 * 4
+    # ragged last proxy tile: 688 = 2 * 256 + 176 columns
+    assert p1 >= 3 * 256 * 256
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4096, 14336, 100, prox.PROX_BF16), prox.PROX_EINVAL),       # d_model % G
+    ((4096, 14336, 32, prox.PROX_BF16), prox.PROX_EUNSUPPORTED),  # G not 64/128/256
+    ((0, 14336, 128, prox.PROX_BF16), prox.PROX_EINVAL),
+    ((4096, 0, 128, prox.PROX_BF16), prox.PROX_EINVAL),
+    ((4096, 14336, 128, 7), prox.PROX_EINVAL),                    # dtype
+    ((256 * 3, 1000, 64, prox.PROX_BF16), prox.PROX_EUNSUPPORTED), # d_model % 512 (bf16)
+    ((4096, 40000, 128, prox.PROX_BF16), prox.PROX_EUNSUPPORTED), # d_ff above 32768
+])
+def test_query_sizes_rejects(lib, args, status):
+    assert _q(*args)[0] == status
+    assert prox.prox_last_error() != ""
+
+
+def test_query_sizes_rejects_batch(lib):
+    assert _q(4096, 14336, 128, prox.PROX_BF16, 9)[0] == prox.PROX_EUNSUPPORTED
+    assert _q(4096, 14336, 128, prox.PROX_BF16, 0)[0] == prox.PROX_EINVAL
+
+
+def test_null_arguments_rejected_before_any_launch(lib):
+    P = ctypes.c_void_p
+    assert lib.prox_ffn_forward(None, P(16), 0.5, 3, P(16), None) == prox.PROX_EINVAL
+    assert lib.prox_ffn_forward_batch(None, P(16), 1, 0.5, 3, P(16), None) == prox.PROX_EINVAL
+    assert lib.prox_dense_ffn_forward(None, P(16), 1, P(16), None) == prox.PROX_EINVAL
+    h = ctypes.c_void_p()
+    sh = prox.prox_shape(512, 1024, 128, prox.PROX_BF16, 1)
+    assert lib.prox_prepare_layer(ctypes.byref(sh), None, None, None, None, None, None,
+                                  None, ctypes.byref(h)) == prox.PROX_EINVAL
+    assert lib.prox_prepare_layer(None, P(256), P(256), P(256), P(256), P(256), P(256),
+                                  None, ctypes.byref(h)) == prox.PROX_EINVAL
+    # misaligned buffers
+    assert lib.prox_prepare_layer(ctypes.byref(sh), P(256), P(256), P(256), P(258),
+                                  P(256), P(256), None, ctypes.byref(h)) == prox.PROX_EINVAL
+    assert lib.prox_stack_forward(None, 0, None, 3, None, 1, 1e-5, None) == prox.PROX_EINVAL
+    arr = (ctypes.c_void_p * 1)(None)
+    th = (ctypes.c_float * 1)(math.nan)
+    assert lib.prox_stack_forward(arr, 1, th, 3, P(256), 1, 1e-5, None) == prox.PROX_EINVAL
+    lib.prox_destroy_layer(None)  # no-op
+
+
+def test_costmodel_effective_sparsity_of_configs():
+    """Effective sparsity (Sec. 4.2 cost model) of the k choices used here:
+    k = 30% of d_ff with half the inputs kept gives e = 0.7 - 2/9 * 0.5."""
+    from free_sparse_swiglu_amd import costmodel, synth
+    k = synth.k_for(14336, 0.7)
+    assert k == 4301
+    s2 = 1 - k / 14336
+    e = costmodel.effective_sparsity(0.5, s2)
+    assert abs(e - (s2 - 1 / 9)) < 1e-12
+    assert [synth.k_for(14336, p) for p in (0.5, 0.6, 0.7)] == [7168, 5734, 4301]
+    assert [synth.k_for(17408, p) for p in (0.6, 0.7)] == [6963, 5222]
+    assert synth.k_for(28672, 0.7) == 8602 and synth.k_for(688, 0.7) == 206

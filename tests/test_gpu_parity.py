@@ -1,0 +1,306 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (checked element by element on the same seeded inputs):
+  - prepared INT4 codes and scales: bit-exact with the oracle's quantizer;
+  - Stage 1 survivors (count and ascending list): bit-exact;
+  - |s~|: max |diff| <= 1e-4 * max |s~| (float32 vs double summation);
+  - top-k mask: exactly k ascending channels, differing from the oracle's only
+    inside the 1e-3 tie band around the k-th value (tests/parity_utils.py);
+  - exact s of the selected channels: max |diff| <= 1e-4 * max |s|;
+  - y: max |diff| / max |y_ref| <= 2e-2 (bf16 weights, float32 accumulation)
+    or <= 1e-5 (float32 layer).
+Configurations: the tiny float32 layer, a ragged bf16 layer (several proxy
+tiles plus a partial one), and the 8B / 14B / 70B shapes at full size.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from free_sparse_swiglu_amd import prox, synth
+from tests.parity_utils import check_mask, expected_y, rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+RAGGED = synth.Config("ragged", 1024, 3000, 128, "bf16", "student_t", 0.5, 32, (0.7,))
+
+
+def _tol(cfg):
+    return 1e-5 if cfg.dtype == "f32" else 2e-2
+
+
+class Case:
+    """A layer on both sides: GPU prepared layer + oracle layer (+ dense s)."""
+
+    def __init__(self, cfg, layer=0, gen_device="cpu", max_batch=1):
+        self.cfg = cfg
+        W = synth.make_layer(cfg, layer, gen_device)
+        self.Wg_dev = [w.to(DEV) for w in W]
+        self.L = prox.prox_prepare_layer(*self.Wg_dev, cfg.group, max_batch)
+        self.Wnp = [w.float().cpu().numpy() for w in W]
+        self.ol = oracle.Layer(*self.Wnp, cfg.group)
+        calib = synth.make_inputs(cfg, cfg.n_calib, "calib", layer, gen_device)
+        self.tau = synth.calibrate_tau(calib, cfg.tau_quantile)
+
+    def inputs(self, n, purpose="test"):
+        return synth.make_inputs(self.cfg, n, purpose, 0, "cpu")
+
+
+_CASES = {}
+
+
+def get_case(cfg, gen_device="cpu", max_batch=1):
+    key = (cfg, gen_device, max_batch)
+    if key not in _CASES:
+        if cfg.d_model >= 4096:  # keep at most one full-size layer alive
+            for k2 in [k for k in _CASES if k[0].d_model >= 4096]:
+                del _CASES[k2]
+        _CASES[key] = Case(cfg, 0, gen_device, max_batch)
+    return _CASES[key]
+
+
+def _check_token(case, x_row_dev, x_np, tau, k, out, t=0, stats=None):
+    """Compare token t of a debug forward with the oracle."""
+    cfg = case.cfg
+    ref = oracle.forward(case.ol, x_np, tau, k)
+    n1 = int(out["n1"][t])
+    assert n1 == ref["idx"].size
+    assert out["idx"][t, :n1].cpu().numpy().tolist() == ref["idx"].tolist()
+    y = out["y"][t].float().cpu().numpy().astype(np.float64)
+    if k == 0:
+        assert not np.any(y)
+        return
+    s_abs = out["s_abs"][t].cpu().numpy().astype(np.float64)
+    e_s = rel_err(s_abs, np.abs(ref["s_t"]))
+    if np.max(np.abs(ref["s_t"])) > 0:
+        assert e_s <= 1e-4, f"|s~| error {e_s:.3e}"
+    else:
+        assert not np.any(s_abs)
+    sel = out["sel"][t, :k].cpu().numpy()
+    m = check_mask(sel, ref["sel"], ref["s_t"], k)
+    s_exact, _ = oracle.dense(x_np, *case.Wnp)
+    y_ref = expected_y(sel, ref["sel"], ref["y"], s_exact, case.Wnp[2])
+    e_y = rel_err(y, y_ref)
+    assert e_y <= _tol(cfg), f"y error {e_y:.3e} (k={k}, tau={tau})"
+    if out.get("s_sel") is not None and x_row_dev is not None:
+        s_sel = out["s_sel"][t, :k].cpu().numpy().astype(np.float64)
+        if out["sel"].shape[0] == 1:
+            e_ss = rel_err(s_sel, s_exact[sel])
+            assert e_ss <= 1e-4, f"exact s error {e_ss:.3e}"
+    if stats is not None:
+        stats.append(dict(k=k, n1=n1, band=m["band"], diff=m["diff"], e_y=e_y, e_s=e_s))
+
+
+# ---------------------------------------------------------------------------
+# Prepare
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [synth.CONFIGS["tiny"], RAGGED], ids=lambda c: c.name)
+def test_prepare_quantizer_bit_exact(cfg):
+    case = get_case(cfg)
+    for m, (q_or, sc_or) in enumerate(((case.ol.q_up, case.ol.sc_up),
+                                       (case.ol.q_gate, case.ol.sc_gate))):
+        codes, scales = prox.prox_export_proxy(case.L, m)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes.cpu().numpy(), q_or)
+        np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32),
+                                      sc_or.view(np.uint32))
+
+
+def test_prepare_quantizer_bit_exact_8b():
+    cfg = synth.CONFIGS["8b"]
+    W = synth.make_layer(cfg, 0, DEV)
+    L = prox.prox_prepare_layer(*W, cfg.group, 1)
+    for m in (0, 1):
+        codes, scales = prox.prox_export_proxy(L, m)
+        q_or, sc_or = oracle.quantize(W[m].float().cpu().numpy(), cfg.group)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), q_or)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), sc_or.view(np.uint32))
+
+
+def test_relayout_is_exact_copy():
+    cfg = RAGGED
+    W = synth.make_layer(cfg, 0, DEV)
+    L = prox.prox_prepare_layer(*W, cfg.group, 1)
+    torch.cuda.synchronize()
+    d, f = cfg.d_model, cfg.d_ff
+    wb = L.weights.view(torch.bfloat16)
+    wug = wb[: 2 * d * f].view(f, 2, d)
+    assert torch.equal(wug[:, 0, :], W[0].t())
+    assert torch.equal(wug[:, 1, :], W[1].t())
+    off = ((2 * d * f * 2 + 255) // 256 * 256) // 2
+    assert torch.equal(wb[off: off + f * d].view(f, d), W[2])
+
+
+# ---------------------------------------------------------------------------
+# Forward, small shapes (many inputs, edge cases)
+# ---------------------------------------------------------------------------
+def test_tiny_f32_parity():
+    cfg = synth.CONFIGS["tiny"]
+    case = get_case(cfg)
+    k = synth.k_for(cfg.d_ff, 0.7)
+    X = case.inputs(16)
+    stats = []
+    for t in range(X.shape[0]):
+        xd = X[t:t + 1].to(DEV)
+        out = prox.prox_ffn_forward_debug(case.L, xd, case.tau, k)
+        torch.cuda.synchronize()
+        _check_token(case, xd, X[t].numpy(), case.tau, k, out, stats=stats)
+    print("tiny:", stats[:3], "max e_y", max(s["e_y"] for s in stats))
+
+
+@pytest.mark.parametrize("k_frac", [0.0, 1 / 3000, 0.3, 0.5, 0.999, 1.0])
+def test_ragged_bf16_parity_k_sweep(k_frac):
+    case = get_case(RAGGED)
+    k = int(round(k_frac * RAGGED.d_ff))
+    X = case.inputs(3)
+    for t in range(X.shape[0]):
+        xd = X[t:t + 1].to(DEV)
+        out = prox.prox_ffn_forward_debug(case.L, xd, case.tau, k)
+        torch.cuda.synchronize()
+        _check_token(case, xd, X[t].float().numpy(), case.tau, k, out)
+
+
+@pytest.mark.parametrize("tau", [0.0, -1.0, float("inf"), 1e30, 2.5])
+def test_ragged_threshold_edges(tau):
+    case = get_case(RAGGED)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    X = case.inputs(2, "edges")
+    for t in range(X.shape[0]):
+        xd = X[t:t + 1].to(DEV)
+        out = prox.prox_ffn_forward_debug(case.L, xd, tau, k)
+        torch.cuda.synchronize()
+        _check_token(case, xd, X[t].float().numpy(), tau, k, out)
+        if math.isinf(tau):
+            assert int(out["n1"][0]) == 0
+            assert out["sel"][0, :k].cpu().tolist() == list(range(k))
+
+
+def test_product_entry_matches_debug_entry_and_is_deterministic():
+    case = get_case(RAGGED)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    x = case.inputs(1)[0].to(DEV)
+    y1 = prox.prox_ffn_forward(case.L, x, case.tau, k)
+    y2 = prox.prox_ffn_forward(case.L, x, case.tau, k)
+    yd = prox.prox_ffn_forward_debug(case.L, x[None], case.tau, k)["y"][0]
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), yd.view(torch.int16))
+
+
+def test_argument_errors_with_a_layer():
+    case = get_case(RAGGED)
+    x = case.inputs(1)[0].to(DEV)
+    with pytest.raises(prox.ProxError) as e:
+        prox.prox_ffn_forward(case.L, x, float("nan"), 10)
+    assert e.value.status == prox.PROX_EINVAL
+    with pytest.raises(prox.ProxError):
+        prox.prox_ffn_forward(case.L, x, 0.5, RAGGED.d_ff + 1)
+    with pytest.raises(prox.ProxError):
+        prox.prox_ffn_forward(case.L, x, 0.5, -1)
+    with pytest.raises(prox.ProxError):
+        prox.prox_ffn_forward_batch(case.L, torch.zeros(2, RAGGED.d_model, dtype=torch.bfloat16,
+                                                        device=DEV), 0.5, 10)
+
+
+# ---------------------------------------------------------------------------
+# Dense baseline
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [synth.CONFIGS["tiny"], RAGGED], ids=lambda c: c.name)
+def test_dense_parity(cfg):
+    case = get_case(cfg)
+    X = case.inputs(2, "dense")
+    for t in range(X.shape[0]):
+        y = prox.prox_dense_ffn_forward(case.L, X[t:t + 1].to(DEV))
+        torch.cuda.synchronize()
+        _, y_ref = oracle.dense(X[t].float().numpy(), *case.Wnp)
+        assert rel_err(y[0].float().cpu().numpy(), y_ref) <= _tol(cfg)
+
+
+# ---------------------------------------------------------------------------
+# Batch path: per-token masks, union-driven streaming
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [2, 3, 8])
+def test_batch_equals_independent_tokens(B):
+    case = get_case(RAGGED, max_batch=8)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    X = case.inputs(B, "batch")
+    xd = X.to(DEV)
+    out = prox.prox_ffn_forward_debug(case.L, xd, case.tau, k)
+    torch.cuda.synchronize()
+    sels = []
+    for t in range(B):
+        _check_token(case, xd[t], X[t].float().numpy(), case.tau, k, out, t=t)
+        sels.append(set(out["sel"][t, :k].cpu().tolist()))
+    nu = int(out["n_union"][0])
+    assert out["union_idx"][:nu].cpu().tolist() == sorted(set.union(*sels))
+    yb = prox.prox_ffn_forward_batch(case.L, xd, case.tau, k)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int16), out["y"].view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Stack: RMSNorm + FFN + residual over several layers
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("k_frac", [0.3, -1])
+def test_stack_parity(k_frac):
+    cfg = synth.Config("stacksmall", 1024, 2816, 128, "bf16", "student_t", 0.5, 32, (0.7,))
+    nl = 4
+    layers, olayers, taus = [], [], []
+    ws = None
+    for l in range(nl):
+        W = synth.make_layer(cfg, l, "cpu")
+        L = prox.prox_prepare_layer(*[w.to(DEV) for w in W], cfg.group, 1, workspace=ws)
+        ws = L.workspace
+        layers.append(L)
+        olayers.append(oracle.Layer(*[w.float().numpy() for w in W], cfg.group))
+        taus.append(synth.layer_tau(cfg, l, "cpu") * 0.5)
+    k = synth.k_for(cfg.d_ff, 0.7) if k_frac > 0 else cfg.d_ff
+    R0 = synth.make_inputs(cfg, 3, "stack", 0, "cpu").float()
+    for t in range(R0.shape[0]):
+        r = R0[t].clone().to(DEV)
+        prox.prox_stack_forward(layers, taus, k if k_frac > 0 else -1, r)
+        torch.cuda.synchronize()
+        r_ref, _ = oracle.stack_forward(olayers, taus, k, R0[t].numpy())
+        assert rel_err(r.cpu().numpy(), r_ref) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Full-size shapes (8B, 14B, 70B), in the launch configuration bench.py times
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["8b", "14b", "70b"])
+def test_full_size_parity(name):
+    cfg = synth.CONFIGS[name]
+    case = get_case(cfg, DEV, 8 if name == "70b" else 1)
+    X = synth.make_inputs(cfg, 2, "test", 0, DEV)
+    stats = []
+    for sp in cfg.sparsities:
+        k = synth.k_for(cfg.d_ff, sp)
+        for t in range(X.shape[0]):
+            xd = X[t:t + 1]
+            out = prox.prox_ffn_forward_debug(case.L, xd, case.tau, k)
+            torch.cuda.synchronize()
+            _check_token(case, xd, X[t].float().cpu().numpy(), case.tau, k, out, stats=stats)
+    print(name, stats)
+    # the dense baseline of the same shape
+    y = prox.prox_dense_ffn_forward(case.L, X[:1])
+    torch.cuda.synchronize()
+    _, y_ref = oracle.dense(X[0].float().cpu().numpy(), *case.Wnp)
+    assert rel_err(y[0].float().cpu().numpy(), y_ref) <= 2e-2
+
+
+@pytest.mark.parametrize("B", [2, 4, 8])
+def test_70b_batch_parity(B):
+    cfg = synth.CONFIGS["70b"]
+    case = get_case(cfg, DEV, 8)
+    k = synth.k_for(cfg.d_ff, 0.7)
+    X = synth.make_inputs(cfg, B, "batch", 0, DEV)
+    out = prox.prox_ffn_forward_debug(case.L, X, case.tau, k)
+    torch.cuda.synchronize()
+    for t in range(B):
+        _check_token(case, X[t], X[t].float().cpu().numpy(), case.tau, k, out, t=t)
