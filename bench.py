@@ -1,0 +1,398 @@
+#!/usr/bin/env python3
+"""Benchmark of the Prox two-stage sparse SwiGLU FFN decode step on one GPU.
+
+Default workload: one 8B-shaped FFN layer (d_model 4096, d_ff 14336, bf16,
+INT4 proxy with G = 128) at 70% FFN sparsity (k = 4301 of 14336 channels),
+batch 1.  A step is one full forward of the layer (Stage 1 threshold +
+compaction + INT4 proxy, top-k mask, Stage 2 exact up/gate + SwiGLU, Stage 2
+down projection) for one token.  Steps rotate over a ring of distinct seeded
+layers (8 x 415 MB by default) and inputs so that the 256 MB last-level cache
+cannot serve a repeated layer: the bytes come from HBM.
+
+Printed: one JSON line.  value = achieved GB/s on the algorithmic bytes of a
+step (weights actually needed, x, y) over the measured step time; also
+microseconds per layer, the per-kernel breakdown (HIP events recorded by the
+library between its kernels, on the launch stream), the dense bf16 baseline on
+the same relaid weights, and the CPU oracle timed on the host cores.
+
+Other workloads (--workload): 14b (k at 70%), 70b (batch 1/2/4/8), stack8b
+(32 layers x 128 sequential tokens, tokens/s), copy (a plain device copy of
+known size, used to scale rocprofv3 byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+KERNEL_NAMES = ["stage1_proxy", "topk", "stage2_upgate", "stage2_down"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("prox_kernels.hip", "prox_api.hip", "prox_internal.h"):
+        with open(os.path.join(ROOT, "free_sparse_swiglu_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch of the dominant kernel from committed rocprofv3
+    counter summaries, if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t
+
+
+def algorithmic_bytes(cfg, n1, groups_touched, k, batch=1, union=None):
+    """Bytes the step must move: proxy codes of surviving rows and scales of
+    touched groups (Stage 1), up+gate rows and down rows of the selected
+    channels (Stage 2), x and y."""
+    import math
+    ntile = math.ceil(cfg.d_ff / 256)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    stage1 = n1 * ntile * 256 + groups_touched * 2 * cfg.d_ff * 4
+    m = k if union is None else union
+    upgate = m * 2 * cfg.d_model * esz
+    down = m * cfg.d_model * esz
+    io = 2 * batch * cfg.d_model * esz
+    return dict(stage1=stage1, upgate=upgate, down=down, io=io,
+                total=stage1 + upgate + down + io)
+
+
+def build_ring(cfg, ring, max_batch=1):
+    import torch
+
+    from free_sparse_swiglu_amd import prox, synth
+    layers, taus = [], []
+    ws = None
+    for l in range(ring):
+        W = synth.make_layer(cfg, l, "cuda")
+        L = prox.prox_prepare_layer(*W, cfg.group, max_batch, workspace=ws)
+        ws = L.workspace
+        torch.cuda.synchronize()
+        del W
+        layers.append(L)
+        taus.append(synth.layer_tau(cfg, l, "cuda"))
+    return layers, taus
+
+
+def time_loop(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        fn(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps  # ms per step
+
+
+def profile_kernels(call, steps, n_events):
+    """Average per-kernel milliseconds from library-recorded events."""
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(steps)]
+    nrec = 0
+    for i in range(steps):
+        nrec = call(i, evs[i])
+    torch.cuda.synchronize()
+    sums = [0.0] * (nrec - 1)
+    for i in range(steps):
+        for j in range(nrec - 1):
+            sums[j] += evs[i][j].elapsed_time(evs[i][j + 1])
+    return [s / steps for s in sums]
+
+
+def cpu_baseline(cfg, k, tau, budget_s, bytes_per_step):
+    """The oracle as it stands, single-threaded C, on a bounded sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from free_sparse_swiglu_amd import synth
+    W = [w.float().cpu().numpy() for w in synth.make_layer(cfg, 0, "cuda")]
+    ol = oracle.Layer(*W, cfg.group)  # prepare (quantize), not timed
+    X = synth.make_inputs(cfg, 512, "cpu-sample", 0, "cuda").float().cpu().numpy()
+    n, t_total = 0, 0.0
+    while n < X.shape[0] and (t_total < budget_s or n == 0):
+        t0 = time.perf_counter()
+        oracle.forward(ol, X[n], tau, k)
+        t_total += time.perf_counter() - t0
+        n += 1
+    sec = t_total / n
+    return dict(value=round(bytes_per_step / sec / 1e9, 4), unit="GB/s",
+                us_per_layer=round(sec * 1e6, 1), cores=1, kind="oracle",
+                sample=f"oracle forward (input mask, INT4 proxy, top-k, exact Stage 2) of "
+                       f"{n} tokens on layer 0 of the {cfg.name} ring, single-threaded C "
+                       f"(host has {os.cpu_count()} logical CPUs)")
+
+
+def bench_single_layer(args, name):
+    import numpy as np
+    import torch
+
+    from free_sparse_swiglu_amd import costmodel, prox, synth
+    cfg = synth.CONFIGS[name]
+    k = synth.k_for(cfg.d_ff, args.sparsity)
+    layers, taus = build_ring(cfg, args.ring)
+    R = len(layers)
+    NX = 16
+    X = [synth.make_inputs(cfg, NX, "bench", l, "cuda") for l in range(R)]
+    y = torch.empty(cfg.d_model, dtype=X[0].dtype, device="cuda")
+
+    # Survivor counts of the bench inputs, from the library's own compaction.
+    n1s, gts = [], []
+    for l in range(R):
+        for t in range(NX):
+            out = prox.prox_ffn_forward_debug(layers[l], X[l][t:t + 1], taus[l], k)
+            idx = out["idx"][0, :int(out["n1"][0])].cpu().numpy()
+            n1s.append(idx.size)
+            gts.append(np.unique(idx // cfg.group).size)
+    torch.cuda.synchronize()
+    n1m, gtm = float(np.mean(n1s)), float(np.mean(gts))
+    ab = algorithmic_bytes(cfg, n1m, gtm, k)
+
+    def step(i):
+        l = i % R
+        prox.prox_ffn_forward(layers[l], X[l][(i // R) % NX], taus[l], k, y)
+
+    ms = time_loop(step, args.steps, args.warmup)
+
+    def pstep(i, evs):
+        l = i % R
+        return prox.prox_ffn_forward_profiled(layers[l], X[l][(i // R) % NX][None], taus[l], k,
+                                              evs, y[None])[1]
+    kms = profile_kernels(pstep, min(args.steps, 200), 6)
+
+    def dstep(i):
+        l = i % R
+        prox.prox_dense_ffn_forward(layers[l], X[l][(i // R) % NX], y)
+    dms = time_loop(dstep, args.steps, args.warmup)
+
+    def dpstep(i, evs):
+        l = i % R
+        return prox.prox_dense_ffn_forward_profiled(layers[l], X[l][(i // R) % NX][None], evs,
+                                                    y[None])[1]
+    dkms = profile_kernels(dpstep, min(args.steps, 100), 3)
+
+    # Graph-launched step (same kernels, one replay per ring pass).
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(R):
+                step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                step(i)
+        reps = max(1, args.steps // R)
+        graph_ms = time_loop(lambda i: g.replay(), reps, 2) / R
+    except Exception as e:  # capture unsupported: report eager numbers only
+        print(f"graph capture skipped: {e}", file=sys.stderr)
+
+    # Other sparsities of the same shape (shorter loops).
+    others = {}
+    for sp in cfg.sparsities:
+        if abs(sp - args.sparsity) < 1e-9:
+            continue
+        kk = synth.k_for(cfg.d_ff, sp)
+
+        def ostep(i, kk=kk):
+            l = i % R
+            prox.prox_ffn_forward(layers[l], X[l][(i // R) % NX], taus[l], kk, y)
+        oms = time_loop(ostep, max(20, args.steps // 2), 5)
+        ob = algorithmic_bytes(cfg, n1m, gtm, kk)["total"]
+        others[f"{int(round(sp * 100))}%"] = dict(k=kk, us_per_layer=round(oms * 1e3, 2),
+                                                  GBps=round(ob / (oms * 1e-3) / 1e9, 1),
+                                                  speedup_vs_dense=round(dms / oms, 3))
+
+    kern = {}
+    kbytes = dict(stage1_proxy=ab["stage1"] + cfg.d_model * 2, topk=None,
+                  stage2_upgate=ab["upgate"] + cfg.d_model * 2, stage2_down=ab["down"])
+    for nm, t in zip(KERNEL_NAMES, kms):
+        b = kbytes.get(nm)
+        kern[nm] = dict(us=round(t * 1e3, 2),
+                        GBps=round(b / (t * 1e-3) / 1e9, 1) if b else None)
+    dom = "stage2_upgate"
+    dom_us = kern[dom]["us"]
+    achieved = kbytes[dom] / (dom_us * 1e-6) / 1e9
+    traffic = load_traffic(name)
+    roof = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
+                unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
+                bytes_per_launch=int(kbytes[dom]),
+                traffic=(traffic or {}).get("bytes_per_launch") if traffic else None)
+
+    s1 = 1.0 - n1m / cfg.d_model
+    s2 = 1.0 - k / cfg.d_ff
+    res = dict(
+        metric="us/FFN layer and achieved HBM GB/s at 70% sparsity, 8B-shaped, batch 1"
+        if name == "8b" else f"us/FFN layer and achieved HBM GB/s, {name}-shaped, batch 1",
+        value=round(ab["total"] / (ms * 1e-3) / 1e9, 1),
+        unit="GB/s",
+        n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 5),
+        us_per_layer=round(ms * 1e3, 2),
+        us_per_layer_graph=round(graph_ms * 1e3, 2) if graph_ms else None,
+        hbm_frac=round(ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=f"{name}-shaped single FFN layer, batch 1",
+                    d_model=cfg.d_model, d_ff=cfg.d_ff, group=cfg.group, k=k,
+                    sparsity=args.sparsity, ring_layers=R, tau_quantile=cfg.tau_quantile,
+                    mean_n1=round(n1m, 1), realised_s1=round(s1, 4), s2=round(s2, 4),
+                    effective_sparsity=round(costmodel.effective_sparsity(s1, s2), 4),
+                    bytes_per_step=int(ab["total"])),
+        kernels=kern,
+        dense=dict(us_per_layer=round(dms * 1e3, 2),
+                   GBps=round(3 * cfg.d_model * cfg.d_ff * 2 / (dms * 1e-3) / 1e9, 1),
+                   kernels=dict(upgate_us=round(dkms[0] * 1e3, 2), down_us=round(dkms[1] * 1e3, 2))),
+        speedup_vs_dense=round(dms / ms, 3),
+        other_sparsities=others,
+        roofline=roof,
+    )
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, k, taus[0], args.cpu_seconds, ab["total"])
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def bench_batch(args):
+    import numpy as np
+    import torch
+
+    from free_sparse_swiglu_amd import prox, synth
+    cfg = synth.CONFIGS["70b"]
+    k = synth.k_for(cfg.d_ff, args.sparsity)
+    layers, taus = build_ring(cfg, args.ring, max_batch=8)
+    R = len(layers)
+    out = {}
+    for B in cfg.batches:
+        X = [synth.make_inputs(cfg, B, f"bench{B}", l, "cuda") for l in range(R)]
+        y = torch.empty_like(X[0])
+        unions = []
+        for l in range(R):
+            o = prox.prox_ffn_forward_debug(layers[l], X[l], taus[l], k)
+            unions.append(int(o["n_union"][0]) if B > 1 else k)
+        ms = time_loop(lambda i: prox.prox_ffn_forward_batch(layers[i % R], X[i % R], taus[i % R],
+                                                             k, y), args.steps, args.warmup)
+        dms = time_loop(lambda i: prox.prox_dense_ffn_forward(layers[i % R], X[i % R], y),
+                        args.steps, args.warmup)
+        out[f"B{B}"] = dict(us_per_step=round(ms * 1e3, 2), dense_us=round(dms * 1e3, 2),
+                            speedup_vs_dense=round(dms / ms, 3),
+                            mean_union=float(np.mean(unions)),
+                            union_frac=round(float(np.mean(unions)) / cfg.d_ff, 4))
+    return dict(metric="us per batched FFN step, 70B-shaped, 70% sparsity", unit="us",
+                n_gpus=1, steps=args.steps, warmup=args.warmup, dtype="bf16",
+                data="synthetic", config=dict(workload="70B-shaped single FFN layer, "
+                                                       "batch 1/2/4/8", k=k, ring_layers=R),
+                batches=out)
+
+
+def bench_stack(args):
+    import torch
+
+    from free_sparse_swiglu_amd import calibrate, prox, synth
+    cfg = synth.CONFIGS["stack8b"]
+    k = synth.k_for(cfg.d_ff, args.sparsity)
+    layers = []
+    ws = None
+    for l in range(cfg.layers):
+        W = synth.make_layer(cfg, l, "cuda")
+        L = prox.prox_prepare_layer(*W, cfg.group, 8, workspace=ws)
+        ws = L.workspace
+        torch.cuda.synchronize()
+        del W
+        layers.append(L)
+    calib = synth.make_inputs(cfg, cfg.n_calib, "calib", 0, "cuda").float()
+    taus = calibrate.sequential_thresholds(layers, calib, cfg.tau_quantile, k)
+    ntok = 128
+    R0 = synth.make_inputs(cfg, ntok, "stack", 0, "cuda").float()
+    r = R0.clone()
+
+    def run_tokens(kk):
+        r.copy_(R0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(ntok):
+            prox.prox_stack_forward(layers, taus, kk, r[t])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    run_tokens(k)
+    sec = run_tokens(k)
+    dsec = run_tokens(-1)
+    return dict(metric="tokens/s of a 32-layer 8B-shaped FFN stack, batch 1, 70% sparsity",
+                value=round(ntok / sec, 1), unit="tokens/s", n_gpus=1, dtype="bf16",
+                data="synthetic", higher_is_better=True,
+                config=dict(workload="32 x 8B-shaped FFN layers + RMSNorm + residual, "
+                                     "128 sequential tokens", k=k, layers=cfg.layers),
+                dense_tokens_per_s=round(ntok / dsec, 1), speedup_vs_dense=round(dsec / sec, 3),
+                us_per_layer=round(sec / ntok / cfg.layers * 1e6, 2),
+                thresholds=[round(t, 5) for t in taus])
+
+
+def bench_copy(args):
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    ms = time_loop(lambda i: b.copy_(a), args.steps, args.warmup)
+    return dict(metric="device copy", bytes_read=n, bytes_written=n, ms=round(ms, 4),
+                GBps=round(2 * n / (ms * 1e-3) / 1e9, 1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="8b", choices=["8b", "14b", "70b", "stack8b", "copy"])
+    ap.add_argument("--sparsity", type=float, default=0.7)
+    ap.add_argument("--ring", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the multi-GPU split is a design note, not a measured path)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.workload in ("8b", "14b"):
+        res = bench_single_layer(args, args.workload)
+    elif args.workload == "70b":
+        res = bench_batch(args)
+    elif args.workload == "stack8b":
+        res = bench_stack(args)
+    else:
+        res = bench_copy(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

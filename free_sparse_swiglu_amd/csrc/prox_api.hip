@@ -88,7 +88,7 @@ Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch) {
   p.esz = bf16 ? 2 : 4;
   p.ngroups = d_model / G;
   p.ntile = (d_ff + kTile - 1) / kTile;
-  p.nchunk = (p.ngroups + 3) / 4;
+  p.nchunk = (d_model / 64 + 7) / 8;  // proxy work-groups per tile (8 slices of 64 rows)
   p.ncol = d_model / kDownCols;
   int nrc = 512 / p.ncol;
   if (nrc < 1) nrc = 1;
@@ -128,39 +128,69 @@ Layout make_layout(const Plan &p) {
 
 namespace {
 
+// Optional instrumentation: caller-owned HIP events recorded on the launch
+// stream before the first kernel and after each kernel of a call.
+struct EventLog {
+  void *const *ev;
+  int cap;
+  int n;
+  hipError_t mark(hipStream_t s) {
+    if (!ev) return hipSuccess;
+    if (n >= cap) return hipErrorInvalidValue;
+    return hipEventRecord((hipEvent_t)ev[n++], s);
+  }
+};
+
 // Stage 1, top-k and Stage 2 for `batch` tokens; writes y.
 prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau,
-                        int k, void *y, float *resid, hipStream_t s) {
+                        int k, void *y, float *resid, hipStream_t s,
+                        EventLog *log = nullptr) {
   const prox::Plan &p = L->plan;
   const prox::Bufs &b = L->bufs;
+  EventLog none{nullptr, 0, 0};
+  EventLog &lg = log ? *log : none;
   hipError_t e;
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   if (k == 0) {
     e = prox::launch_zero_y(p, y, batch, s);
     if (e != hipSuccess) return hip_fail(e, "zero output");
+    if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
     return PROX_OK;  // y = 0 adds nothing to the residual
   }
   if ((e = prox::launch_proxy(p, b, x, batch, tau, s)) != hipSuccess)
     return hip_fail(e, "stage 1 proxy kernel");
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = prox::launch_topk(p, b, batch, k, s)) != hipSuccess)
     return hip_fail(e, "top-k kernel");
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   const int mode = batch == 1 ? 0 : 1;
-  if (mode == 1 && (e = prox::launch_union(p, b, batch, k, s)) != hipSuccess)
-    return hip_fail(e, "mask union kernel");
+  if (mode == 1) {
+    if ((e = prox::launch_union(p, b, batch, k, s)) != hipSuccess)
+      return hip_fail(e, "mask union kernel");
+    if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
+  }
   if ((e = prox::launch_upgate(p, b, x, batch, mode, k, s)) != hipSuccess)
     return hip_fail(e, "stage 2 up/gate kernel");
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = prox::launch_down(p, b, batch, mode, k, y, resid, s)) != hipSuccess)
     return hip_fail(e, "stage 2 down kernel");
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   return PROX_OK;
 }
 
 prox_status run_dense(const prox_layer *L, const void *x, int batch, void *y,
-                      float *resid, hipStream_t s) {
+                      float *resid, hipStream_t s, EventLog *log = nullptr) {
   const prox::Plan &p = L->plan;
+  EventLog none{nullptr, 0, 0};
+  EventLog &lg = log ? *log : none;
   hipError_t e;
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = prox::launch_upgate(p, L->bufs, x, batch, 2, p.d_ff, s)) != hipSuccess)
     return hip_fail(e, "dense up/gate kernel");
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = prox::launch_down(p, L->bufs, batch, 2, p.d_ff, y, resid, s)) != hipSuccess)
     return hip_fail(e, "dense down kernel");
+  if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   return PROX_OK;
 }
 
@@ -362,6 +392,47 @@ prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
                                            L->bufs.ybuf, resid, s);
     if (st != PROX_OK) return st;
   }
+  return PROX_OK;
+}
+
+prox_status prox_ffn_forward_profiled(const prox_layer *layer, const void *x, int batch,
+                                      float threshold, int k, void *y,
+                                      void *const *events, int n_events, int *n_recorded,
+                                      void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, batch, threshold, k, y);
+  if (st != PROX_OK) return st;
+  if (!events || n_events < 6 || !n_recorded)
+    return fail(PROX_EINVAL, "events (at least 6) and n_recorded are required");
+  EventLog lg{events, n_events, 0};
+  st = run_forward(layer, x, batch, threshold, k, y, nullptr, (hipStream_t)stream, &lg);
+  *n_recorded = lg.n;
+  return st;
+}
+
+prox_status prox_dense_ffn_forward_profiled(const prox_layer *layer, const void *x,
+                                            int batch, void *y, void *const *events,
+                                            int n_events, int *n_recorded, void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, batch, 0.0f, 0, y);
+  if (st != PROX_OK) return st;
+  if (!events || n_events < 3 || !n_recorded)
+    return fail(PROX_EINVAL, "events (at least 3) and n_recorded are required");
+  EventLog lg{events, n_events, 0};
+  st = run_dense(layer, x, batch, y, nullptr, (hipStream_t)stream, &lg);
+  *n_recorded = lg.n;
+  return st;
+}
+
+prox_status prox_rmsnorm(const prox_layer *layer, const float *resid, int batch, float eps,
+                         void *x, void *stream) {
+  g_err.clear();
+  if (!layer || !resid || !x) return fail(PROX_EINVAL, "layer, resid and x are required");
+  if (batch < 1 || batch > prox::kMaxBatch)
+    return fail(PROX_EINVAL, "batch %d outside [1, %d]", batch, prox::kMaxBatch);
+  if (!(eps >= 0.0f)) return fail(PROX_EINVAL, "eps must be >= 0");
+  hipError_t e = prox::launch_rmsnorm(layer->plan, resid, batch, eps, x, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel");
   return PROX_OK;
 }
 

@@ -26,7 +26,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 struct Bufs {
   // weights_buf
   void *wug;       // [d_ff][2][d_model] dtype: channel j's up row, then gate row
-  void *wd;        // [d_ff][d_model]    dtype: W_down as given
+  void *wd;        // [d_model/256][d_ff][256] dtype: W_down in 256-column chunks
   // proxy_buf
   uint8_t *pq;     // [ntile][d_model][256] bytes: (code + 8) nibbles, up | gate
   float *psc;      // [ntile][ngroups][2][256] float32 scales
@@ -50,7 +50,7 @@ struct Plan {
   int esz;          // bytes per element
   int ngroups;      // d_model / G
   int ntile;        // ceil(d_ff / 256)
-  int nchunk;       // ceil(ngroups / 4): proxy work-groups per tile
+  int nchunk;       // ceil(d_model / 512): proxy work-groups per tile
   int ncol;         // d_model / 256
   int nrc;          // row chunks of the down projection
   int upgate_cap;   // max work-groups of the up/gate kernel

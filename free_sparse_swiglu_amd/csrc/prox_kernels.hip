@@ -62,11 +62,57 @@ __device__ __forceinline__ float round_elem(float v) {
     return v;
 }
 
+// Cache policy of weight-stream loads: non-temporal (each weight byte is read
+// once per call; keeping it out of the caches lifts streaming bandwidth).
+constexpr int kNT = 2;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
                                                             uint32_t bytes) {
   // raw buffer: stride 0, num_records = bytes; out-of-range reads return 0.
   return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes,
                                            0x00020000);
+}
+
+// Cross-work-group exchange of partial sums.  Partials are written and read
+// with agent-scope atomic accesses, which are coherent across the XCDs' L2
+// caches on their own (write-through / read-through), so no L2-wide
+// writeback or invalidate is needed.  A work-group publishes its partials,
+// waits until its own stores have completed, and only then counts its
+// arrival; the last arrival reads every partial.
+__device__ __forceinline__ void xstore(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float xload(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// sum_{c < n} p[c * stride], loads issued 16 at a time before any is used,
+// added in index order (deterministic).
+__device__ __forceinline__ float xsum_strided(const float *p, int n, size_t stride) {
+  float acc = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = xload(p + (size_t)min(c0 + u, n - 1) * stride);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += (c0 + u < n) ? v[u] : 0.0f;
+  }
+  return acc;
+}
+
+// Returns true in every thread of the last work-group to arrive at *cnt
+// (of `total`), which also resets the counter for the next launch.
+__device__ __forceinline__ bool arrive_last(unsigned *cnt, unsigned total, int *s_flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own partial stores done
+  __syncthreads();                                   // ... in every wave
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == total - 1u;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
 }
 
 // Sum over the 64 lanes of a wave, returned uniform: DPP within each row of
@@ -195,6 +241,18 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void *w_up,
   }
 }
 
+// W_down [d_ff][d_model] -> wd[c][j][0..256): output-column chunks of 256
+// stored one after another, so the rows a down-projection work-group reads
+// for one chunk are contiguous 256-column runs.
+template <bool BF16>
+__global__ __launch_bounds__(256) void retile_down_kernel(const void *w_down, void *wd,
+                                                          int d_model, int d_ff) {
+  typedef typename std::conditional<BF16, uint16_t, float>::type E;
+  const int j = blockIdx.x, cc = blockIdx.y, c = threadIdx.x;
+  ((E *)wd)[((size_t)cc * d_ff + j) * kDownCols + c] =
+      ((const E *)w_down)[(size_t)j * d_model + cc * kDownCols + c];
+}
+
 // One thread per proxy column of a tile, one work-group per (group, tile,
 // matrix).  scale = absmax / 7, code = clamp(rint(w / scale), -7, 7), both
 // divisions correctly rounded float32; stored as (code + 8) nibbles, two
@@ -252,16 +310,22 @@ __global__ __launch_bounds__(256) void export_proxy_kernel(
 // K-c  Stage 1: threshold + compact + INT4 proxy up/gate GEMV + SwiGLU
 //      (Sec. 4.1, m_x and u~/h~ equations; Sec. 4.3, fused Stage 1 kernel)
 // ---------------------------------------------------------------------------
-// Grid (nchunk, ntile), 4 waves.  Wave w of chunk c handles scale group
-// g = 4c + w of column tile t.  It finds the group's surviving rows with one
-// ballot per 64-row slice (the compaction never leaves registers), parks the
-// masked x values of the group in LDS, then streams only the surviving rows'
-// 256-byte code runs, 16 rows in flight while the previous 16 are consumed.
-// Lane l covers 8 consecutive columns: lanes 0-31 the up proxy, lanes 32-63
-// the gate proxy of the same columns.  Since
-//   sum_i x_i * code_i = sum_i x_i * nib_i - 8 * sum_i x_i,
-// each code costs one byte->float conversion and one FMA per token, and the
-// -8 offset and the group scale are applied once per group.
+// Grid (nchunk, ntile), 8 waves.  Wave w of chunk c handles the 64-row slice
+// 8c + w of column tile t.  It finds the slice's surviving rows with one
+// ballot (the compaction never leaves registers and LDS), parks their row
+// numbers and masked x values in LDS, then streams only those rows' 256-byte
+// code runs, 16 rows in flight while the previous 16 are consumed.  Lane l
+// covers 8 consecutive columns: lanes 0-31 the up proxy, lanes 32-63 the
+// gate proxy of the same columns.  A code is stored as nib = q + 8, and
+//   sum_i x_i q_i = sum_i x_i nib_i - 8 sum_i x_i,
+// so the offset and the group scale are applied once per slice.
+//   bf16 layers: two surviving rows a, b are taken together; for each column
+//   the pair (128 + nib_a, 128 + nib_b) is formed as two bf16 values by
+//   placing the nibbles under the exponent byte 0x43 (128 + n is exact in
+//   bf16 for n < 128), and one v_dot2_f32_bf16 with (x_a, x_b) adds
+//   x_a nib_a + x_b nib_b + 128 (x_a + x_b); the slice then removes
+//   136 sum x instead of 8 sum x.
+//   float32 layers: byte -> float conversion and one FMA per code.
 // The last work-group to finish a tile adds the partials of all chunks in a
 // fixed order and writes |s~| = |u~ * SiLU(g~)| for the tile's columns.
 struct ProxyArgs {
@@ -275,19 +339,20 @@ struct ProxyArgs {
   float *sabs;
 };
 
-template <int NB, bool BF16, int NSL>
-__global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
-  constexpr int U = 16;            // rows per pipeline stage
-  constexpr int GR = NSL * 64;     // rows per group
-  constexpr int LL = GR + 3 * U;   // list length incl. padding for prefetch
-  __shared__ float red[4][512];
-  __shared__ __attribute__((aligned(16))) int rl[4][LL];      // surviving rows of the group
-  __shared__ __attribute__((aligned(16))) float xc[4][NB][LL]; // their x (0 where a token drops them)
+template <int NB, bool BF16>
+__global__ __launch_bounds__(512) void proxy_kernel(ProxyArgs a) {
+  constexpr int NW = 8;             // waves (64-row slices) per work-group
+  constexpr int U = 16;             // rows per pipeline stage
+  constexpr int LL = 64 + 3 * U;    // list length incl. padding for prefetch
+  __shared__ float red[NW][512];
+  __shared__ __attribute__((aligned(16))) int rl[NW][LL];       // surviving rows
+  __shared__ __attribute__((aligned(16))) float xc[NW][NB][LL]; // their x (0 if a token drops them)
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunk = blockIdx.x, t = blockIdx.y;
-  const int g = chunk * 4 + wv;
+  const int sl = chunk * NW + wv;    // 64-row slice
+  const int nsl = a.d_model >> 6;
 
   float acc[NB][8];
 #pragma unroll
@@ -295,38 +360,30 @@ __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[b][c] = 0.0f;
 
-  if (g < a.ngroups) {
-    // Input mask of the group's rows (Sec. 4.1, m_x), compacted in LDS: the
+  if (sl < nsl) {
+    // Input mask of the slice's rows (Sec. 4.1, m_x), compacted in LDS: the
     // union over tokens decides which rows are read; each token keeps its
     // own x or 0.
     float xsum[NB];
+    float xm[NB];
+    uint64_t un = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) xsum[b] = 0.0f;
-    int cnt = 0;
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-      float xm[NB];
-      uint64_t un = 0;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float xl;
-        const uint64_t mk =
-            slice_mask<BF16>(a.x, (size_t)b * a.d_model + g * GR + sl * 64, a.tau, xl);
-        xm[b] = ((mk >> lane) & 1ull) ? xl : 0.0f;
-        xsum[b] += wave_sum(xm[b]);
-        un |= mk;
-      }
-      if ((un >> lane) & 1ull) {
-        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
-                                  (unsigned)(un >> 32),
-                                  __builtin_amdgcn_mbcnt_lo((unsigned)un, 0u));
-        rl[wv][pos] = sl * 64 + lane;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) xc[wv][b][pos] = xm[b];
-      }
-      cnt += (int)__popcll(un);
+    for (int b = 0; b < NB; ++b) {
+      float xl;
+      const uint64_t mk = slice_mask<BF16>(a.x, (size_t)b * a.d_model + sl * 64, a.tau, xl);
+      xm[b] = ((mk >> lane) & 1ull) ? xl : 0.0f;
+      xsum[b] = wave_sum(xm[b]);
+      un |= mk;
     }
-    // Padding: row 0 of the group (a valid address) with x = 0.
+    const int cnt = (int)__popcll(un);
+    if ((un >> lane) & 1ull) {
+      const int pos = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(un >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((unsigned)un, 0u));
+      rl[wv][pos] = lane;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xc[wv][b][pos] = xm[b];
+    }
+    // Padding: row 0 of the slice (a valid address) with x = 0.
     if (lane < 3 * U) {
       rl[wv][cnt + lane] = 0;
 #pragma unroll
@@ -335,12 +392,11 @@ __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
     __builtin_amdgcn_wave_barrier();
 
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(a.pq + (size_t)t * a.d_model * kTileBytes,
-                  (uint32_t)a.d_model * kTileBytes);
+        make_rsrc(a.pq + (size_t)t * a.d_model * kTileBytes, (uint32_t)a.d_model * kTileBytes);
     const uint32_t voff = (uint32_t)lane * 4u;
-    const uint32_t gbase = (uint32_t)g * GR * kTileBytes;
+    const uint32_t sbase = (uint32_t)sl * 64u * kTileBytes;
 
-    // Stage `base`: 16 row indices (uniform) and their code words.
+    // Stage `base`: 16 row numbers (uniform) and their code words.
     auto fetch = [&](int base, uint32_t (&w)[U]) {
 #pragma unroll
       for (int q = 0; q < U / 4; ++q) {
@@ -349,42 +405,74 @@ __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(rr[e]);
-          w[4 * q + e] = __builtin_amdgcn_raw_buffer_load_b32(
-              rs, voff, gbase + row * kTileBytes, 0);
+          w[4 * q + e] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, sbase + row * kTileBytes, kNT);
         }
       }
     };
     // 0x0f0f0f0f kept opaque to the optimizer: with a visible constant it
     // fuses mask + shift into one bit-field extract per nibble, while this
-    // way one AND serves four byte->float conversions (v_cvt_f32_ubyte0..3).
+    // way one AND serves four nibbles.
     uint32_t nib_mask;
     asm volatile("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(nib_mask));
-    // Consume one stage: 16 rows, per token one FMA per code.
     auto consume = [&](int base, const uint32_t (&w)[U]) {
+      if constexpr (BF16) {
 #pragma unroll
-      for (int q = 0; q < U / 4; ++q) {
-        float4 x4[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) x4[b] = *(const float4 *)&xc[wv][b][base + 4 * q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t wcur = w[4 * q + e];
-          const uint32_t lo = wcur & nib_mask;
-          const uint32_t hi = (wcur >> 4) & nib_mask;
-          float n[8];
-          n[0] = (float)(lo & 0xffu);
-          n[1] = (float)(hi & 0xffu);
-          n[2] = (float)((lo >> 8) & 0xffu);
-          n[3] = (float)((hi >> 8) & 0xffu);
-          n[4] = (float)((lo >> 16) & 0xffu);
-          n[5] = (float)((hi >> 16) & 0xffu);
-          n[6] = (float)(lo >> 24);
-          n[7] = (float)(hi >> 24);
+        for (int q = 0; q < U / 4; ++q) {
+          // x of rows base+4q .. base+4q+3 as two bf16 pairs per token.
+          uint32_t xp[NB][2];
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
-            const float xv = e == 0 ? x4[b].x : e == 1 ? x4[b].y : e == 2 ? x4[b].z : x4[b].w;
+            const float4 x4 = *(const float4 *)&xc[wv][b][base + 4 * q];
+            xp[b][0] = (__float_as_uint(x4.x) >> 16) | (__float_as_uint(x4.y) & 0xffff0000u);
+            xp[b][1] = (__float_as_uint(x4.z) >> 16) | (__float_as_uint(x4.w) & 0xffff0000u);
+          }
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[b][c] = fmaf(xv, n[c], acc[b][c]);
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t wa = w[4 * q + 2 * h], wb = w[4 * q + 2 * h + 1];
+            const uint32_t la = wa & nib_mask, ha = (wa >> 4) & nib_mask;
+            const uint32_t lb = wb & nib_mask, hb = (wb >> 4) & nib_mask;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // bytes: [nib_a, 0, nib_b, 0] | 0x43004300 = bf16 (128+nib_a, 128+nib_b)
+              const uint32_t sel = (uint32_t)i | 0x0c00u | ((uint32_t)(4 + i) << 16) | 0x0c000000u;
+              const uint32_t pl = __builtin_amdgcn_perm(lb, la, sel) | 0x43004300u;
+              const uint32_t ph = __builtin_amdgcn_perm(hb, ha, sel) | 0x43004300u;
+#pragma unroll
+              for (int b = 0; b < NB; ++b) {
+                acc[b][2 * i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pl), as_bf16x2(xp[b][h]),
+                                                                acc[b][2 * i], false);
+                acc[b][2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                    as_bf16x2(ph), as_bf16x2(xp[b][h]), acc[b][2 * i + 1], false);
+              }
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < U / 4; ++q) {
+          float4 x4[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) x4[b] = *(const float4 *)&xc[wv][b][base + 4 * q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wcur = w[4 * q + e];
+            const uint32_t lo = wcur & nib_mask;
+            const uint32_t hi = (wcur >> 4) & nib_mask;
+            float n[8];
+            n[0] = (float)(lo & 0xffu);
+            n[1] = (float)(hi & 0xffu);
+            n[2] = (float)((lo >> 8) & 0xffu);
+            n[3] = (float)((hi >> 8) & 0xffu);
+            n[4] = (float)((lo >> 16) & 0xffu);
+            n[5] = (float)((hi >> 16) & 0xffu);
+            n[6] = (float)(lo >> 24);
+            n[7] = (float)(hi >> 24);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const float xv = e == 0 ? x4[b].x : e == 1 ? x4[b].y : e == 2 ? x4[b].z : x4[b].w;
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[b][c] = fmaf(xv, n[c], acc[b][c]);
+            }
           }
         }
       }
@@ -398,20 +486,19 @@ __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
       fetch(base + 2 * U, wa);
       if (base + U < cnt) consume(base + U, wb);
     }
-    // Apply the group scale: u~ contribution = scale * (sum x*nib - 8 sum x).
-    const float4 *sp = (const float4 *)(a.psc +
-                                        ((size_t)t * a.ngroups + g) * 512 +
-                                        (size_t)lane * 8);
+    // Group scale and code offset: contribution = scale * (acc - off * sum x).
+    const float off = BF16 ? 136.0f : 8.0f;
+    const int g = (sl * 64) / a.G;
+    const float4 *sp = (const float4 *)(a.psc + ((size_t)t * a.ngroups + g) * 512 + (size_t)lane * 8);
     const float4 s0 = sp[0], s1 = sp[1];
     const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        acc[b][c] = sc[c] * (acc[b][c] - 8.0f * xsum[b]);
+      for (int c = 0; c < 8; ++c) acc[b][c] = sc[c] * (acc[b][c] - off * xsum[b]);
   }
 
-  // Sum the four waves (fixed order) and publish this chunk's partials.
+  // Sum the waves (fixed order) and publish this chunk's partials.
   float *part = a.part + ((size_t)t * a.nchunk + chunk) * NB * 512;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -419,125 +506,169 @@ __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
     rp[0] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
     rp[1] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
     __syncthreads();
-    for (int e = threadIdx.x; e < 512; e += 256)
-      part[b * 512 + e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+    {
+      const int e = threadIdx.x;  // 512 threads, 512 partials
+      float v = red[0][e];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) v += red[q][e];
+      xstore(&part[b * 512 + e], v);
+    }
     __syncthreads();
   }
 
-  // Release this work-group's partials (every thread), then count arrival.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = (atomicAdd(&a.tile_cnt[t], 1u) == (unsigned)(a.nchunk - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, &s_last)) return;
 
   // Tile epilogue: u~, g~ for 256 columns per token, then |s~|.
   const float *tp = a.part + (size_t)t * a.nchunk * NB * 512;
-  for (int e = threadIdx.x; e < NB * 256; e += 256) {
+  for (int e = threadIdx.x; e < NB * 256; e += 512) {
     const int b = e >> 8, col = e & 255;
-    float u = 0.0f, gg = 0.0f;
-    for (int ch = 0; ch < a.nchunk; ++ch) {
-      u += tp[((size_t)ch * NB + b) * 512 + col];
-      gg += tp[((size_t)ch * NB + b) * 512 + 256 + col];
-    }
+    const float u = xsum_strided(&tp[(size_t)b * 512 + col], a.nchunk, (size_t)NB * 512);
+    const float gg = xsum_strided(&tp[(size_t)b * 512 + 256 + col], a.nchunk, (size_t)NB * 512);
     const int j = t * kTile + col;
     if (j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(u * silu(gg));
   }
-  if (threadIdx.x == 0) a.tile_cnt[t] = 0u;  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
 // K-d  Top-k channel mask (App. A.6, top-k equation), ties to the lower index
 // ---------------------------------------------------------------------------
 // One 1024-thread work-group per token.  |s~| >= 0, so its float32 bit
-// pattern orders like the value; a three-pass most-significant-digit radix
-// select (11, 11, 10 bits) finds the k-th largest key T and how many keys
-// equal to T are taken.  Thread t owns the contiguous channels
-// [t*PER, (t+1)*PER) in registers, so one exclusive scan gives each thread
-// its output position and the list comes out ascending; keys equal to T are
-// taken lowest index first.
+// pattern orders like the value: a most-significant-digit radix select on the
+// bits (digits of 11, 11 and 9 bits below the always-zero sign bit) finds the
+// k-th largest key T and how many keys equal to T are taken (kk).
+// Channel j is held by thread j % 1024 in register slot j / 1024, so loads
+// are coalesced and each slot is one run of 1024 consecutive channels: the
+// output position of a kept channel is (kept in earlier slots) + (kept in
+// earlier waves of its slot) + (kept in lower lanes), from ballots and one
+// scan of the per-(slot, wave) counts, so the list comes out ascending.
+// Each digit's bin is picked by wave 0 alone (one barrier per digit).
+
+// Wave 0 scans hist[0, NBINS) from the top and finds the bin holding the
+// kk-th largest key; writes it and the remaining rank to *s_bin / *s_kk.
+template <int NBINS>
+__device__ __forceinline__ void pick_bin(const unsigned *hist, unsigned kk,
+                                         unsigned *s_bin, unsigned *s_kk) {
+  constexpr int BPL = NBINS / 64;  // bins per lane, lane l owns the l-th block from the top
+  const int lane = threadIdx.x & 63;
+  const int hi = NBINS - 1 - lane * BPL;  // lane's highest bin
+  unsigned c[BPL];
+  unsigned sum = 0;
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    c[i] = hist[hi - i];
+    sum += c[i];
+  }
+  const unsigned incl = wave_incl_scan(sum);
+  unsigned above = incl - sum;  // keys in higher bins than this lane's block
+  if (above < kk && incl >= kk) {
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      if (above < kk && above + c[i] >= kk) {
+        *s_bin = (unsigned)(hi - i);
+        *s_kk = kk - above;
+      }
+      above += c[i];
+    }
+  }
+}
+
 template <int PER>
-__global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
-                                                    int k, int *sel) {
-  __shared__ unsigned hist[2048];
-  __shared__ unsigned wsum[16];
+__global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff, int k,
+                                                    int *sel) {
+  __shared__ unsigned h1[2048];
+  __shared__ unsigned h2[2048];
+  __shared__ unsigned h3[512];
+  __shared__ unsigned cnt[PER * 16];
   __shared__ unsigned s_bin, s_kk;
   const int b = blockIdx.x;
   if (k <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float *z = sabs + (size_t)b * d_ff;
   int *out = sel + (size_t)b * d_ff;
-  const int tid = threadIdx.x;
-  const int j0 = tid * PER;
-
   unsigned key[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int j = j0 + e;
+    const int j = e * 1024 + tid;
     key[e] = (j < d_ff) ? __float_as_uint(z[j]) : 0u;
   }
+  h1[tid] = 0u; h1[tid + 1024] = 0u;
+  h2[tid] = 0u; h2[tid + 1024] = 0u;
+  if (tid < 512) h3[tid] = 0u;
+  __syncthreads();
 
-  unsigned prefix = 0u, pmask = 0u, kk = (unsigned)k;
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const unsigned nb = pass == 2 ? 1024u : 2048u;
-    for (int i = tid; i < 2048; i += 1024) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (j0 + e < d_ff && (key[e] & pmask) == prefix)
-        atomicAdd(&hist[(key[e] >> sh) & (nb - 1u)], 1u);
-    __syncthreads();
-    // Thread t owns bins [t*bpt, (t+1)*bpt); count of keys in higher bins.
-    const int bpt = (int)(nb >> 10);
-    unsigned c1 = hist[tid * bpt];
-    unsigned c2 = (bpt == 2) ? hist[tid * bpt + 1] : 0u;
-    unsigned total;
-    const unsigned below = block_excl_scan<16>(c1 + c2, wsum, total);
-    const unsigned above = total - below - (c1 + c2);
-    if (bpt == 2) {
-      if (above < kk && above + c2 >= kk) {
-        s_bin = (unsigned)(tid * 2 + 1);
-        s_kk = kk - above;
-      } else if (above + c2 < kk && above + c2 + c1 >= kk) {
-        s_bin = (unsigned)(tid * 2);
-        s_kk = kk - above - c2;
-      }
-    } else if (above < kk && above + c1 >= kk) {
-      s_bin = (unsigned)tid;
-      s_kk = kk - above;
-    }
-    __syncthreads();
-    prefix |= s_bin << sh;
-    pmask |= (nb - 1u) << sh;
-    kk = s_kk;
-    __syncthreads();
-  }
-
-  // Compaction: keys > T all go, keys == T go while fewer than kk taken.
-  unsigned gt = 0u, eq = 0u;
+  // Digit 1: bits 30..20.
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    if (j0 + e < d_ff) {
-      gt += key[e] > prefix;
-      eq += key[e] == prefix;
-    }
-  unsigned total;
-  const unsigned before = block_excl_scan<16>((eq << 16) | gt, wsum, total);
-  unsigned eq_seen = before >> 16;
-  unsigned pos = (before & 0xffffu) + min(eq_seen, kk);
+    if (e * 1024 + tid < d_ff) atomicAdd(&h1[key[e] >> 20], 1u);
+  __syncthreads();
+  if (w == 0) pick_bin<2048>(h1, (unsigned)k, &s_bin, &s_kk);
+  __syncthreads();
+  const unsigned b1 = s_bin;
+  unsigned kk = s_kk;
+
+  // Digit 2: bits 19..9 of the keys with digit 1 = b1.
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (e * 1024 + tid < d_ff && (key[e] >> 20) == b1) atomicAdd(&h2[(key[e] >> 9) & 2047u], 1u);
+  __syncthreads();
+  if (w == 0) pick_bin<2048>(h2, kk, &s_bin, &s_kk);
+  __syncthreads();
+  const unsigned p2 = (b1 << 11) | s_bin;
+  kk = s_kk;
+
+  // Digit 3: bits 8..0 of the keys with digits 1-2 = p2.
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (e * 1024 + tid < d_ff && (key[e] >> 9) == p2) atomicAdd(&h3[key[e] & 511u], 1u);
+  __syncthreads();
+  if (w == 0) pick_bin<512>(h3, kk, &s_bin, &s_kk);
+  __syncthreads();
+  const unsigned T = (p2 << 9) | s_bin;
+  kk = s_kk;  // keys equal to T that are kept (the lowest-index ones)
+
+  // Compaction.  Pass A: per (slot, wave) counts of keys > T and == T.
+  uint64_t mgt[PER], meq[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int j = j0 + e;
+    const bool ok = e * 1024 + tid < d_ff;
+    mgt[e] = __ballot(ok && key[e] > T);
+    meq[e] = __ballot(ok && key[e] == T);
+    if (lane == 0) cnt[e * 16 + w] = ((unsigned)__popcll(meq[e]) << 16) | (unsigned)__popcll(mgt[e]);
+  }
+  __syncthreads();
+  // Wave 0: exclusive scan of the PER*16 counts in (slot, wave) order.
+  if (w == 0) {
+    constexpr int CPL = (PER * 16 + 63) / 64;
+    unsigned c[CPL], sum = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int q = lane * CPL + i;
+      c[i] = q < PER * 16 ? cnt[q] : 0u;
+      sum += c[i];
+    }
+    unsigned run = wave_incl_scan(sum) - sum;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int q = lane * CPL + i;
+      if (q < PER * 16) cnt[q] = run;
+      run += c[i];
+    }
+  }
+  __syncthreads();
+  // Pass B: positions.  Before this key: gt_b keys > T and eq_b keys == T;
+  // it is kept if > T, or == T with eq_b < kk; its position is gt_b + min(eq_b, kk).
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = e * 1024 + tid;
+    const unsigned base = cnt[e * 16 + w];
+    const unsigned gt_b = (base & 0xffffu) + (unsigned)__popcll(mgt[e] & below);
+    const unsigned eq_b = (base >> 16) + (unsigned)__popcll(meq[e] & below);
     if (j < d_ff) {
-      if (key[e] > prefix) {
-        out[pos++] = j;
-      } else if (key[e] == prefix) {
-        if (eq_seen < kk) out[pos++] = j;
-        ++eq_seen;
-      }
+      if (key[e] > T)
+        out[gt_b + min(eq_b, kk)] = j;
+      else if (key[e] == T && eq_b < kk)
+        out[gt_b + eq_b] = j;
     }
   }
 }
@@ -636,8 +767,8 @@ __global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
       for (int u = 0; u < MU; ++u) {
         const uint32_t off = (uint32_t)((m0 + u) * 64 + lane) * 16u;
         if (m0 + u < nsteps) {
-          wu[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase, 0);
-          wg[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, gbase, 0);
+          wu[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase, kNT);
+          wg[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, gbase, kNT);
         }
       }
 #pragma unroll
@@ -664,6 +795,48 @@ __global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
   }
 }
 
+// Batch-1 form of K-e: x (d_model elements, 16 bytes per lane per step) is
+// held in registers, so a wave starts streaming weights at once, with no LDS
+// prologue or barrier.  Wave w takes the contiguous list positions
+// [w*per, (w+1)*per), per chosen by the host so that all waves are resident
+// and carry equal work.  NSTEP = d_model / (64 lanes * 16 bytes / element).
+template <bool BF16, int MODE, int NSTEP>
+__global__ __launch_bounds__(256) void upgate1_kernel(UpGateArgs a, int per) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p0 = gw * per;
+  const int p1 = min(a.n, p0 + per);
+  if (p0 >= a.n) return;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
+  const uint32_t rowb = (uint32_t)a.d_model * ESZ;  // bytes of one up (or gate) row
+  u4 xr[NSTEP];
+#pragma unroll
+  for (int m = 0; m < NSTEP; ++m) xr[m] = ((const u4 *)a.x)[m * 64 + lane];
+  for (int p = p0; p < p1; ++p) {
+    const int j = (MODE == 2) ? p : a.list[p];
+    const uint32_t ubase = (uint32_t)j * 2u * rowb;
+    u4 wu[NSTEP], wg[NSTEP];
+#pragma unroll
+    for (int m = 0; m < NSTEP; ++m) {
+      const uint32_t off = (uint32_t)(m * 64 + lane) * 16u;
+      wu[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase, kNT);
+      wg[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase + rowb, kNT);
+    }
+    // Keep every load of the channel in flight before the first use.
+    __builtin_amdgcn_sched_barrier(0);
+    float au = 0.0f, ag = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NSTEP; ++m) {
+      au = dot16<BF16>(wu[m], xr[m], au);
+      ag = dot16<BF16>(wg[m], xr[m], ag);
+    }
+    const float u = wave_sum(au);
+    const float g = wave_sum(ag);
+    if (lane == 0) a.ssp[p] = u * silu(g);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // K-f  Stage 2b: input-sparse down projection y = s_sp W_down[sel, :]
 //      (Sec. 4.1, Stage 2 equations; Sec. 3.1, weighted-sum view)
@@ -671,7 +844,9 @@ __global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
 // Grid (ncol, nrc), 4 waves.  Work-group (c, r) covers output columns
 // [256c, 256c + 256) and list positions [rR, rR + R); lane l owns 4 columns
 // and walks its wave's rows (8 bytes bf16 / 16 bytes f32 per row), with the
-// row index and s value uniform across the wave.  The last work-group of a
+// row index and s value uniform across the wave.  W_down is stored in
+// 256-column chunks (see retile_down_kernel), so a chunk's rows are
+// contiguous and a dense pass streams each chunk sequentially.  The last work-group of a
 // column chunk adds the nrc partials in order, casts y to the layer dtype
 // and, for the stack, adds it to the float32 residual.
 struct DownArgs {
@@ -687,11 +862,11 @@ struct DownArgs {
   float *resid;
 };
 
-template <int NB, bool BF16, int MODE>
-__global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
-  constexpr int U = 16;  // rows in flight per wave
+template <int NB, bool BF16, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void down_kernel(DownArgs a) {
+  constexpr int U = 8;   // rows in flight per wave
   constexpr int ESZ = BF16 ? 2 : 4;
-  __shared__ float red[4][NB][kDownCols];
+  __shared__ float red[NW][NB][kDownCols];
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -700,9 +875,11 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
   const int R = (n + a.nrc - 1) / a.nrc;
   const int p0 = rc * R;
   const int p1 = min(n, p0 + R);
-  const int col = cc * kDownCols + lane * 4;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wd, a.wd_bytes);
-  const uint32_t voff = (uint32_t)col * ESZ;
+  // this chunk's rows: [d_ff][256] elements starting at chunk cc
+  const size_t chunk_bytes = (size_t)a.d_ff * kDownCols * ESZ;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc((const char *)a.wd + cc * chunk_bytes, (uint32_t)chunk_bytes);
+  const uint32_t voff = (uint32_t)lane * 4u * ESZ;
 
   float acc[NB][4];
 #pragma unroll
@@ -710,28 +887,28 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[b][c] = 0.0f;
 
-  // Rows p0+wv, p0+wv+4, ... of this chunk; an out-of-range slot re-reads a
+  // Rows p0+wv, p0+wv+NW, ... of this chunk; an out-of-range slot re-reads a
   // valid row and gets s = 0, so the loop body has no branches.
-  for (int p = p0 + wv; p < p1; p += 4 * U) {
+  for (int p = p0 + wv; p < p1; p += NW * U) {
     float wf[U][4];
     float sv[U][NB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int pp = p + 4 * u;
+      const int pp = p + NW * u;
       const bool ok = pp < p1;
       const int ppc = ok ? pp : p;
       const int j = (MODE == 2) ? ppc : a.list[ppc];
 #pragma unroll
       for (int b = 0; b < NB; ++b) sv[u][b] = ok ? a.ssp[(size_t)b * a.d_ff + ppc] : 0.0f;
-      const uint32_t rowoff = (uint32_t)j * (uint32_t)a.d_model * ESZ;
+      const uint32_t rowoff = (uint32_t)j * (uint32_t)(kDownCols * ESZ);
       if constexpr (BF16) {
-        const u2 w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, rowoff, 0);
+        const u2 w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, rowoff, kNT);
         wf[u][0] = bf16_to_f32(w.x & 0xffffu);
         wf[u][1] = bf16_to_f32(w.x >> 16);
         wf[u][2] = bf16_to_f32(w.y & 0xffffu);
         wf[u][3] = bf16_to_f32(w.y >> 16);
       } else {
-        const u4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, 0);
+        const u4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, kNT);
         wf[u][0] = __uint_as_float(w.x);
         wf[u][1] = __uint_as_float(w.y);
         wf[u][2] = __uint_as_float(w.z);
@@ -752,27 +929,22 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
         make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
   __syncthreads();
   float *yp = a.ypart + (size_t)rc * NB * a.d_model;
-  for (int e = threadIdx.x; e < NB * kDownCols; e += 256) {
+  for (int e = threadIdx.x; e < NB * kDownCols; e += NW * 64) {
     const int b = e / kDownCols, c = e % kDownCols;
-    yp[(size_t)b * a.d_model + cc * kDownCols + c] =
-        ((red[0][b][c] + red[1][b][c]) + red[2][b][c]) + red[3][b][c];
+    float v = red[0][b][c];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) v += red[q][b][c];
+    xstore(&yp[(size_t)b * a.d_model + cc * kDownCols + c], v);
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = (atomicAdd(&a.col_cnt[cc], 1u) == (unsigned)(a.nrc - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int e = threadIdx.x; e < NB * kDownCols; e += 256) {
+  if (!arrive_last(&a.col_cnt[cc], (unsigned)a.nrc, &s_last)) return;
+  for (int e = threadIdx.x; e < NB * kDownCols; e += NW * 64) {
     const int b = e / kDownCols, c = cc * kDownCols + e % kDownCols;
-    float v = 0.0f;
-    for (int r = 0; r < a.nrc; ++r) v += a.ypart[((size_t)r * NB + b) * a.d_model + c];
+    const float v = xsum_strided(&a.ypart[(size_t)b * a.d_model + c], a.nrc,
+                                 (size_t)NB * a.d_model);
     const size_t o = (size_t)b * a.d_model + c;
     st_elem<BF16>(a.y, o, v);
     if (a.resid) a.resid[o] += round_elem<BF16>(v);
   }
-  if (threadIdx.x == 0) a.col_cnt[cc] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -864,8 +1036,12 @@ hipError_t launch_prepare(const Plan &p, const Bufs &b, const void *w_up,
     transpose_kernel<false><<<tg, 256, 0, s>>>(w_up, w_gate, b.wug, p.d_model, p.d_ff);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipMemcpyAsync(b.wd, w_down, (size_t)p.d_ff * p.d_model * p.esz,
-                     hipMemcpyDeviceToDevice, s);
+  dim3 rg(p.d_ff, p.ncol);
+  if (p.bf16)
+    retile_down_kernel<true><<<rg, kDownCols, 0, s>>>(w_down, b.wd, p.d_model, p.d_ff);
+  else
+    retile_down_kernel<false><<<rg, kDownCols, 0, s>>>(w_down, b.wd, p.d_model, p.d_ff);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Padding columns of the last tile keep code 0 (nibble 8) and scale 0.
   e = hipMemsetAsync(b.pq, 0x88, (size_t)p.ntile * p.d_model * kTileBytes, s);
@@ -897,17 +1073,10 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
   ProxyArgs a{b.pq, b.psc, x, tau, p.d_model, p.d_ff, p.G, p.ngroups,
               p.nchunk, b.part, b.tile_cnt, b.sabs};
   dim3 g(p.nchunk, p.ntile);
-  const int nsl = p.G / 64;
   if (p.bf16) {
-    if (nsl == 1) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true, 1><<<g, 256, 0, s>>>(a))); }
-    else if (nsl == 2) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true, 2><<<g, 256, 0, s>>>(a))); }
-    else if (nsl == 4) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true, 4><<<g, 256, 0, s>>>(a))); }
-    else return hipErrorInvalidValue;
+    PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true><<<g, 512, 0, s>>>(a)));
   } else {
-    if (nsl == 1) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false, 1><<<g, 256, 0, s>>>(a))); }
-    else if (nsl == 2) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false, 2><<<g, 256, 0, s>>>(a))); }
-    else if (nsl == 4) { PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false, 4><<<g, 256, 0, s>>>(a))); }
-    else return hipErrorInvalidValue;
+    PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false><<<g, 512, 0, s>>>(a)));
   }
   return hipGetLastError();
 }
@@ -954,6 +1123,47 @@ static hipError_t upgate_go(const UpGateArgs &a, int grid, size_t lds, hipStream
   return hipGetLastError();
 }
 
+// Waves of a kernel that fit on the device at once (occupancy x CUs).
+static int resident_waves(const void *fn, int block) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * cus * (block / 64);
+}
+
+template <bool BF16, int MODE, int NSTEP>
+static hipError_t upgate1_go(const UpGateArgs &a, hipStream_t s) {
+  auto fn = upgate1_kernel<BF16, MODE, NSTEP>;
+  static int cap = 0;
+  if (!cap) cap = resident_waves((const void *)fn, 256);
+  const int per = (a.n + cap - 1) / cap;    // equal share per wave
+  const int waves = (a.n + per - 1) / per;
+  fn<<<(waves + 3) / 4, 256, 0, s>>>(a, per);
+  return hipGetLastError();
+}
+
+template <bool BF16, int MODE>
+static bool upgate1_dispatch(const Plan &p, const UpGateArgs &a, hipStream_t s, hipError_t &e) {
+  const int nstep = p.d_model / (64 * (BF16 ? 8 : 4));
+  switch (nstep) {
+    case 1: e = upgate1_go<BF16, MODE, 1>(a, s); return true;
+    case 2: e = upgate1_go<BF16, MODE, 2>(a, s); return true;
+    case 4: e = upgate1_go<BF16, MODE, 4>(a, s); return true;
+    case 8: e = upgate1_go<BF16, MODE, 8>(a, s); return true;
+    case 10: e = upgate1_go<BF16, MODE, 10>(a, s); return true;
+    case 16: e = upgate1_go<BF16, MODE, 16>(a, s); return true;
+    default: return false;
+  }
+}
+
 hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
                          int mode, int n, hipStream_t s) {
   UpGateArgs a{b.wug, (uint32_t)((size_t)p.d_ff * 2 * p.d_model * p.esz), x,
@@ -962,6 +1172,15 @@ hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
   if (mode == 1) a.n_ptr = b.nuni;
   const int maxn = (mode == 1) ? p.d_ff : n;
   if (maxn <= 0) return hipSuccess;
+  if (batch == 1 && mode != 1) {
+    hipError_t e1 = hipSuccess;
+    bool done;
+    if (p.bf16)
+      done = mode == 0 ? upgate1_dispatch<true, 0>(p, a, s, e1) : upgate1_dispatch<true, 2>(p, a, s, e1);
+    else
+      done = mode == 0 ? upgate1_dispatch<false, 0>(p, a, s, e1) : upgate1_dispatch<false, 2>(p, a, s, e1);
+    if (done) return e1;
+  }
   int grid = (maxn + 3) / 4;
   if (grid > p.upgate_cap) grid = p.upgate_cap;
   const size_t lds = (size_t)batch * p.d_model * p.esz;
@@ -985,15 +1204,22 @@ hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
              b.ypart, b.col_cnt, y, resid};
   if (mode == 1) a.n_ptr = b.nuni;
   dim3 g(p.ncol, p.nrc);
+  // Waves per work-group: 16 for one or two tokens (more loads in flight),
+  // fewer for larger batches to bound the LDS reduction buffer.
+#define PROX_DOWN(BF, MD)                                                              \
+  PROX_DISPATCH_NB(batch, (NB <= 2 ? (down_kernel<NB, BF, MD, 16><<<g, 1024, 0, s>>>(a), 0)   \
+                           : NB <= 4 ? (down_kernel<NB, BF, MD, 8><<<g, 512, 0, s>>>(a), 0)  \
+                                     : (down_kernel<NB, BF, MD, 4><<<g, 256, 0, s>>>(a), 0)))
   if (p.bf16) {
-    if (mode == 0) { PROX_DISPATCH_NB(batch, (down_kernel<NB, true, 0><<<g, 256, 0, s>>>(a))); }
-    else if (mode == 1) { PROX_DISPATCH_NB(batch, (down_kernel<NB, true, 1><<<g, 256, 0, s>>>(a))); }
-    else { PROX_DISPATCH_NB(batch, (down_kernel<NB, true, 2><<<g, 256, 0, s>>>(a))); }
+    if (mode == 0) { PROX_DOWN(true, 0); }
+    else if (mode == 1) { PROX_DOWN(true, 1); }
+    else { PROX_DOWN(true, 2); }
   } else {
-    if (mode == 0) { PROX_DISPATCH_NB(batch, (down_kernel<NB, false, 0><<<g, 256, 0, s>>>(a))); }
-    else if (mode == 1) { PROX_DISPATCH_NB(batch, (down_kernel<NB, false, 1><<<g, 256, 0, s>>>(a))); }
-    else { PROX_DISPATCH_NB(batch, (down_kernel<NB, false, 2><<<g, 256, 0, s>>>(a))); }
+    if (mode == 0) { PROX_DOWN(false, 0); }
+    else if (mode == 1) { PROX_DOWN(false, 1); }
+    else { PROX_DOWN(false, 2); }
   }
+#undef PROX_DOWN
   return hipGetLastError();
 }
 

@@ -66,6 +66,11 @@ def load_library(path: str = LIB_PATH):
         "prox_ffn_forward_debug": ([P, P, I, F, I, P, ctypes.POINTER(prox_debug), P], I),
         "prox_dense_ffn_forward": ([P, P, I, P, P], I),
         "prox_stack_forward": ([ctypes.POINTER(P), I, ctypes.POINTER(F), I, P, I, F, P], I),
+        "prox_ffn_forward_profiled": ([P, P, I, F, I, P, ctypes.POINTER(P), I,
+                                       ctypes.POINTER(I), P], I),
+        "prox_dense_ffn_forward_profiled": ([P, P, I, P, ctypes.POINTER(P), I,
+                                             ctypes.POINTER(I), P], I),
+        "prox_rmsnorm": ([P, P, I, F, P, P], I),
         "prox_destroy_layer": ([P], None),
         "prox_last_error": ([], ctypes.c_char_p),
     }
@@ -229,6 +234,45 @@ def prox_dense_ffn_forward(layer: Layer, x, y=None):
     B = 1 if x.dim() == 1 else int(x.shape[0])
     _check(load_library().prox_dense_ffn_forward(layer.handle, _ptr(x), B, _ptr(y), _stream()))
     return y
+
+
+def prox_rmsnorm(layer: Layer, resid, eps: float = 1e-5, x=None):
+    """cast(RMSNorm(resid)) for resid [batch][d_model] float32 (batch <= 8)."""
+    B = 1 if resid.dim() == 1 else int(resid.shape[0])
+    if x is None:
+        x = torch.empty(resid.shape, dtype=layer.dtype, device=resid.device)
+    _check(load_library().prox_rmsnorm(layer.handle, _ptr(resid), B, float(eps), _ptr(x),
+                                       _stream()))
+    return x
+
+
+def _event_array(events):
+    for e in events:  # torch creates the underlying hipEvent on first record()
+        if not e.cuda_event:
+            e.record()
+    return (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+
+
+def prox_ffn_forward_profiled(layer: Layer, x, threshold: float, k: int, events, y=None):
+    """Forward of x [batch][d_model] with torch.cuda.Event objects recorded
+    before the first kernel and after each kernel; returns (y, n_recorded)."""
+    y = _out_like(x, y)
+    n = ctypes.c_int()
+    B = 1 if x.dim() == 1 else int(x.shape[0])
+    _check(load_library().prox_ffn_forward_profiled(
+        layer.handle, _ptr(x), B, float(threshold), int(k), _ptr(y),
+        _event_array(events), len(events), ctypes.byref(n), _stream()))
+    return y, n.value
+
+
+def prox_dense_ffn_forward_profiled(layer: Layer, x, events, y=None):
+    y = _out_like(x, y)
+    n = ctypes.c_int()
+    B = 1 if x.dim() == 1 else int(x.shape[0])
+    _check(load_library().prox_dense_ffn_forward_profiled(
+        layer.handle, _ptr(x), B, _ptr(y), _event_array(events), len(events),
+        ctypes.byref(n), _stream()))
+    return y, n.value
 
 
 def prox_stack_forward(layers, thresholds, k: int, resid, eps: float = 1e-5):

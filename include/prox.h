@@ -80,7 +80,8 @@ prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
 /* Build a layer (Sec. 4.3: the INT4 proxy of W_up and W_gate is computed once
  * and stays resident).  Enqueues on `stream`:
  *   - relayout: W_up and W_gate transposed to channel-major rows (channel j's
- *     up row followed by its gate row), W_down copied row-major;
+ *     up row followed by its gate row), W_down kept row-major in chunks of
+ *     256 output columns ([d_model/256][d_ff][256]);
  *   - quantization: per group g of G input rows and per column j,
  *     scale = max|W[i][j]| / 7 (float32), code = clamp(rint(W / scale), -7, 7)
  *     (float32 divide, ties to even; an all-zero group has scale 0, codes 0),
@@ -151,6 +152,32 @@ prox_status prox_dense_ffn_forward(const prox_layer *layer, const void *x,
 prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
                                const float *thresholds, int k, float *resid,
                                int batch, float eps, void *stream);
+
+/* The stack's normalization alone: x = cast(r / sqrt(mean(r^2) + eps)) for
+ * `batch` (1..8) rows of the float32 residual r [batch][d_model], written in
+ * the layer dtype.  Used to collect layer inputs for threshold calibration
+ * (each layer's tau is a quantile of |x| over calibration tokens that went
+ * through the already-calibrated layers before it).                         */
+prox_status prox_rmsnorm(const prox_layer *layer, const float *resid, int batch,
+                         float eps, void *x, void *stream);
+
+/* Instrumented forms of prox_ffn_forward_batch and prox_dense_ffn_forward,
+ * for measurement.  `events` holds n_events caller-created hipEvent_t; one is
+ * recorded on `stream` before the first kernel and one after each kernel, so
+ * consecutive pairs bracket the kernels in launch order:
+ *   sparse: Stage 1 proxy, top-k, [mask union if batch > 1], Stage 2 up/gate,
+ *           Stage 2 down                        (at least 6 events needed)
+ *   dense:  up/gate, down                        (at least 3 events needed)
+ * *n_recorded receives the number of events recorded.  Same results as the
+ * plain calls; no host synchronization.                                      */
+prox_status prox_ffn_forward_profiled(const prox_layer *layer, const void *x,
+                                      int batch, float threshold, int k, void *y,
+                                      void *const *events, int n_events,
+                                      int *n_recorded, void *stream);
+prox_status prox_dense_ffn_forward_profiled(const prox_layer *layer,
+                                            const void *x, int batch, void *y,
+                                            void *const *events, int n_events,
+                                            int *n_recorded, void *stream);
 
 /* Release a handle (host memory only; the caller's buffers are untouched). */
 void prox_destroy_layer(prox_layer *layer);

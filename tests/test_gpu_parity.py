@@ -134,7 +134,8 @@ def test_relayout_is_exact_copy():
     assert torch.equal(wug[:, 0, :], W[0].t())
     assert torch.equal(wug[:, 1, :], W[1].t())
     off = ((2 * d * f * 2 + 255) // 256 * 256) // 2
-    assert torch.equal(wb[off: off + f * d].view(f, d), W[2])
+    wd = wb[off: off + f * d].view(d // 256, f, 256).permute(1, 0, 2).reshape(f, d)
+    assert torch.equal(wd, W[2])
 
 
 # ---------------------------------------------------------------------------
