@@ -8,7 +8,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <stdlib.h>
+
 #include <new>
+#include <algorithm>
 #include <string>
 
 #include "../../include/prox.h"
@@ -95,6 +98,8 @@ Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch) {
   if (nrc > 64) nrc = 64;
   p.nrc = nrc;
   p.upgate_cap = 4096;
+  const char *path = getenv("PROX_PATH");
+  p.use_fused = fused_supported(p) && !(path && strcmp(path, "multi") == 0);
   return p;
 }
 
@@ -116,8 +121,10 @@ Layout make_layout(const Plan &p) {
   L.o_uni = o;       o = align256(o + (size_t)p.d_ff * sizeof(int));
   L.o_nuni = o;      o = align256(o + sizeof(int));
   L.o_umask = o;     o = align256(o + (size_t)p.d_ff);
-  L.o_ypart = o;     o = align256(o + (size_t)p.nrc * B * p.d_model * sizeof(float));
+  const size_t yrows = std::max((size_t)p.nrc * B, (size_t)fused_ypart_rows(p));
+  L.o_ypart = o;     o = align256(o + yrows * p.d_model * sizeof(float));
   L.o_col_cnt = o;   o = align256(o + (size_t)p.ncol * sizeof(unsigned));
+  L.o_sync = o;      o = align256(o + fused_sync_words(p) * sizeof(unsigned));
   L.o_xbuf = o;      o = align256(o + B * p.d_model * p.esz);
   L.o_ybuf = o;      o = align256(o + B * p.d_model * p.esz);
   L.workspace = o;
@@ -156,6 +163,12 @@ prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau
     if (e != hipSuccess) return hip_fail(e, "zero output");
     if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
     return PROX_OK;  // y = 0 adds nothing to the residual
+  }
+  if (batch == 1 && p.use_fused) {
+    if ((e = prox::launch_fused(p, b, x, tau, k, y, resid, s)) != hipSuccess)
+      return hip_fail(e, "fused kernel");
+    if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
+    return PROX_OK;
   }
   if ((e = prox::launch_proxy(p, b, x, batch, tau, s)) != hipSuccess)
     return hip_fail(e, "stage 1 proxy kernel");
@@ -271,9 +284,13 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.umask = (uint8_t *)(ws + lay.o_umask);
   b.ypart = (float *)(ws + lay.o_ypart);
   b.col_cnt = (unsigned *)(ws + lay.o_col_cnt);
+  b.sync = (unsigned *)(ws + lay.o_sync);
   b.xbuf = ws + lay.o_xbuf;
   b.ybuf = ws + lay.o_ybuf;
   hipError_t e = prox::launch_prepare(L->plan, b, w_up, w_gate, w_down, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(b.sync, 0, prox::fused_sync_words(L->plan) * sizeof(unsigned),
+                       (hipStream_t)stream);
   if (e != hipSuccess) {
     delete L;
     return hip_fail(e, "prepare kernels");
@@ -317,11 +334,18 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
   if (st != PROX_OK) return st;
   if (!dbg) return fail(PROX_EINVAL, "dbg is NULL");
   hipStream_t s = (hipStream_t)stream;
-  st = run_forward(layer, x, batch, threshold, k, y, nullptr, s);
-  if (st != PROX_OK) return st;
   const prox::Plan &p = layer->plan;
   const prox::Bufs &b = layer->bufs;
   hipError_t e = hipSuccess;
+  if (dbg->status &&
+      (e = hipMemsetAsync(b.sync + prox::kFusedErrWord, 0, sizeof(unsigned), s)) != hipSuccess)
+    return hip_fail(e, "clear status");
+  st = run_forward(layer, x, batch, threshold, k, y, nullptr, s);
+  if (st != PROX_OK) return st;
+  if (dbg->status &&
+      (e = hipMemcpyAsync(dbg->status, b.sync + prox::kFusedErrWord, sizeof(unsigned),
+                          hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return hip_fail(e, "copy status");
   if (dbg->n1 || dbg->idx) {
     if (!dbg->n1 || !dbg->idx) return fail(PROX_EINVAL, "n1 and idx must be given together");
     e = prox::launch_compact_debug(p, x, batch, threshold, dbg->n1, dbg->idx, s);
@@ -408,6 +432,32 @@ prox_status prox_ffn_forward_profiled(const prox_layer *layer, const void *x, in
   st = run_forward(layer, x, batch, threshold, k, y, nullptr, (hipStream_t)stream, &lg);
   *n_recorded = lg.n;
   return st;
+}
+
+prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x, float threshold,
+                                   int k, void *y, unsigned long long *trace, int trace_items,
+                                   int *counts, void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, 1, threshold, k, y);
+  if (st != PROX_OK) return st;
+  const prox::Plan &p = layer->plan;
+  if (!p.use_fused) return fail(PROX_EUNSUPPORTED, "the layer does not use the persistent kernel");
+  if (k == 0) return fail(PROX_EINVAL, "k = 0 launches no persistent kernel");
+  if (!counts) return fail(PROX_EINVAL, "counts is NULL");
+  const int n_p1 = p.ntile * p.nchunk, n_p3 = (k + 7) / 8;
+  const int total = prox::fused_items(p, k);
+  counts[0] = n_p1;
+  counts[1] = 1;
+  counts[2] = n_p3;
+  counts[3] = total - n_p1 - 1 - n_p3;
+  if (!trace) return PROX_OK;  // size query
+  if (trace_items < total)
+    return fail(PROX_EINVAL, "trace holds %d items, the launch has %d", trace_items, total);
+  if (!aligned(trace, 16)) return fail(PROX_EINVAL, "trace must be 16-byte aligned");
+  hipError_t e = prox::launch_fused(p, layer->bufs, x, threshold, k, y, nullptr,
+                                    (hipStream_t)stream, trace);
+  if (e != hipSuccess) return hip_fail(e, "fused kernel");
+  return PROX_OK;
 }
 
 prox_status prox_dense_ffn_forward_profiled(const prox_layer *layer, const void *x,

@@ -1,0 +1,815 @@
+// The batch-1 Prox FFN step as one persistent kernel for CDNA4 (gfx950).
+//
+// Method: "Prox: Training-Free FFN Activation Sparsity via Approximate
+// Intermediate-Channel Salience in LLMs" (arXiv 2607.27591): Sec. 4.1
+// (Stage 1 input mask and INT4 proxy, Stage 2 exact sparse computation),
+// Sec. 4.3 (fused kernels), App. A.6 (top-k mask).
+//
+// Four dependent phases run inside one launch, so HBM never drains between
+// them:
+//   P1  Stage 1 proxy, one item per (256-column tile, 512-row chunk); the
+//       last item of a tile also adds the tile's digit-1 counts of |s~| to a
+//       global histogram;
+//   P2  the top-k threshold (one item): from the histogram, one pass over the
+//       keys and a small radix select it publishes the k-th key T and, per
+//       group of 64 channels, how many kept channels precede the group;
+//   P3  Stage 2 up/gate + SwiGLU, one item per 8 list positions; each wave
+//       finds the channel at its position from the group table;
+//   P4  Stage 2 down projection, one item per (256-column chunk, 128 rows).
+// Work-groups take items from a global ticket counter in exactly that order.
+// An item only ever waits for items with smaller tickets (P2 for all of P1,
+// P3 for P2, P4 for the P3 items covering its rows); those were handed to
+// running work-groups before it, and P1 items wait for nothing, so the
+// schedule cannot deadlock whatever the residency.  Every wait is bounded
+// (wait_geq).  Data passed between work-groups goes through agent-coherent
+// accesses (xstore/xload and sc1 buffer loads); the last work-group to leave
+// resets the ticket, the flags and the histogram for the next launch.
+#include <type_traits>
+
+#include "prox_device.h"
+
+namespace prox {
+
+// Sync words at the start of the fused workspace block.  Each control word
+// and each P3 flag sits on its own 256-byte line (kSyncStride words), so that
+// polling one flag does not contend with the atomics on another.
+enum : int {
+  kSyncTicket = 0 * kSyncStride,  // next ticket
+  kSyncTiles = 1 * kSyncStride,   // P1 tiles finished
+  kSyncSelect = 2 * kSyncStride,  // P2 finished (0/1)
+  kSyncExit = 3 * kSyncStride,    // work-groups that left the item loop
+  kSyncErr = 4 * kSyncStride,     // sticky error bits (1: a wait timed out, 2: select fallback used)
+  kSyncP3 = 5 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
+};
+static_assert(kSyncErr == kFusedErrWord, "error word index");
+
+constexpr int kFW = 8;             // waves per work-group
+constexpr int kFT = kFW * 64;      // threads per work-group
+constexpr int kWaveCand = 256;     // top-k candidates per wave held in LDS (fast path)
+constexpr int kMaxPer = 64;        // key slots per thread: d_ff <= 64 * 512
+constexpr int kGroups = kMaxPer * kFW;  // groups of 64 channels: d_ff <= 512 * 64
+constexpr int kKC = 16;            // key slots loaded per round of a select pass
+constexpr int kP4Rows = 128;       // list positions per P4 item (16 per wave)
+constexpr int kSelBits = 16;       // buffer-load aux bit: sc1 (agent-coherent)
+
+struct FusedArgs {
+  const uint8_t *pq;
+  const float *psc;
+  const void *wug;
+  uint32_t wug_bytes;
+  const void *wd;
+  int d_model, d_ff, G, ngroups, ntile, nchunk, ncol, nrc;
+  const void *x;
+  float tau;
+  int k;
+  void *y;
+  float *resid;
+  float *part;
+  unsigned *tile_cnt;
+  float *sabs;
+  int *sel;
+  float *ssp;
+  float *ypart;
+  unsigned *col_cnt;
+  unsigned *sync;
+  unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
+  int n_p1, n_p3, n_p4;
+  unsigned long long *trace;  // optional per-ticket timeline (nullptr: off)
+};
+
+// Timeline stamp of the current item: when its wait for earlier items ended
+// (thread 0 only; 100 MHz s_memrealtime clock).
+__shared__ unsigned long long g_twait;
+__device__ __forceinline__ void stamp_wait(const FusedArgs &a) {
+  if (a.trace) g_twait = __builtin_amdgcn_s_memrealtime();
+}
+
+// ---------------------------------------------------------------------------
+// LDS of each phase (one union per work-group)
+// ---------------------------------------------------------------------------
+struct P1Smem {
+  float red[kFW][512];
+  __attribute__((aligned(16))) int rl[kFW][64 + 48];
+  __attribute__((aligned(16))) float xc[kFW][64 + 48];
+};
+struct P2Smem {
+  unsigned h[2048];
+  unsigned ck[kFW * kWaveCand];  // candidate keys (per-wave lists)
+  int ci[kFW * kWaveCand];       // candidate channels
+  uint64_t gtm[kGroups];         // per group of 64 channels: keys above T
+  uint64_t eqm[kGroups];         // ... and equal to T
+  unsigned ccnt[kFW];
+  unsigned wt[16];
+  unsigned misc[8];
+};
+struct P4Smem {
+  float red[kFW][kDownCols];
+  int rs[kP4Rows];
+  float sv[kP4Rows];
+};
+
+// ---------------------------------------------------------------------------
+// P1: Stage 1 for one (tile, chunk) item.  Same arithmetic as proxy_kernel
+// (see there): one wave per 64-row slice, survivors by ballot, nibble pairs
+// decoded under the bf16 exponent byte for bf16 layers.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
+  constexpr int U = 16;
+  const int chunk = item % a.nchunk, t = item / a.nchunk;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sl = chunk * kFW + wv;
+  const int nsl = a.d_model >> 6;
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+
+  if (sl < nsl) {
+    float xl;
+    const uint64_t un = slice_mask<BF16>(a.x, (size_t)sl * 64, a.tau, xl);
+    const float xm = ((un >> lane) & 1ull) ? xl : 0.0f;
+    const float xsum = wave_sum(xm);
+    const int cnt = (int)__popcll(un);
+    if ((un >> lane) & 1ull) {
+      const int pos = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(un >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((unsigned)un, 0u));
+      sm.rl[wv][pos] = lane;
+      sm.xc[wv][pos] = xm;
+    }
+    if (lane < 3 * U) {
+      sm.rl[wv][cnt + lane] = 0;
+      sm.xc[wv][cnt + lane] = 0.0f;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(a.pq + (size_t)t * a.d_model * kTileBytes, (uint32_t)a.d_model * kTileBytes);
+    const uint32_t voff = (uint32_t)lane * 4u;
+    const uint32_t sbase = (uint32_t)sl * 64u * kTileBytes;
+    auto fetch = [&](int base, uint32_t (&w)[U]) {
+#pragma unroll
+      for (int q = 0; q < U / 4; ++q) {
+        const int4 r4 = *(const int4 *)&sm.rl[wv][base + 4 * q];
+        const int rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(rr[e]);
+          w[4 * q + e] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, sbase + row * kTileBytes, kNT);
+        }
+      }
+    };
+    uint32_t nib_mask;
+    asm volatile("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(nib_mask));
+    auto consume = [&](int base, const uint32_t (&w)[U]) {
+#pragma unroll
+      for (int q = 0; q < U / 4; ++q) {
+        const float4 x4 = *(const float4 *)&sm.xc[wv][base + 4 * q];
+        if constexpr (BF16) {
+          const uint32_t xp[2] = {
+              (__float_as_uint(x4.x) >> 16) | (__float_as_uint(x4.y) & 0xffff0000u),
+              (__float_as_uint(x4.z) >> 16) | (__float_as_uint(x4.w) & 0xffff0000u)};
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t wa = w[4 * q + 2 * h], wb = w[4 * q + 2 * h + 1];
+            const uint32_t la = wa & nib_mask, ha = (wa >> 4) & nib_mask;
+            const uint32_t lb = wb & nib_mask, hb = (wb >> 4) & nib_mask;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t sel = (uint32_t)i | 0x0c00u | ((uint32_t)(4 + i) << 16) | 0x0c000000u;
+              const uint32_t pl = __builtin_amdgcn_perm(lb, la, sel) | 0x43004300u;
+              const uint32_t ph = __builtin_amdgcn_perm(hb, ha, sel) | 0x43004300u;
+              acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pl), as_bf16x2(xp[h]),
+                                                          acc[2 * i], false);
+              acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ph), as_bf16x2(xp[h]),
+                                                              acc[2 * i + 1], false);
+            }
+          }
+        } else {
+          const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wcur = w[4 * q + e];
+            const uint32_t lo = wcur & nib_mask, hi = (wcur >> 4) & nib_mask;
+            const float n[8] = {(float)(lo & 0xffu), (float)(hi & 0xffu),
+                                (float)((lo >> 8) & 0xffu), (float)((hi >> 8) & 0xffu),
+                                (float)((lo >> 16) & 0xffu), (float)((hi >> 16) & 0xffu),
+                                (float)(lo >> 24), (float)(hi >> 24)};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = fmaf(xs[e], n[c], acc[c]);
+          }
+        }
+      }
+    };
+    uint32_t wa[U], wb[U];
+    fetch(0, wa);
+    for (int base = 0; base < cnt; base += 2 * U) {
+      fetch(base + U, wb);
+      consume(base, wa);
+      fetch(base + 2 * U, wa);
+      if (base + U < cnt) consume(base + U, wb);
+    }
+    const float off = BF16 ? 136.0f : 8.0f;
+    const int g = (sl * 64) / a.G;
+    const float4 *sp =
+        (const float4 *)(a.psc + ((size_t)t * a.ngroups + g) * 512 + (size_t)lane * 8);
+    const float4 s0 = sp[0], s1 = sp[1];
+    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = sc[c] * (acc[c] - off * xsum);
+  }
+
+  float4 *rp = (float4 *)&sm.red[wv][lane * 8];
+  rp[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  rp[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  __syncthreads();
+  float *part = a.part + ((size_t)t * a.nchunk + chunk) * 512;
+  {
+    const int e = threadIdx.x;
+    float v = sm.red[0][e];
+#pragma unroll
+    for (int q = 1; q < kFW; ++q) v += sm.red[q][e];
+    xstore(&part[e], v);
+  }
+  if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, s_flag)) return;
+
+  // Tile epilogue: |s~| = |u~ * SiLU(g~)| of the tile's 256 channels, and the
+  // tile's counts of digit 1 (bits 30..20 of |s~|) added to the global
+  // histogram (the partials in LDS are consumed, so it holds the counts).
+  unsigned *h = (unsigned *)&sm.red[0][0];
+  for (int i = threadIdx.x; i < 2048; i += kFT) h[i] = 0u;
+  __syncthreads();
+  const float *tp = a.part + (size_t)t * a.nchunk * 512;
+  if (threadIdx.x < 256) {
+    const int col = threadIdx.x;
+    const float u = xsum_strided(&tp[col], a.nchunk, 512);
+    const float gg = xsum_strided(&tp[256 + col], a.nchunk, 512);
+    const int j = t * kTile + col;
+    if (j < a.d_ff) {
+      const float v = fabsf(u * silu(gg));
+      xstore(&a.sabs[j], v);
+      atomicAdd(&h[__float_as_uint(v) >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2048; i += kFT) {
+    const unsigned c = h[i];
+    if (c) __hip_atomic_fetch_add(&a.ghist[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(&a.sync[kSyncTiles], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// P2: the top-k select (App. A.6, top-k equation), ties to the lower index.
+// ---------------------------------------------------------------------------
+// |s~| >= 0, so its float32 bits order like the value; digit 1 = bits 30..20,
+// digit 2 = bits 19..9, digit 3 = bits 8..0.  Channel j is read by thread
+// j % 512 in slot j / 512 and belongs to group j / 64 (one wave, one slot).
+// Fast path:
+//   1. the global digit-1 histogram (built by the P1 tile epilogues) gives
+//      the bin b* of the k-th largest key and the rank kk of that key in it;
+//   2. one pass over the keys records, per group, the bit mask of keys with
+//      digit 1 above b* and gathers the keys with digit 1 = b* (typically a
+//      few hundred) in per-wave LDS lists;
+//   3. two radix steps over the gathered keys give the k-th key T and the
+//      number kk of keys equal to T that are kept (the lowest-index ones);
+//      the gathered keys then set their bits in their group's above-T or
+//      equal-to-T mask.
+// Fallback (a wave gathers more than kWaveCand keys, e.g. massive exact
+// ties): the radix steps and the masks over all keys.
+// List: one thread per group keeps its above-T channels and its first
+// min(equal, kk - equal channels before the group) equal ones; a block scan
+// of the kept counts places each group's channels, ascending, in sel.
+
+// All waves: bins [NB - (t+1)*BPL, NB - t*BPL) belong to thread t (from the
+// top).  Finds the bin holding the kk-th largest; 2 barriers.
+template <int NBINS, typename H>
+__device__ __forceinline__ void pick_bin_all(H hist, unsigned kk, unsigned *wt, unsigned *out) {
+  constexpr int BPL = NBINS / kFT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hi = NBINS - 1 - tid * BPL;
+  unsigned c[BPL], sum = 0;
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    c[i] = hist(hi - i);
+    sum += c[i];
+  }
+  const unsigned incl = wave_incl_scan_dpp(sum);
+  if (lane == 63) wt[w] = incl;
+  __syncthreads();
+  unsigned above = incl - sum;
+#pragma unroll
+  for (int q = 0; q < kFW; ++q) above += (q < w) ? wt[q] : 0u;
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    if (above < kk && above + c[i] >= kk) {
+      out[0] = (unsigned)(hi - i);
+      out[1] = kk - above;
+    }
+    above += c[i];
+  }
+  __syncthreads();
+}
+
+__device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
+  if (threadIdx.x == 0) {
+    wait_geq(&a.sync[kSyncTiles], (unsigned)a.ntile, &a.sync[kSyncErr]);
+    stamp_wait(a);
+  }
+  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = a.d_ff;
+  const int per = (n + kFT - 1) / kFT;
+  const unsigned k = (unsigned)a.k;
+  // Keys of slots [e0, e0 + kKC): unconditional loads (indices clamped into
+  // range) so that they all stay in flight; callers mask j >= n themselves.
+  auto load_keys = [&](int e0, unsigned (&kc)[kKC]) {
+#pragma unroll
+    for (int m = 0; m < kKC; ++m) {
+      const int j = min((e0 + m) * kFT + tid, n - 1);
+      kc[m] = __float_as_uint(xload(&a.sabs[j]));
+    }
+  };
+  for (int i = tid; i < 2048; i += kFT) sm.h[i] = xload_u(&a.ghist[i]);
+  for (int i = tid; i < kGroups; i += kFT) sm.eqm[i] = 0ull;
+  __syncthreads();
+
+  // 1. the digit-1 bin of the k-th key.
+  pick_bin_all<2048>([&](int b) { return sm.h[b]; }, k, sm.wt, &sm.misc[2]);
+  const unsigned bstar = sm.misc[2];
+  unsigned kk = sm.misc[3];
+  unsigned T;
+
+  // 2. above-b* masks (lane e of mlo/mhi holds slot e's), candidates at b*.
+  unsigned mlo = 0u, mhi = 0u, cbase = 0u;
+  for (int e0 = 0; e0 < per; e0 += kKC) {
+    unsigned kc[kKC];
+    load_keys(e0, kc);
+#pragma unroll
+    for (int m = 0; m < kKC; ++m) {
+      const int e = e0 + m;
+      if (e < per) {
+        const int j = e * kFT + tid;
+        const unsigned d1 = kc[m] >> 20;
+        const bool valid = j < n;
+        const uint64_t mg = __ballot(valid && d1 > bstar);
+        mlo = lane == e ? (unsigned)mg : mlo;
+        mhi = lane == e ? (unsigned)(mg >> 32) : mhi;
+        const bool c = valid && d1 == bstar;
+        const uint64_t mc = __ballot(c);
+        const unsigned pos = cbase + __builtin_amdgcn_mbcnt_hi(
+                                         (unsigned)(mc >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mc, 0u));
+        if (c && pos < (unsigned)kWaveCand) {
+          sm.ck[w * kWaveCand + pos] = kc[m];
+          sm.ci[w * kWaveCand + pos] = j;
+        }
+        cbase += (unsigned)__popcll(mc);
+      }
+    }
+  }
+  if (lane < per) sm.gtm[lane * kFW + w] = ((uint64_t)mhi << 32) | mlo;
+  if (lane == 0) sm.ccnt[w] = cbase;
+  __syncthreads();
+  bool fast = true;
+#pragma unroll
+  for (int q = 0; q < kFW; ++q) fast = fast && sm.ccnt[q] <= (unsigned)kWaveCand;
+  // candidate slot i (of kFW * kWaveCand) is in use?
+  auto cand = [&](int i) { return (unsigned)(i % kWaveCand) < sm.ccnt[i / kWaveCand]; };
+  if (fast) {
+    // 3. digits 2 and 3 over the candidates.
+    for (int i = tid; i < 2048; i += kFT) sm.h[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < kFW * kWaveCand; i += kFT)
+      if (cand(i)) atomicAdd(&sm.h[(sm.ck[i] >> 9) & 2047u], 1u);
+    __syncthreads();
+    pick_bin_all<2048>([&](int b) { return sm.h[b]; }, kk, sm.wt, &sm.misc[2]);
+    const unsigned p2 = (bstar << 11) | sm.misc[2];
+    kk = sm.misc[3];
+    __syncthreads();
+    for (int i = tid; i < 512; i += kFT) sm.h[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < kFW * kWaveCand; i += kFT)
+      if (cand(i) && (sm.ck[i] >> 9) == p2) atomicAdd(&sm.h[sm.ck[i] & 511u], 1u);
+    __syncthreads();
+    pick_bin_all<512>([&](int b) { return sm.h[b]; }, kk, sm.wt, &sm.misc[2]);
+    T = (p2 << 9) | sm.misc[2];
+    kk = sm.misc[3];
+    for (int i = tid; i < kFW * kWaveCand; i += kFT) {
+      if (cand(i)) {
+        const unsigned key = sm.ck[i];
+        const int j = sm.ci[i];
+        const uint64_t bit = 1ull << (j & 63);
+        if (key > T) atomicOr(&sm.gtm[j >> 6], bit);
+        else if (key == T) atomicOr(&sm.eqm[j >> 6], bit);
+      }
+    }
+  } else {
+    // Fallback: radix over all keys (digits 11, 11, 9 bits), then the masks
+    // against T.
+    if (tid == 0) atomicOr(&a.sync[kSyncErr], 2u);
+    unsigned prefix = 0u, pmask = 0u;
+    kk = k;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sh = pass == 0 ? 20 : (pass == 1 ? 9 : 0);
+      const unsigned nb = pass == 2 ? 512u : 2048u;
+      __syncthreads();
+      for (int i = tid; i < 2048; i += kFT) sm.h[i] = 0u;
+      __syncthreads();
+      for (int e0 = 0; e0 < per; e0 += kKC) {
+        unsigned kc[kKC];
+        load_keys(e0, kc);
+#pragma unroll
+        for (int m = 0; m < kKC; ++m)
+          if (e0 + m < per && (e0 + m) * kFT + tid < n && (kc[m] & pmask) == prefix)
+            atomicAdd(&sm.h[(kc[m] >> sh) & (nb - 1u)], 1u);
+      }
+      __syncthreads();
+      if (pass < 2)
+        pick_bin_all<2048>([&](int b) { return sm.h[b]; }, kk, sm.wt, &sm.misc[2]);
+      else
+        pick_bin_all<512>([&](int b) { return sm.h[b]; }, kk, sm.wt, &sm.misc[2]);
+      prefix |= sm.misc[2] << sh;
+      pmask |= (nb - 1u) << sh;
+      kk = sm.misc[3];
+    }
+    T = prefix;
+    for (int e0 = 0; e0 < per; e0 += kKC) {
+      unsigned kc[kKC];
+      load_keys(e0, kc);
+#pragma unroll
+      for (int m = 0; m < kKC; ++m) {
+        const int e = e0 + m;
+        if (e < per) {
+          const bool valid = e * kFT + tid < n;
+          const uint64_t mg = __ballot(valid && kc[m] > T);
+          const uint64_t me = __ballot(valid && kc[m] == T);
+          if (lane == 0) {
+            sm.gtm[e * kFW + w] = mg;
+            sm.eqm[e * kFW + w] = me;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // The list: thread g owns group g (groups past the keys are empty).
+  {
+    const int g = tid;
+    const bool in = g < per * kFW;
+    const uint64_t gm = in ? sm.gtm[g] : 0ull;
+    uint64_t em = in ? sm.eqm[g] : 0ull;
+    unsigned tot;
+    const unsigned eqb = block_excl_scan<kFW>((unsigned)__popcll(em), sm.wt, tot);
+    const unsigned room = kk > eqb ? kk - eqb : 0u;
+    // keep the lowest `room` equal channels of the group
+    uint64_t ek = 0ull;
+    for (unsigned c = 0; em != 0ull && c < room; ++c) {
+      ek |= em & (~em + 1ull);
+      em &= em - 1ull;
+    }
+    uint64_t km = gm | ek;
+    unsigned pos = block_excl_scan<kFW>((unsigned)__popcll(km), sm.wt, tot);
+    while (km != 0ull) {
+      const int b = (int)__builtin_ctzll(km);
+      km &= km - 1ull;
+      if (pos < k) xstore_u((unsigned *)&a.sel[pos], (unsigned)(g * 64 + b));
+      ++pos;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) xstore_u(&a.sync[kSyncSelect], 1u);
+}
+
+// ---------------------------------------------------------------------------
+// P3: Stage 2a for 8 list positions (one per wave): exact up/gate rows of the
+// selected channel (contiguous 2*d_model elements), dot2 with x, s = u *
+// SiLU(g) (Sec. 4.1, Stage 2 equations).
+// ---------------------------------------------------------------------------
+// CH 16-byte steps of both rows (and of x) in flight, then their dot products.
+template <bool BF16, int CH>
+__device__ __forceinline__ void p3_pass(const FusedArgs &a, __amdgpu_buffer_rsrc_t rs, uint32_t ubase,
+                                        uint32_t rowb, int m0, int lane, float &au, float &ag) {
+  u4 wu[CH], wg[CH], xr[CH];
+#pragma unroll
+  for (int m = 0; m < CH; ++m) {
+    const uint32_t off = (uint32_t)((m0 + m) * 64 + lane) * 16u;
+    wu[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase, kNT);
+    wg[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase + rowb, kNT);
+  }
+#pragma unroll
+  for (int m = 0; m < CH; ++m) xr[m] = ((const u4 *)a.x)[(m0 + m) * 64 + lane];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < CH; ++m) {
+    au = dot16<BF16>(wu[m], xr[m], au);
+    ag = dot16<BF16>(wg[m], xr[m], ag);
+  }
+}
+
+template <bool BF16>
+__device__ void p3_item(const FusedArgs &a, int item) {
+  if (threadIdx.x == 0) {
+    wait_geq(&a.sync[kSyncSelect], 1u, &a.sync[kSyncErr]);
+    stamp_wait(a);
+  }
+  __syncthreads();
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = item * kFW + wv;
+  if (p < a.k) {
+    const int j = (int)__builtin_amdgcn_readfirstlane((int)xload_u((const unsigned *)&a.sel[p]));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
+    const uint32_t rowb = (uint32_t)a.d_model * ESZ;
+    const uint32_t ubase = (uint32_t)j * 2u * rowb;
+    // One 16-byte step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a
+    // multiple of 1024, so the steps tile the row exactly.
+    const int nstep = (int)(rowb >> 10);
+    float au = 0.0f, ag = 0.0f;
+    int m0 = 0;
+    // 4 steps per pass: 8 KB in flight per wave at ~110 VGPRs (8 steps
+    // would spill with x held in registers).
+    for (; m0 + 4 <= nstep; m0 += 4) p3_pass<BF16, 4>(a, rs, ubase, rowb, m0, lane, au, ag);
+    if (m0 + 2 <= nstep) {
+      p3_pass<BF16, 2>(a, rs, ubase, rowb, m0, lane, au, ag);
+      m0 += 2;
+    }
+    if (m0 < nstep) p3_pass<BF16, 1>(a, rs, ubase, rowb, m0, lane, au, ag);
+    const float u = wave_sum(au);
+    const float g = wave_sum(ag);
+    if (lane == 0) xstore(&a.ssp[p], u * silu(g));
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) xstore_u(&a.sync[kSyncP3 + item * kSyncStride], 1u);
+}
+
+// ---------------------------------------------------------------------------
+// P4: Stage 2b for one (256-column chunk, 128 list positions) item (Sec. 4.1,
+// Stage 2 equations; Sec. 3.1 weighted-sum view): partial y over the item's
+// positions; the last item of a column chunk sums the partials in a fixed
+// order.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
+  constexpr int U = kP4Rows / kFW;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const int rc = item / a.ncol, cc = item % a.ncol;
+  const int p0 = rc * kP4Rows;
+  const int p1 = min(a.k, p0 + kP4Rows);
+  const int lane = threadIdx.x & 63;
+  // Wait for the P3 items of positions [p0, p1): one flag per lane of wave 0.
+  if (threadIdx.x < 64) {
+    const int q0 = p0 / kFW, q1 = (p1 - 1) / kFW;  // at most kP4Rows / 8 = 16 flags
+    const int q = q0 + lane;
+    const unsigned *f = &a.sync[kSyncP3 + min(q, q1) * kSyncStride];
+    unsigned n = 0;
+    while (!__all(xload_u(f) >= 1u)) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++n > (1u << 22)) {
+        if (lane == 0) atomicOr(&a.sync[kSyncErr], 1u);
+        break;
+      }
+    }
+    if (lane == 0) stamp_wait(a);
+  }
+  __syncthreads();
+  if (threadIdx.x < kP4Rows) {
+    const int pp = p0 + (int)threadIdx.x;
+    const int pc = pp < p1 ? pp : p0;
+    const unsigned j = xload_u((const unsigned *)&a.sel[pc]);
+    const float sv = xload(&a.ssp[pc]);
+    sm.rs[threadIdx.x] = (int)j;
+    sm.sv[threadIdx.x] = pp < p1 ? sv : 0.0f;
+  }
+  __syncthreads();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t chunk_bytes = (size_t)a.d_ff * kDownCols * ESZ;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc((const char *)a.wd + cc * chunk_bytes, (uint32_t)chunk_bytes);
+  const uint32_t voff = (uint32_t)lane * 4u * ESZ;
+  using WT = typename std::conditional<BF16, u2, u4>::type;
+  WT wr[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = wv + kFW * u;
+    const uint32_t rowoff = (uint32_t)__builtin_amdgcn_readfirstlane(sm.rs[r]) * (uint32_t)(kDownCols * ESZ);
+    if constexpr (BF16)
+      wr[u] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, rowoff, kNT);
+    else
+      wr[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, kNT);
+  }
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float sv = sm.sv[wv + kFW * u];
+    float wf[4];
+    if constexpr (BF16) {
+      wf[0] = bf16_to_f32(wr[u].x & 0xffffu);
+      wf[1] = bf16_to_f32(wr[u].x >> 16);
+      wf[2] = bf16_to_f32(wr[u].y & 0xffffu);
+      wf[3] = bf16_to_f32(wr[u].y >> 16);
+    } else {
+      wf[0] = __uint_as_float(wr[u].x);
+      wf[1] = __uint_as_float(wr[u].y);
+      wf[2] = __uint_as_float(wr[u].z);
+      wf[3] = __uint_as_float(wr[u].w);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = fmaf(sv, wf[c], acc[c]);
+  }
+  *(float4 *)&sm.red[wv][lane * 4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  if (threadIdx.x < kDownCols) {
+    const int c = threadIdx.x;
+    float v = sm.red[0][c];
+#pragma unroll
+    for (int q = 1; q < kFW; ++q) v += sm.red[q][c];
+    xstore(&a.ypart[(size_t)rc * a.d_model + cc * kDownCols + c], v);
+  }
+  if (!arrive_last(&a.col_cnt[cc], (unsigned)a.nrc, s_flag)) return;
+  // Sum of the nrc partials of the chunk: wave q adds rows q, q + 8, ... of
+  // 4 columns per lane (agent-coherent 16-byte loads), then the 8 wave sums
+  // are added in wave order.
+  {
+    const int q = wv;
+    const __amdgpu_buffer_rsrc_t yr =
+        make_rsrc(a.ypart, (uint32_t)((size_t)a.nrc * a.d_model * sizeof(float)));
+    const uint32_t coff = (uint32_t)(cc * kDownCols + lane * 4) * 4u;
+    float4 s4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int r0 = q; r0 < a.nrc; r0 += kFW * 8) {
+      u4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = min(r0 + kFW * u, a.nrc - 1);
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(yr, coff, (uint32_t)r * a.d_model * 4u, kSelBits);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (r0 + kFW * u < a.nrc) {
+          s4.x += __uint_as_float(v[u].x);
+          s4.y += __uint_as_float(v[u].y);
+          s4.z += __uint_as_float(v[u].z);
+          s4.w += __uint_as_float(v[u].w);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with red
+    *(float4 *)&sm.red[q][lane * 4] = s4;
+  }
+  __syncthreads();
+  if (threadIdx.x < kDownCols) {
+    const int c = threadIdx.x;
+    float v = sm.red[0][c];
+#pragma unroll
+    for (int q = 1; q < kFW; ++q) v += sm.red[q][c];
+    const int col = cc * kDownCols + c;
+    st_elem<BF16>(a.y, col, v);
+    if (a.resid) a.resid[col] += round_elem<BF16>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The persistent kernel.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) void ffn_fused_kernel(
+    FusedArgs a) {
+  __shared__ union {
+    P1Smem p1;
+    P2Smem p2;
+    P4Smem p4;
+  } sm;
+  __shared__ int s_ticket, s_flag;
+  const int total = a.n_p1 + 1 + a.n_p3 + a.n_p4;
+  for (;;) {
+    __syncthreads();  // the previous item is done with the LDS
+    if (threadIdx.x == 0)
+      s_ticket = (int)__hip_atomic_fetch_add(&a.sync[kSyncTicket], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = s_ticket;
+    if (t >= total) break;
+    unsigned long long t0 = 0;
+    if (a.trace && threadIdx.x == 0) {
+      t0 = __builtin_amdgcn_s_memrealtime();
+      g_twait = t0;
+    }
+    int r = t;
+    if (r < a.n_p1) {
+      p1_item<BF16>(a, r, sm.p1, &s_flag);
+    } else if ((r -= a.n_p1) == 0) {
+      p2_select(a, sm.p2);
+    } else if ((r -= 1) < a.n_p3) {
+      p3_item<BF16>(a, r);
+    } else {
+      p4_item<BF16>(a, r - a.n_p3, sm.p4, &s_flag);
+    }
+    if (a.trace && threadIdx.x == 0) {
+      unsigned long long *e = a.trace + 4 * (size_t)t;
+      e[0] = t0;
+      e[1] = g_twait;
+      e[2] = __builtin_amdgcn_s_memrealtime();
+      e[3] = blockIdx.x;
+    }
+  }
+  // The last work-group out clears the ticket and flags for the next launch.
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_flag = __hip_atomic_fetch_add(&a.sync[kSyncExit], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
+  __syncthreads();
+  if (s_flag) {
+    for (int i = threadIdx.x; i < 5 + a.n_p3; i += kFT) {
+      const int w = i < 5 ? i * kSyncStride : kSyncP3 + (i - 5) * kSyncStride;
+      if (w != kSyncErr) xstore_u(&a.sync[w], 0u);
+    }
+    for (int i = threadIdx.x; i < 2048; i += kFT) xstore_u(&a.ghist[i], 0u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launcher
+// ---------------------------------------------------------------------------
+template <bool BF16>
+static hipError_t fused_go(FusedArgs &a, hipStream_t s) {
+  auto fn = ffn_fused_kernel<BF16>;
+  static int cap = 0;
+  if (!cap) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, kFT, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    cap = per_cu * cus;
+  }
+  const int total = a.n_p1 + 1 + a.n_p3 + a.n_p4;
+  const int grid = total < cap ? total : cap;
+  fn<<<grid, kFT, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+bool fused_supported(const Plan &p) {
+  return (p.d_ff + kFT - 1) / kFT <= kMaxPer && ((size_t)p.d_model * p.esz) % 1024 == 0;
+}
+
+// Sync block: control words, P3 flags, then the digit-1 histogram.
+static size_t fused_hist_word(const Plan &p) {
+  return (size_t)kSyncP3 + (size_t)((p.d_ff + kFW - 1) / kFW) * kSyncStride;
+}
+
+size_t fused_sync_words(const Plan &p) { return fused_hist_word(p) + 2048; }
+
+int fused_ypart_rows(const Plan &p) { return (p.d_ff + kP4Rows - 1) / kP4Rows; }
+
+int fused_items(const Plan &p, int k) {
+  return p.ntile * p.nchunk + 1 + (k + kFW - 1) / kFW + p.ncol * ((k + kP4Rows - 1) / kP4Rows);
+}
+
+hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
+                        float *resid, hipStream_t s, unsigned long long *trace) {
+  FusedArgs a{};
+  a.trace = trace;
+  a.pq = b.pq;
+  a.psc = b.psc;
+  a.wug = b.wug;
+  a.wug_bytes = (uint32_t)((size_t)p.d_ff * 2 * p.d_model * p.esz);
+  a.wd = b.wd;
+  a.d_model = p.d_model;
+  a.d_ff = p.d_ff;
+  a.G = p.G;
+  a.ngroups = p.ngroups;
+  a.ntile = p.ntile;
+  a.nchunk = p.nchunk;
+  a.ncol = p.ncol;
+  a.nrc = (k + kP4Rows - 1) / kP4Rows;
+  a.x = x;
+  a.tau = tau;
+  a.k = k;
+  a.y = y;
+  a.resid = resid;
+  a.part = b.part;
+  a.tile_cnt = b.tile_cnt;
+  a.sabs = b.sabs;
+  a.sel = b.sel;
+  a.ssp = b.ssp;
+  a.ypart = b.ypart;
+  a.col_cnt = b.col_cnt;
+  a.sync = b.sync;
+  a.ghist = b.sync + fused_hist_word(p);
+  a.n_p1 = p.ntile * p.nchunk;
+  a.n_p3 = (k + kFW - 1) / kFW;
+  a.n_p4 = p.ncol * a.nrc;
+  return p.bf16 ? fused_go<true>(a, s) : fused_go<false>(a, s);
+}
+
+}  // namespace prox

@@ -41,6 +41,7 @@ struct Bufs {
   uint8_t *umask;  // [d_ff]                        token bits per union entry
   float *ypart;    // [nrc][batch][d_model]         Stage 2 down partial sums
   unsigned *col_cnt;  // [ncol]                    Stage 2 arrival counters
+  unsigned *sync;  // [(5 + ceil(d_ff/8)) * 64]     fused kernel tickets and flags
   void *xbuf;      // [batch][d_model] dtype         stack: normalized input
   void *ybuf;      // [batch][d_model] dtype         stack: layer output
 };
@@ -54,13 +55,14 @@ struct Plan {
   int ncol;         // d_model / 256
   int nrc;          // row chunks of the down projection
   int upgate_cap;   // max work-groups of the up/gate kernel
+  int use_fused;    // batch-1 forwards run the persistent fused kernel
 };
 
 struct Layout {
   size_t weights, proxy, workspace;
   size_t o_wd, o_psc;
   size_t o_part, o_tile_cnt, o_sabs, o_sel, o_ssp, o_uni, o_nuni, o_umask,
-      o_ypart, o_col_cnt, o_xbuf, o_ybuf;
+      o_ypart, o_col_cnt, o_sync, o_xbuf, o_ybuf;
 };
 
 Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch);
@@ -89,5 +91,20 @@ hipError_t launch_compact_debug(const Plan &p, const void *x, int batch,
 hipError_t launch_rmsnorm(const Plan &p, const float *resid, int batch,
                           float eps, void *x, hipStream_t s);
 hipError_t launch_zero_y(const Plan &p, void *y, int batch, hipStream_t s);
+
+// The batch-1 step as one persistent kernel (prox_fused.hip).
+bool fused_supported(const Plan &p);
+size_t fused_sync_words(const Plan &p);
+int fused_ypart_rows(const Plan &p);  // partial-y rows the fused kernel needs
+// trace: optional [fused_items][4] u64 timeline (start, wait end, end, block).
+hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
+                        float *resid, hipStream_t s, unsigned long long *trace = nullptr);
+int fused_items(const Plan &p, int k);
+// Words between two control words of the fused kernel (one 256-byte line each).
+#ifndef PROX_SYNC_STRIDE
+#define PROX_SYNC_STRIDE 64
+#endif
+constexpr int kSyncStride = PROX_SYNC_STRIDE;
+constexpr int kFusedErrWord = 4 * kSyncStride;  // index of the sticky error word in Bufs::sync
 
 }  // namespace prox

@@ -40,7 +40,7 @@ class prox_debug(ctypes.Structure):
     _fields_ = [("n1", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("s_abs", ctypes.c_void_p), ("sel", ctypes.c_void_p),
                 ("s_sel", ctypes.c_void_p), ("n_union", ctypes.c_void_p),
-                ("union_idx", ctypes.c_void_p)]
+                ("union_idx", ctypes.c_void_p), ("status", ctypes.c_void_p)]
 
 
 _lib = None
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH):
                                        ctypes.POINTER(I), P], I),
         "prox_dense_ffn_forward_profiled": ([P, P, I, P, ctypes.POINTER(P), I,
                                              ctypes.POINTER(I), P], I),
+        "prox_ffn_forward_traced": ([P, P, F, I, P, P, I, ctypes.POINTER(I), P], I),
         "prox_rmsnorm": ([P, P, I, F, P, P], I),
         "prox_destroy_layer": ([P], None),
         "prox_last_error": ([], ctypes.c_char_p),
@@ -220,9 +221,10 @@ def prox_ffn_forward_debug(layer: Layer, x, threshold: float, k: int):
         s_sel=torch.full((B, layer.d_ff), float("nan"), device=dev),
         n_union=torch.zeros(1, dtype=torch.int32, device=dev),
         union_idx=torch.full((layer.d_ff,), -1, dtype=torch.int32, device=dev),
+        status=torch.zeros(1, dtype=torch.int32, device=dev),
     )
     dbg = prox_debug(*(ctypes.c_void_p(out[k].data_ptr()) for k in
-                       ("n1", "idx", "s_abs", "sel", "s_sel", "n_union", "union_idx")))
+                       ("n1", "idx", "s_abs", "sel", "s_sel", "n_union", "union_idx", "status")))
     _check(load_library().prox_ffn_forward_debug(layer.handle, _ptr(x), B, float(threshold),
                                                  int(k), _ptr(out["y"]), ctypes.byref(dbg),
                                                  _stream()))
@@ -273,6 +275,24 @@ def prox_dense_ffn_forward_profiled(layer: Layer, x, events, y=None):
         layer.handle, _ptr(x), B, _ptr(y), _event_array(events), len(events),
         ctypes.byref(n), _stream()))
     return y, n.value
+
+
+def prox_ffn_forward_traced(layer: Layer, x, threshold: float, k: int, y=None):
+    """Batch-1 forward on the persistent kernel with its per-ticket timeline.
+
+    Returns (y, trace, counts): trace is an int64 tensor [tickets][4] of
+    (start, wait end, end, work-group), times in 100 MHz clock ticks; counts
+    gives the tickets of each phase (Stage 1, select, up/gate, down)."""
+    y = _out_like(x, y)
+    counts = (ctypes.c_int * 4)()
+    lib = load_library()
+    _check(lib.prox_ffn_forward_traced(layer.handle, _ptr(x), float(threshold), int(k), _ptr(y),
+                                       None, 0, counts, _stream()))
+    total = sum(counts)
+    trace = torch.zeros(total, 4, dtype=torch.int64, device=x.device)
+    _check(lib.prox_ffn_forward_traced(layer.handle, _ptr(x), float(threshold), int(k), _ptr(y),
+                                       _ptr(trace), total, counts, _stream()))
+    return y, trace, list(counts)
 
 
 def prox_stack_forward(layers, thresholds, k: int, resid, eps: float = 1e-5):

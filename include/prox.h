@@ -102,7 +102,10 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
 prox_status prox_export_proxy(const prox_layer *layer, int matrix /*0 up, 1 gate*/,
                               int8_t *codes, float *scales, void *stream);
 
-/* One token: y = Prox-FFN(x) (batch 1, the decode hot path).
+/* One token: y = Prox-FFN(x) (batch 1, the decode hot path).  Runs as one
+ * persistent kernel whose work-groups take Stage 1, top-k, Stage 2 up/gate
+ * and Stage 2 down items in dependency order (setting the environment
+ * variable PROX_PATH=multi before prepare selects the four-kernel form).
  *   x          [d_model] layer dtype
  *   threshold  tau of the Stage 1 input mask; an input survives iff
  *              |x_i| >= threshold (so threshold <= 0 keeps every input and
@@ -131,6 +134,9 @@ typedef struct {
   float *s_sel;      /* [batch][d_ff]      exact s of sel[b][t] at t (k used) */
   int32_t *n_union;  /* [1]                size of the union of the masks     */
   int32_t *union_idx;/* [d_ff]             the union, ascending               */
+  int32_t *status;   /* [1]  0, or bit 0: a bounded wait of the fused batch-1
+                        kernel timed out (results invalid); bit 1: its top-k
+                        took the slow exact path (results valid)             */
 } prox_debug;
 
 /* prox_ffn_forward_batch plus a copy of its intermediate results into `dbg`. */
@@ -178,6 +184,21 @@ prox_status prox_dense_ffn_forward_profiled(const prox_layer *layer,
                                             const void *x, int batch, void *y,
                                             void *const *events, int n_events,
                                             int *n_recorded, void *stream);
+
+/* Timeline of one batch-1 forward on the persistent kernel (the default path
+ * of prox_ffn_forward for k > 0), for performance work.  The launch takes
+ * work items by ticket: counts[0..3] (host) receive the number of Stage 1
+ * items, select items (1), Stage 2 up/gate items (ceil(k/8)) and Stage 2 down
+ * items; their sum is the ticket count.  With trace == NULL only counts are
+ * written.  Otherwise trace (device, [trace_items >= tickets][4] u64) receives
+ * per ticket: start, end of its wait for earlier items, end (ticks of the
+ * 100 MHz GPU real-time clock) and the work-group that ran it.  y is the
+ * same as prox_ffn_forward's.  PROX_EUNSUPPORTED when the layer runs the
+ * multi-kernel path (PROX_PATH=multi at prepare time).                       */
+prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x,
+                                   float threshold, int k, void *y,
+                                   unsigned long long *trace, int trace_items,
+                                   int *counts, void *stream);
 
 /* Release a handle (host memory only; the caller's buffers are untouched). */
 void prox_destroy_layer(prox_layer *layer);

@@ -67,6 +67,8 @@ def get_case(cfg, gen_device="cpu", max_batch=1):
 def _check_token(case, x_row_dev, x_np, tau, k, out, t=0, stats=None):
     """Compare token t of a debug forward with the oracle."""
     cfg = case.cfg
+    # bit 0: a bounded wait of the persistent kernel timed out
+    assert (int(out["status"][0]) & 1) == 0, f"status word {int(out['status'][0])}"
     ref = oracle.forward(case.ol, x_np, tau, k)
     n1 = int(out["n1"][t])
     assert n1 == ref["idx"].size
@@ -305,3 +307,39 @@ def test_70b_batch_parity(B):
     torch.cuda.synchronize()
     for t in range(B):
         _check_token(case, X[t], X[t].float().cpu().numpy(), case.tau, k, out, t=t)
+
+
+# ---------------------------------------------------------------------------
+# The multi-kernel path (PROX_PATH=multi at prepare time) against the oracle
+# and against the persistent single-launch path of the same layer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["ragged", "8b"])
+def test_multi_kernel_path_parity(name, monkeypatch):
+    cfg = RAGGED if name == "ragged" else synth.CONFIGS["8b"]
+    gen = "cpu" if name == "ragged" else DEV
+    fused = get_case(cfg, gen)
+    monkeypatch.setenv("PROX_PATH", "multi")
+    multi = Case(cfg, 0, gen, 1)
+    monkeypatch.delenv("PROX_PATH")
+    k = synth.k_for(cfg.d_ff, 0.7)
+    X = synth.make_inputs(cfg, 2, "paths", 0, gen)
+    for t in range(X.shape[0]):
+        xd = X[t:t + 1].to(DEV)
+        out = prox.prox_ffn_forward_debug(multi.L, xd, multi.tau, k)
+        yf = prox.prox_ffn_forward(fused.L, xd[0], fused.tau, k)
+        torch.cuda.synchronize()
+        _check_token(multi, xd, X[t].float().cpu().numpy(), multi.tau, k, out)
+        e = rel_err(yf.float().cpu().numpy(), out["y"][0].float().cpu().numpy())
+        assert e <= _tol(cfg), f"paths differ by {e:.3e}"
+
+
+def test_fused_path_repeated_launches_are_identical():
+    """The persistent kernel resets its ticket and flags on exit: many
+    back-to-back launches on one stream give the same bits."""
+    case = get_case(RAGGED)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    x = case.inputs(1, "repeat")[0].to(DEV)
+    ys = [prox.prox_ffn_forward(case.L, x, case.tau, k) for _ in range(50)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
