@@ -356,6 +356,14 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
     if (dbg->s_abs &&
         (e = hipMemcpyAsync(dbg->s_abs, b.sabs, nf * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
       return hip_fail(e, "copy |s~|");
+    if (batch == 1 && p.use_fused) {
+      // the persistent kernel keeps per-range masks and s by channel
+      int *selp = dbg->sel ? (int *)dbg->sel : b.sel;
+      if ((dbg->sel || dbg->s_sel) &&
+          (e = prox::launch_fused_list(p, b, k, selp, (float *)dbg->s_sel, s)) != hipSuccess)
+        return hip_fail(e, "list kernel");
+      return PROX_OK;
+    }
     if (dbg->sel &&
         (e = hipMemcpyAsync(dbg->sel, b.sel, nf * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
       return hip_fail(e, "copy sel");
@@ -444,7 +452,7 @@ prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x, floa
   if (!p.use_fused) return fail(PROX_EUNSUPPORTED, "the layer does not use the persistent kernel");
   if (k == 0) return fail(PROX_EINVAL, "k = 0 launches no persistent kernel");
   if (!counts) return fail(PROX_EINVAL, "counts is NULL");
-  const int n_p1 = p.ntile * p.nchunk, n_p3 = (k + 7) / 8;
+  const int n_p1 = p.ntile * p.nchunk, n_p3 = prox::fused_p3_items(p);
   const int total = prox::fused_items(p, k);
   counts[0] = n_p1;
   counts[1] = 1;

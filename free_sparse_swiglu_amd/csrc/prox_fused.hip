@@ -10,20 +10,27 @@
 //   P1  Stage 1 proxy, one item per (256-column tile, 512-row chunk); the
 //       last item of a tile also adds the tile's digit-1 counts of |s~| to a
 //       global histogram;
-//   P2  the top-k threshold (one item): from the histogram, one pass over the
-//       keys and a small radix select it publishes the k-th key T and, per
-//       group of 64 channels, how many kept channels precede the group;
-//   P3  Stage 2 up/gate + SwiGLU, one item per 8 list positions; each wave
-//       finds the channel at its position from the group table;
-//   P4  Stage 2 down projection, one item per (256-column chunk, 128 rows).
+//   P2  the top-k threshold (one item): the histogram gives the digit-1 bin
+//       b* of the k-th key, which is published at once; the keys in that bin
+//       then give the exact k-th key T and the tie cutoff J;
+//   P3  Stage 2 up/gate + SwiGLU, one item per 32 consecutive channels: the
+//       channels with digit 1 above b* (selected whatever T is) and those in
+//       bin b* (about twice as many as will be kept), so nothing waits for T;
+//   P4  Stage 2 down projection, one item per (512 channels, 256 columns):
+//       with T and J known, the kept channels of the range, ascending, give a
+//       partial y; the last item of a column chunk adds the partials in range
+//       order.
+// The selection of channel j is: |s~_j| > T, or |s~_j| = T and j <= J (the
+// lowest-index channels win ties), which keeps exactly k channels.
+//
 // Work-groups take items from a global ticket counter in exactly that order.
 // An item only ever waits for items with smaller tickets (P2 for all of P1,
-// P3 for P2, P4 for the P3 items covering its rows); those were handed to
-// running work-groups before it, and P1 items wait for nothing, so the
-// schedule cannot deadlock whatever the residency.  Every wait is bounded
-// (wait_geq).  Data passed between work-groups goes through agent-coherent
-// accesses (xstore/xload and sc1 buffer loads); the last work-group to leave
-// resets the ticket, the flags and the histogram for the next launch.
+// P3 for P2, P4 for P2 and the P3 items of its range); those were handed to running
+// work-groups before it, and P1 items wait for nothing, so the schedule
+// cannot deadlock whatever the residency.  Every wait is bounded.  Data
+// passed between work-groups goes through agent-coherent accesses
+// (xstore/xload, sc1 buffer loads); the last work-group to leave resets the
+// ticket, the flags and the histogram for the next launch.
 #include <type_traits>
 
 #include "prox_device.h"
@@ -36,10 +43,11 @@ namespace prox {
 enum : int {
   kSyncTicket = 0 * kSyncStride,  // next ticket
   kSyncTiles = 1 * kSyncStride,   // P1 tiles finished
-  kSyncSelect = 2 * kSyncStride,  // P2 finished (0/1)
+  kSyncSelect = 2 * kSyncStride,  // T and J published (0/1); T at +1, J at +2
   kSyncExit = 3 * kSyncStride,    // work-groups that left the item loop
   kSyncErr = 4 * kSyncStride,     // sticky error bits (1: a wait timed out, 2: select fallback used)
-  kSyncP3 = 5 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
+  kSyncBin = 5 * kSyncStride,     // b* + 1 once published (0 before)
+  kSyncP3 = 6 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
 };
 static_assert(kSyncErr == kFusedErrWord, "error word index");
 
@@ -48,8 +56,9 @@ constexpr int kFT = kFW * 64;      // threads per work-group
 constexpr int kWaveCand = 256;     // top-k candidates per wave held in LDS (fast path)
 constexpr int kMaxPer = 64;        // key slots per thread: d_ff <= 64 * 512
 constexpr int kGroups = kMaxPer * kFW;  // groups of 64 channels: d_ff <= 512 * 64
-constexpr int kKC = 16;            // key slots loaded per round of a select pass
-constexpr int kP4Rows = 128;       // list positions per P4 item (16 per wave)
+constexpr int kKC = 32;            // key slots loaded per round of a select pass
+constexpr int kP3Ch = 32;          // channels per P3 item
+constexpr int kP4Ch = 512;         // channels per P4 item (kP4Ch / kP3Ch P3 items)
 constexpr int kSelBits = 16;       // buffer-load aux bit: sc1 (agent-coherent)
 
 struct FusedArgs {
@@ -58,7 +67,7 @@ struct FusedArgs {
   const void *wug;
   uint32_t wug_bytes;
   const void *wd;
-  int d_model, d_ff, G, ngroups, ntile, nchunk, ncol, nrc;
+  int d_model, d_ff, G, ngroups, ntile, nchunk, ncol, nrange;
   const void *x;
   float tau;
   int k;
@@ -67,12 +76,12 @@ struct FusedArgs {
   float *part;
   unsigned *tile_cnt;
   float *sabs;
-  int *sel;
-  float *ssp;
+  float *sdense;    // [d_ff] exact s of each kept channel (others stale)
   float *ypart;
   unsigned *col_cnt;
   unsigned *sync;
   unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
+  unsigned *gmask;  // [n_p3][2] per P3 item: channels above bin b*, channels in it
   int n_p1, n_p3, n_p4;
   unsigned long long *trace;  // optional per-ticket timeline (nullptr: off)
 };
@@ -82,6 +91,19 @@ struct FusedArgs {
 __shared__ unsigned long long g_twait;
 __device__ __forceinline__ void stamp_wait(const FusedArgs &a) {
   if (a.trace) g_twait = __builtin_amdgcn_s_memrealtime();
+}
+
+// Bounded wait of a whole wave until every lane's flag is >= 1 (lanes with
+// nothing to wait for pass their own satisfied flag).
+__device__ __forceinline__ void wave_wait_flags(const unsigned *f, unsigned *err) {
+  unsigned n = 0;
+  while (!__all(xload_u(f) >= 1u)) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++n > (1u << 22)) {
+      if ((threadIdx.x & 63) == 0) atomicOr(err, 1u);
+      break;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -96,16 +118,19 @@ struct P2Smem {
   unsigned h[2048];
   unsigned ck[kFW * kWaveCand];  // candidate keys (per-wave lists)
   int ci[kFW * kWaveCand];       // candidate channels
-  uint64_t gtm[kGroups];         // per group of 64 channels: keys above T
-  uint64_t eqm[kGroups];         // ... and equal to T
+  unsigned ceq[kGroups];         // per group of 64 channels: keys equal to T
   unsigned ccnt[kFW];
   unsigned wt[16];
   unsigned misc[8];
 };
+struct P3Smem {
+  unsigned bstar;
+};
 struct P4Smem {
   float red[kFW][kDownCols];
-  int rs[kP4Rows];
-  float sv[kP4Rows];
+  int rs[kP4Ch];
+  float sv[kP4Ch];
+  unsigned wcnt[kFW];
 };
 
 // ---------------------------------------------------------------------------
@@ -126,6 +151,11 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
 
   if (sl < nsl) {
+    // the slice's scales first, so that their latency hides behind the rest
+    const int g = (sl * 64) / a.G;
+    const float4 *sp =
+        (const float4 *)(a.psc + ((size_t)t * a.ngroups + g) * 512 + (size_t)lane * 8);
+    const float4 s0 = sp[0], s1 = sp[1];
     float xl;
     const uint64_t un = slice_mask<BF16>(a.x, (size_t)sl * 64, a.tau, xl);
     const float xm = ((un >> lane) & 1ull) ? xl : 0.0f;
@@ -210,10 +240,6 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
       if (base + U < cnt) consume(base + U, wb);
     }
     const float off = BF16 ? 136.0f : 8.0f;
-    const int g = (sl * 64) / a.G;
-    const float4 *sp =
-        (const float4 *)(a.psc + ((size_t)t * a.ngroups + g) * 512 + (size_t)lane * 8);
-    const float4 s0 = sp[0], s1 = sp[1];
     const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = sc[c] * (acc[c] - off * xsum);
@@ -263,26 +289,23 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
 }
 
 // ---------------------------------------------------------------------------
-// P2: the top-k select (App. A.6, top-k equation), ties to the lower index.
+// P2: the top-k threshold (App. A.6, top-k equation), ties to the lower index.
 // ---------------------------------------------------------------------------
 // |s~| >= 0, so its float32 bits order like the value; digit 1 = bits 30..20,
 // digit 2 = bits 19..9, digit 3 = bits 8..0.  Channel j is read by thread
 // j % 512 in slot j / 512 and belongs to group j / 64 (one wave, one slot).
 // Fast path:
 //   1. the global digit-1 histogram (built by the P1 tile epilogues) gives
-//      the bin b* of the k-th largest key and the rank kk of that key in it;
-//   2. one pass over the keys records, per group, the bit mask of keys with
-//      digit 1 above b* and gathers the keys with digit 1 = b* (typically a
+//      the bin b* of the k-th largest key; b* is published for P3;
+//   2. one pass over the keys gathers those with digit 1 = b* (typically a
 //      few hundred) in per-wave LDS lists;
 //   3. two radix steps over the gathered keys give the k-th key T and the
-//      number kk of keys equal to T that are kept (the lowest-index ones);
-//      the gathered keys then set their bits in their group's above-T or
-//      equal-to-T mask.
+//      number kk of keys equal to T that are kept;
+//   4. the tie cutoff J: the channel of the kk-th key equal to T in index
+//      order (every key equal to T was gathered); J = d_ff - 1 when all of
+//      them are kept, the usual case.
 // Fallback (a wave gathers more than kWaveCand keys, e.g. massive exact
-// ties): the radix steps and the masks over all keys.
-// List: one thread per group keeps its above-T channels and its first
-// min(equal, kk - equal channels before the group) equal ones; a block scan
-// of the kept counts places each group's channels, ascending, in sel.
+// ties): the radix steps over all keys.
 
 // All waves: bins [NB - (t+1)*BPL, NB - t*BPL) belong to thread t (from the
 // top).  Finds the bin holding the kk-th largest; 2 barriers.
@@ -334,17 +357,18 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
     }
   };
   for (int i = tid; i < 2048; i += kFT) sm.h[i] = xload_u(&a.ghist[i]);
-  for (int i = tid; i < kGroups; i += kFT) sm.eqm[i] = 0ull;
+  for (int i = tid; i < kGroups; i += kFT) sm.ceq[i] = 0u;
   __syncthreads();
 
-  // 1. the digit-1 bin of the k-th key.
+  // 1. the digit-1 bin of the k-th key, published at once.
   pick_bin_all<2048>([&](int b) { return sm.h[b]; }, k, sm.wt, &sm.misc[2]);
   const unsigned bstar = sm.misc[2];
   unsigned kk = sm.misc[3];
+  if (tid == 0) xstore_u(&a.sync[kSyncBin], bstar + 1u);
   unsigned T;
 
-  // 2. above-b* masks (lane e of mlo/mhi holds slot e's), candidates at b*.
-  unsigned mlo = 0u, mhi = 0u, cbase = 0u;
+  // 2. candidates at b*.
+  unsigned cbase = 0u;
   for (int e0 = 0; e0 < per; e0 += kKC) {
     unsigned kc[kKC];
     load_keys(e0, kc);
@@ -353,12 +377,7 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
       const int e = e0 + m;
       if (e < per) {
         const int j = e * kFT + tid;
-        const unsigned d1 = kc[m] >> 20;
-        const bool valid = j < n;
-        const uint64_t mg = __ballot(valid && d1 > bstar);
-        mlo = lane == e ? (unsigned)mg : mlo;
-        mhi = lane == e ? (unsigned)(mg >> 32) : mhi;
-        const bool c = valid && d1 == bstar;
+        const bool c = j < n && (kc[m] >> 20) == bstar;
         const uint64_t mc = __ballot(c);
         const unsigned pos = cbase + __builtin_amdgcn_mbcnt_hi(
                                          (unsigned)(mc >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mc, 0u));
@@ -370,13 +389,12 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
       }
     }
   }
-  if (lane < per) sm.gtm[lane * kFW + w] = ((uint64_t)mhi << 32) | mlo;
   if (lane == 0) sm.ccnt[w] = cbase;
   __syncthreads();
   bool fast = true;
 #pragma unroll
   for (int q = 0; q < kFW; ++q) fast = fast && sm.ccnt[q] <= (unsigned)kWaveCand;
-  // candidate slot i (of kFW * kWaveCand) is in use?
+  // candidate slot i (of kFW * kWaveCand) in use?
   auto cand = [&](int i) { return (unsigned)(i % kWaveCand) < sm.ccnt[i / kWaveCand]; };
   if (fast) {
     // 3. digits 2 and 3 over the candidates.
@@ -397,18 +415,12 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
     pick_bin_all<512>([&](int b) { return sm.h[b]; }, kk, sm.wt, &sm.misc[2]);
     T = (p2 << 9) | sm.misc[2];
     kk = sm.misc[3];
-    for (int i = tid; i < kFW * kWaveCand; i += kFT) {
-      if (cand(i)) {
-        const unsigned key = sm.ck[i];
-        const int j = sm.ci[i];
-        const uint64_t bit = 1ull << (j & 63);
-        if (key > T) atomicOr(&sm.gtm[j >> 6], bit);
-        else if (key == T) atomicOr(&sm.eqm[j >> 6], bit);
-      }
-    }
+    // keys equal to T, per group
+    for (int i = tid; i < kFW * kWaveCand; i += kFT)
+      if (cand(i) && sm.ck[i] == T) atomicAdd(&sm.ceq[sm.ci[i] >> 6], 1u);
   } else {
-    // Fallback: radix over all keys (digits 11, 11, 9 bits), then the masks
-    // against T.
+    // Fallback: radix over all keys (digits 11, 11, 9 bits), then the equal
+    // counts per group.
     if (tid == 0) atomicOr(&a.sync[kSyncErr], 2u);
     unsigned prefix = 0u, pmask = 0u;
     kk = k;
@@ -444,41 +456,57 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
       for (int m = 0; m < kKC; ++m) {
         const int e = e0 + m;
         if (e < per) {
-          const bool valid = e * kFT + tid < n;
-          const uint64_t mg = __ballot(valid && kc[m] > T);
-          const uint64_t me = __ballot(valid && kc[m] == T);
-          if (lane == 0) {
-            sm.gtm[e * kFW + w] = mg;
-            sm.eqm[e * kFW + w] = me;
-          }
+          const uint64_t me = __ballot(e * kFT + tid < n && kc[m] == T);
+          if (lane == 0) sm.ceq[e * kFW + w] = (unsigned)__popcll(me);
         }
       }
     }
   }
   __syncthreads();
 
-  // The list: thread g owns group g (groups past the keys are empty).
-  {
-    const int g = tid;
-    const bool in = g < per * kFW;
-    const uint64_t gm = in ? sm.gtm[g] : 0ull;
-    uint64_t em = in ? sm.eqm[g] : 0ull;
-    unsigned tot;
-    const unsigned eqb = block_excl_scan<kFW>((unsigned)__popcll(em), sm.wt, tot);
-    const unsigned room = kk > eqb ? kk - eqb : 0u;
-    // keep the lowest `room` equal channels of the group
-    uint64_t ek = 0ull;
-    for (unsigned c = 0; em != 0ull && c < room; ++c) {
-      ek |= em & (~em + 1ull);
-      em &= em - 1ull;
+  // 4. tie cutoff (wave 0): the group holding the kk-th equal key, then the
+  // lane inside it.
+  if (w == 0) {
+    constexpr int CPL = kGroups / 64;
+    const int ng = per * kFW;
+    unsigned ce[CPL], se = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int g = lane * CPL + i;
+      ce[i] = g < ng ? sm.ceq[g] : 0u;
+      se += ce[i];
     }
-    uint64_t km = gm | ek;
-    unsigned pos = block_excl_scan<kFW>((unsigned)__popcll(km), sm.wt, tot);
-    while (km != 0ull) {
-      const int b = (int)__builtin_ctzll(km);
-      km &= km - 1ull;
-      if (pos < k) xstore_u((unsigned *)&a.sel[pos], (unsigned)(g * 64 + b));
-      ++pos;
+    const unsigned incl = wave_incl_scan_dpp(se);
+    const unsigned total = __builtin_amdgcn_readlane(incl, 63);
+    int J = n - 1;
+    if (total > kk) {
+      // group g* with eq-before < kk <= eq-before + ce, and kk's rank in it
+      unsigned eb = incl - se;
+      int gsel = -1;
+      unsigned rin = 0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        if (eb < kk && eb + ce[i] >= kk) {
+          gsel = lane * CPL + i;
+          rin = kk - eb;  // 1-based
+        }
+        eb += ce[i];
+      }
+      const uint64_t who = __ballot(gsel >= 0);
+      const int src = who ? (int)__builtin_ctzll(who) : 0;
+      const int g = max(__builtin_amdgcn_readlane(gsel, src), 0);
+      const unsigned r1 = __builtin_amdgcn_readlane(rin, src);
+      const int j = (g << 6) + lane;
+      const unsigned key = __float_as_uint(xload(&a.sabs[min(j, n - 1)]));
+      const uint64_t me = __ballot(j < n && key == T);
+      const unsigned rank = __builtin_amdgcn_mbcnt_hi((unsigned)(me >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((unsigned)me, 0u));
+      const uint64_t hit = __ballot(((me >> lane) & 1ull) && rank + 1u == r1);
+      J = (who && hit) ? (g << 6) + (int)__builtin_ctzll(hit) : n - 1;
+    }
+    if (lane == 0) {
+      xstore_u(&a.sync[kSyncSelect + 1], T);
+      xstore_u(&a.sync[kSyncSelect + 2], (unsigned)J);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -487,11 +515,11 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
 }
 
 // ---------------------------------------------------------------------------
-// P3: Stage 2a for 8 list positions (one per wave): exact up/gate rows of the
-// selected channel (contiguous 2*d_model elements), dot2 with x, s = u *
-// SiLU(g) (Sec. 4.1, Stage 2 equations).
+// P3: Stage 2a for 32 consecutive channels (Sec. 4.1, Stage 2 equations):
+// for each kept channel, its exact up/gate rows (contiguous 2*d_model
+// elements), dot2 with x, s = u * SiLU(g), stored by channel.  The kept
+// channels are dealt to the 8 waves in ascending order.
 // ---------------------------------------------------------------------------
-// CH 16-byte steps of both rows (and of x) in flight, then their dot products.
 template <bool BF16, int CH>
 __device__ __forceinline__ void p3_pass(const FusedArgs &a, __amdgpu_buffer_rsrc_t rs, uint32_t ubase,
                                         uint32_t rowb, int m0, int lane, float &au, float &ag) {
@@ -513,37 +541,63 @@ __device__ __forceinline__ void p3_pass(const FusedArgs &a, __amdgpu_buffer_rsrc
 }
 
 template <bool BF16>
-__device__ void p3_item(const FusedArgs &a, int item) {
+__device__ __forceinline__ void p3_channel(const FusedArgs &a, int j, int lane) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
+  const uint32_t rowb = (uint32_t)a.d_model * ESZ;
+  const uint32_t ubase = (uint32_t)j * 2u * rowb;
+  // One 16-byte step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a
+  // multiple of 1024, so the steps tile the row exactly.  4 steps per pass:
+  // 8 KB in flight per wave at ~110 VGPRs (8 would spill with x in registers).
+  const int nstep = (int)(rowb >> 10);
+  float au = 0.0f, ag = 0.0f;
+  int m0 = 0;
+  for (; m0 + 4 <= nstep; m0 += 4) p3_pass<BF16, 4>(a, rs, ubase, rowb, m0, lane, au, ag);
+  if (m0 + 2 <= nstep) {
+    p3_pass<BF16, 2>(a, rs, ubase, rowb, m0, lane, au, ag);
+    m0 += 2;
+  }
+  if (m0 < nstep) p3_pass<BF16, 1>(a, rs, ubase, rowb, m0, lane, au, ag);
+  const float u = wave_sum(au);
+  const float g = wave_sum(ag);
+  if (lane == 0) xstore(&a.sdense[j], u * silu(g));
+}
+
+// The i-th set bit (0-based) of a wave-uniform mask, found by all lanes.
+__device__ __forceinline__ int nth_bit(uint64_t m, int i, int lane) {
+  const unsigned r = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+  const uint64_t hit = __ballot(((m >> lane) & 1ull) && r == (unsigned)i);
+  return (int)__builtin_ctzll(hit);
+}
+
+template <bool BF16>
+__device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   if (threadIdx.x == 0) {
-    wait_geq(&a.sync[kSyncSelect], 1u, &a.sync[kSyncErr]);
+    wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
+    sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
     stamp_wait(a);
   }
   __syncthreads();
-  constexpr int ESZ = BF16 ? 2 : 4;
+  const unsigned bstar = sm.bstar;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p = item * kFW + wv;
-  if (p < a.k) {
-    const int j = (int)__builtin_amdgcn_readfirstlane((int)xload_u((const unsigned *)&a.sel[p]));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
-    const uint32_t rowb = (uint32_t)a.d_model * ESZ;
-    const uint32_t ubase = (uint32_t)j * 2u * rowb;
-    // One 16-byte step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a
-    // multiple of 1024, so the steps tile the row exactly.
-    const int nstep = (int)(rowb >> 10);
-    float au = 0.0f, ag = 0.0f;
-    int m0 = 0;
-    // 4 steps per pass: 8 KB in flight per wave at ~110 VGPRs (8 steps
-    // would spill with x held in registers).
-    for (; m0 + 4 <= nstep; m0 += 4) p3_pass<BF16, 4>(a, rs, ubase, rowb, m0, lane, au, ag);
-    if (m0 + 2 <= nstep) {
-      p3_pass<BF16, 2>(a, rs, ubase, rowb, m0, lane, au, ag);
-      m0 += 2;
-    }
-    if (m0 < nstep) p3_pass<BF16, 1>(a, rs, ubase, rowb, m0, lane, au, ag);
-    const float u = wave_sum(au);
-    const float g = wave_sum(ag);
-    if (lane == 0) xstore(&a.ssp[p], u * silu(g));
+  const int n = a.d_ff;
+  const int c0 = item * kP3Ch;
+  const int j = c0 + lane;
+  const bool valid = lane < kP3Ch && j < n;
+  const unsigned d1 = __float_as_uint(xload(&a.sabs[min(j, n - 1)])) >> 20;
+  const uint64_t dm = __ballot(valid && d1 > bstar);   // selected whatever T is
+  const uint64_t bm = __ballot(valid && d1 == bstar);  // decided later by T and J
+  // s of both sets: the bin-b* channels are computed before T is known
+  // (about twice the kept ones, a few percent of the step's bytes) so that
+  // nothing here waits for the select.
+  const uint64_t cm = dm | bm;
+  const int nc = (int)__popcll(cm);
+  for (int i = wv; i < nc; i += kFW) p3_channel<BF16>(a, c0 + nth_bit(cm, i, lane), lane);
+  if (threadIdx.x == 0) {
+    xstore_u(&a.gmask[2 * item], (unsigned)dm);
+    xstore_u(&a.gmask[2 * item + 1], (unsigned)bm);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -551,108 +605,124 @@ __device__ void p3_item(const FusedArgs &a, int item) {
 }
 
 // ---------------------------------------------------------------------------
-// P4: Stage 2b for one (256-column chunk, 128 list positions) item (Sec. 4.1,
-// Stage 2 equations; Sec. 3.1 weighted-sum view): partial y over the item's
-// positions; the last item of a column chunk sums the partials in a fixed
-// order.
+// P4: Stage 2b for one (range of 512 channels, 256-column chunk) item (Sec.
+// 4.1, Stage 2 equations; Sec. 3.1 weighted-sum view): the range's kept
+// channels, ascending, each scaled by its s; the last item of a column chunk
+// adds the range partials in range order.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
-  constexpr int U = kP4Rows / kFW;
+  constexpr int U = 16;  // rows per wave per batch
   constexpr int ESZ = BF16 ? 2 : 4;
-  const int rc = item / a.ncol, cc = item % a.ncol;
-  const int p0 = rc * kP4Rows;
-  const int p1 = min(a.k, p0 + kP4Rows);
-  const int lane = threadIdx.x & 63;
-  // Wait for the P3 items of positions [p0, p1): one flag per lane of wave 0.
-  if (threadIdx.x < 64) {
-    const int q0 = p0 / kFW, q1 = (p1 - 1) / kFW;  // at most kP4Rows / 8 = 16 flags
-    const int q = q0 + lane;
-    const unsigned *f = &a.sync[kSyncP3 + min(q, q1) * kSyncStride];
-    unsigned n = 0;
-    while (!__all(xload_u(f) >= 1u)) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++n > (1u << 22)) {
-        if (lane == 0) atomicOr(&a.sync[kSyncErr], 1u);
-        break;
-      }
-    }
+  constexpr int QPR = kP4Ch / kP3Ch;  // P3 items per range
+  const int r = item / a.ncol, cc = item % a.ncol;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q0 = r * QPR;
+  const int q1 = min(a.n_p3, q0 + QPR) - 1;
+  if (tid < 64) {
+    // lanes 0..15: the range's P3 items; the others: the select (T and J)
+    const unsigned *f = lane < QPR ? &a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride]
+                                   : &a.sync[kSyncSelect];
+    wave_wait_flags(f, &a.sync[kSyncErr]);
     if (lane == 0) stamp_wait(a);
   }
   __syncthreads();
-  if (threadIdx.x < kP4Rows) {
-    const int pp = p0 + (int)threadIdx.x;
-    const int pc = pp < p1 ? pp : p0;
-    const unsigned j = xload_u((const unsigned *)&a.sel[pc]);
-    const float sv = xload(&a.ssp[pc]);
-    sm.rs[threadIdx.x] = (int)j;
-    sm.sv[threadIdx.x] = pp < p1 ? sv : 0.0f;
+  // Kept channels of the range -> LDS list (ascending), with their s.
+  {
+    const unsigned T = xload_u(&a.sync[kSyncSelect + 1]);
+    const int J = (int)xload_u(&a.sync[kSyncSelect + 2]);
+    const int ch = r * kP4Ch + tid;
+    const int q = min(q0 + tid / kP3Ch, q1);
+    const unsigned dmq = xload_u(&a.gmask[2 * q]), bmq = xload_u(&a.gmask[2 * q + 1]);
+    const unsigned key = __float_as_uint(xload(&a.sabs[min(ch, a.d_ff - 1)]));
+    const unsigned bit = 1u << (tid % kP3Ch);
+    const bool kept = ch < a.d_ff &&
+                      ((dmq & bit) || ((bmq & bit) && (key > T || (key == T && ch <= J))));
+    const float s = xload(&a.sdense[min(ch, a.d_ff - 1)]);
+    const uint64_t bw = __ballot(kept);
+    if (lane == 0) sm.wcnt[wv] = (unsigned)__popcll(bw);
+    __syncthreads();
+    unsigned off = 0;
+#pragma unroll
+    for (int i = 0; i < kFW; ++i) off += i < wv ? sm.wcnt[i] : 0u;
+    if (kept) {
+      const unsigned pos = off + __builtin_amdgcn_mbcnt_hi((unsigned)(bw >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((unsigned)bw, 0u));
+      sm.rs[pos] = ch;
+      sm.sv[pos] = s;
+    }
   }
   __syncthreads();
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int nr = 0;
+#pragma unroll
+  for (int i = 0; i < kFW; ++i) nr += (int)sm.wcnt[i];
   const size_t chunk_bytes = (size_t)a.d_ff * kDownCols * ESZ;
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc((const char *)a.wd + cc * chunk_bytes, (uint32_t)chunk_bytes);
   const uint32_t voff = (uint32_t)lane * 4u * ESZ;
   using WT = typename std::conditional<BF16, u2, u4>::type;
-  WT wr[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int r = wv + kFW * u;
-    const uint32_t rowoff = (uint32_t)__builtin_amdgcn_readfirstlane(sm.rs[r]) * (uint32_t)(kDownCols * ESZ);
-    if constexpr (BF16)
-      wr[u] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, rowoff, kNT);
-    else
-      wr[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, kNT);
-  }
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b0 = 0; b0 < nr; b0 += kFW * U) {
+    WT wr[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const float sv = sm.sv[wv + kFW * u];
-    float wf[4];
-    if constexpr (BF16) {
-      wf[0] = bf16_to_f32(wr[u].x & 0xffffu);
-      wf[1] = bf16_to_f32(wr[u].x >> 16);
-      wf[2] = bf16_to_f32(wr[u].y & 0xffffu);
-      wf[3] = bf16_to_f32(wr[u].y >> 16);
-    } else {
-      wf[0] = __uint_as_float(wr[u].x);
-      wf[1] = __uint_as_float(wr[u].y);
-      wf[2] = __uint_as_float(wr[u].z);
-      wf[3] = __uint_as_float(wr[u].w);
+    for (int u = 0; u < U; ++u) {
+      const int rr = min(b0 + wv + kFW * u, nr - 1);
+      const uint32_t rowoff =
+          (uint32_t)__builtin_amdgcn_readfirstlane(sm.rs[rr]) * (uint32_t)(kDownCols * ESZ);
+      if constexpr (BF16)
+        wr[u] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, rowoff, kNT);
+      else
+        wr[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, kNT);
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = fmaf(sv, wf[c], acc[c]);
+    for (int u = 0; u < U; ++u) {
+      const int rr = b0 + wv + kFW * u;
+      const float sv = rr < nr ? sm.sv[rr] : 0.0f;
+      float wf[4];
+      if constexpr (BF16) {
+        wf[0] = bf16_to_f32(wr[u].x & 0xffffu);
+        wf[1] = bf16_to_f32(wr[u].x >> 16);
+        wf[2] = bf16_to_f32(wr[u].y & 0xffffu);
+        wf[3] = bf16_to_f32(wr[u].y >> 16);
+      } else {
+        wf[0] = __uint_as_float(wr[u].x);
+        wf[1] = __uint_as_float(wr[u].y);
+        wf[2] = __uint_as_float(wr[u].z);
+        wf[3] = __uint_as_float(wr[u].w);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = fmaf(sv, wf[c], acc[c]);
+    }
   }
   *(float4 *)&sm.red[wv][lane * 4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   __syncthreads();
-  if (threadIdx.x < kDownCols) {
-    const int c = threadIdx.x;
+  if (tid < kDownCols) {
+    const int c = tid;
     float v = sm.red[0][c];
 #pragma unroll
     for (int q = 1; q < kFW; ++q) v += sm.red[q][c];
-    xstore(&a.ypart[(size_t)rc * a.d_model + cc * kDownCols + c], v);
+    xstore(&a.ypart[(size_t)r * a.d_model + cc * kDownCols + c], v);
   }
-  if (!arrive_last(&a.col_cnt[cc], (unsigned)a.nrc, s_flag)) return;
-  // Sum of the nrc partials of the chunk: wave q adds rows q, q + 8, ... of
-  // 4 columns per lane (agent-coherent 16-byte loads), then the 8 wave sums
-  // are added in wave order.
+  if (!arrive_last(&a.col_cnt[cc], (unsigned)a.nrange, s_flag)) return;
+  // Sum of the range partials of the chunk: wave q adds ranges q, q + 8, ...
+  // of 4 columns per lane (agent-coherent 16-byte loads), then the 8 wave
+  // sums are added in wave order.
   {
-    const int q = wv;
     const __amdgpu_buffer_rsrc_t yr =
-        make_rsrc(a.ypart, (uint32_t)((size_t)a.nrc * a.d_model * sizeof(float)));
+        make_rsrc(a.ypart, (uint32_t)((size_t)a.nrange * a.d_model * sizeof(float)));
     const uint32_t coff = (uint32_t)(cc * kDownCols + lane * 4) * 4u;
     float4 s4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int r0 = q; r0 < a.nrc; r0 += kFW * 8) {
+    for (int r0 = wv; r0 < a.nrange; r0 += kFW * 8) {
       u4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int r = min(r0 + kFW * u, a.nrc - 1);
-        v[u] = __builtin_amdgcn_raw_buffer_load_b128(yr, coff, (uint32_t)r * a.d_model * 4u, kSelBits);
+        const int rr = min(r0 + kFW * u, a.nrange - 1);
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(yr, coff, (uint32_t)rr * a.d_model * 4u, kSelBits);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (r0 + kFW * u < a.nrc) {
+        if (r0 + kFW * u < a.nrange) {
           s4.x += __uint_as_float(v[u].x);
           s4.y += __uint_as_float(v[u].y);
           s4.z += __uint_as_float(v[u].z);
@@ -661,11 +731,11 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
       }
     }
     __syncthreads();  // every wave is done with red
-    *(float4 *)&sm.red[q][lane * 4] = s4;
+    *(float4 *)&sm.red[wv][lane * 4] = s4;
   }
   __syncthreads();
-  if (threadIdx.x < kDownCols) {
-    const int c = threadIdx.x;
+  if (tid < kDownCols) {
+    const int c = tid;
     float v = sm.red[0][c];
 #pragma unroll
     for (int q = 1; q < kFW; ++q) v += sm.red[q][c];
@@ -684,6 +754,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   __shared__ union {
     P1Smem p1;
     P2Smem p2;
+    P3Smem p3;
     P4Smem p4;
   } sm;
   __shared__ int s_ticket, s_flag;
@@ -701,14 +772,19 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       t0 = __builtin_amdgcn_s_memrealtime();
       g_twait = t0;
     }
+    int phase;
     int r = t;
     if (r < a.n_p1) {
+      phase = 1;
       p1_item<BF16>(a, r, sm.p1, &s_flag);
     } else if ((r -= a.n_p1) == 0) {
+      phase = 2;
       p2_select(a, sm.p2);
     } else if ((r -= 1) < a.n_p3) {
-      p3_item<BF16>(a, r);
+      phase = 3;
+      p3_item<BF16>(a, r, sm.p3);
     } else {
+      phase = 4;
       p4_item<BF16>(a, r - a.n_p3, sm.p4, &s_flag);
     }
     if (a.trace && threadIdx.x == 0) {
@@ -716,21 +792,68 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       e[0] = t0;
       e[1] = g_twait;
       e[2] = __builtin_amdgcn_s_memrealtime();
-      e[3] = blockIdx.x;
+      e[3] = (unsigned long long)blockIdx.x | ((unsigned long long)phase << 32);
     }
   }
-  // The last work-group out clears the ticket and flags for the next launch.
+  // The last work-group out clears the ticket, flags and histogram for the
+  // next launch.
   __syncthreads();
   if (threadIdx.x == 0)
     s_flag = __hip_atomic_fetch_add(&a.sync[kSyncExit], 1u, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
   __syncthreads();
   if (s_flag) {
-    for (int i = threadIdx.x; i < 5 + a.n_p3; i += kFT) {
-      const int w = i < 5 ? i * kSyncStride : kSyncP3 + (i - 5) * kSyncStride;
+    constexpr int kCtl = kSyncP3 / kSyncStride;  // control words before the P3 flags
+    for (int i = threadIdx.x; i < kCtl + a.n_p3; i += kFT) {
+      const int w = i < kCtl ? i * kSyncStride : kSyncP3 + (i - kCtl) * kSyncStride;
       if (w != kSyncErr) xstore_u(&a.sync[w], 0u);
     }
     for (int i = threadIdx.x; i < 2048; i += kFT) xstore_u(&a.ghist[i], 0u);
+  }
+}
+
+// The ascending list of kept channels and their s, from the P3 masks, the
+// keys and T, J (for inspection only; the forward itself never builds it).
+// One work-group.
+__global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, const unsigned *tj,
+                                                         const float *sabs, const float *sdense,
+                                                         int n_p3, int d_ff, int k, int *sel,
+                                                         float *ssel) {
+  __shared__ unsigned wsum[kFW];
+  __shared__ unsigned base;
+  if (threadIdx.x == 0) base = 0u;
+  __syncthreads();
+  const unsigned T = tj[1];
+  const int J = (int)tj[2];
+  for (int q0 = 0; q0 < n_p3; q0 += kFT) {
+    const int q = q0 + (int)threadIdx.x;
+    unsigned m = 0u;
+    if (q < n_p3) {
+      m = gmask[2 * q];
+      unsigned bm = gmask[2 * q + 1];
+      while (bm) {
+        const int b = __builtin_ctz(bm);
+        bm &= bm - 1u;
+        const int ch = q * kP3Ch + b;
+        const unsigned key = __float_as_uint(sabs[ch]);
+        if (key > T || (key == T && ch <= J)) m |= 1u << b;
+      }
+    }
+    unsigned tot;
+    unsigned pos = base + block_excl_scan<kFW>((unsigned)__popc(m), wsum, tot);
+    while (m) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1u;
+      const int ch = q * kP3Ch + b;
+      if (pos < (unsigned)k && ch < d_ff) {
+        sel[pos] = ch;
+        if (ssel) ssel[pos] = sdense[ch];
+      }
+      ++pos;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) base += tot;
+    __syncthreads();
   }
 }
 
@@ -762,18 +885,23 @@ bool fused_supported(const Plan &p) {
   return (p.d_ff + kFT - 1) / kFT <= kMaxPer && ((size_t)p.d_model * p.esz) % 1024 == 0;
 }
 
-// Sync block: control words, P3 flags, then the digit-1 histogram.
+static int fused_n_p3(const Plan &p) { return (p.d_ff + kP3Ch - 1) / kP3Ch; }
+
+// Sync block: control words, P3 flags, the digit-1 histogram, the P3 masks.
 static size_t fused_hist_word(const Plan &p) {
-  return (size_t)kSyncP3 + (size_t)((p.d_ff + kFW - 1) / kFW) * kSyncStride;
+  return (size_t)kSyncP3 + (size_t)fused_n_p3(p) * kSyncStride;
 }
 
-size_t fused_sync_words(const Plan &p) { return fused_hist_word(p) + 2048; }
+size_t fused_sync_words(const Plan &p) { return fused_hist_word(p) + 2048 + 2 * fused_n_p3(p); }
 
-int fused_ypart_rows(const Plan &p) { return (p.d_ff + kP4Rows - 1) / kP4Rows; }
+int fused_ypart_rows(const Plan &p) { return (p.d_ff + kP4Ch - 1) / kP4Ch; }
 
 int fused_items(const Plan &p, int k) {
-  return p.ntile * p.nchunk + 1 + (k + kFW - 1) / kFW + p.ncol * ((k + kP4Rows - 1) / kP4Rows);
+  (void)k;
+  return p.ntile * p.nchunk + 1 + fused_n_p3(p) + p.ncol * fused_ypart_rows(p);
 }
+
+int fused_p3_items(const Plan &p) { return fused_n_p3(p); }
 
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
                         float *resid, hipStream_t s, unsigned long long *trace) {
@@ -791,7 +919,7 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.ntile = p.ntile;
   a.nchunk = p.nchunk;
   a.ncol = p.ncol;
-  a.nrc = (k + kP4Rows - 1) / kP4Rows;
+  a.nrange = fused_ypart_rows(p);
   a.x = x;
   a.tau = tau;
   a.k = k;
@@ -800,16 +928,24 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.part = b.part;
   a.tile_cnt = b.tile_cnt;
   a.sabs = b.sabs;
-  a.sel = b.sel;
-  a.ssp = b.ssp;
+  a.sdense = b.ssp;
   a.ypart = b.ypart;
   a.col_cnt = b.col_cnt;
   a.sync = b.sync;
   a.ghist = b.sync + fused_hist_word(p);
+  a.gmask = a.ghist + 2048;
   a.n_p1 = p.ntile * p.nchunk;
-  a.n_p3 = (k + kFW - 1) / kFW;
-  a.n_p4 = p.ncol * a.nrc;
+  a.n_p3 = fused_n_p3(p);
+  a.n_p4 = p.ncol * a.nrange;
   return p.bf16 ? fused_go<true>(a, s) : fused_go<false>(a, s);
+}
+
+hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,
+                             hipStream_t s) {
+  const unsigned *gmask = b.sync + fused_hist_word(p) + 2048;
+  fused_list_kernel<<<1, kFT, 0, s>>>(gmask, b.sync + kSyncSelect, b.sabs, b.ssp, fused_n_p3(p),
+                                      p.d_ff, k, sel, ssel);
+  return hipGetLastError();
 }
 
 }  // namespace prox

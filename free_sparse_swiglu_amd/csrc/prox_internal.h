@@ -100,6 +100,11 @@ int fused_ypart_rows(const Plan &p);  // partial-y rows the fused kernel needs
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
                         float *resid, hipStream_t s, unsigned long long *trace = nullptr);
 int fused_items(const Plan &p, int k);
+int fused_p3_items(const Plan &p);
+// After a fused forward: the ascending kept-channel list and its exact s
+// (k entries each; ssel may be null).
+hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,
+                             hipStream_t s);
 // Words between two control words of the fused kernel (one 256-byte line each).
 #ifndef PROX_SYNC_STRIDE
 #define PROX_SYNC_STRIDE 64

@@ -281,8 +281,9 @@ def prox_ffn_forward_traced(layer: Layer, x, threshold: float, k: int, y=None):
     """Batch-1 forward on the persistent kernel with its per-ticket timeline.
 
     Returns (y, trace, counts): trace is an int64 tensor [tickets][4] of
-    (start, wait end, end, work-group), times in 100 MHz clock ticks; counts
-    gives the tickets of each phase (Stage 1, select, up/gate, down)."""
+    (start, wait end, end, work-group | phase << 32), times in 100 MHz clock
+    ticks, phase 1..4 = Stage 1, select, up/gate, down; counts gives the
+    tickets of each phase."""
     y = _out_like(x, y)
     counts = (ctypes.c_int * 4)()
     lib = load_library()

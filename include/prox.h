@@ -192,7 +192,9 @@ prox_status prox_dense_ffn_forward_profiled(const prox_layer *layer,
  * items; their sum is the ticket count.  With trace == NULL only counts are
  * written.  Otherwise trace (device, [trace_items >= tickets][4] u64) receives
  * per ticket: start, end of its wait for earlier items, end (ticks of the
- * 100 MHz GPU real-time clock) and the work-group that ran it.  y is the
+ * 100 MHz GPU real-time clock) and the work-group that ran it in the low 32
+ * bits of the 4th word, its phase (1..4: Stage 1, select, up/gate, down) in
+ * the high 32 bits.  y is the
  * same as prox_ffn_forward's.  PROX_EUNSUPPORTED when the layer runs the
  * multi-kernel path (PROX_PATH=multi at prepare time).                       */
 prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x,
