@@ -23,11 +23,13 @@
 // The selection of channel j is: |s~_j| > T, or |s~_j| = T and j <= J (the
 // lowest-index channels win ties), which keeps exactly k channels.
 //
-// Work-groups take items from a global ticket counter in exactly that order.
-// An item only ever waits for items with smaller tickets (P2 for all of P1,
-// P3 for P2, P4 for P2 and the P3 items of its range); those were handed to running
-// work-groups before it, and P1 items wait for nothing, so the schedule
-// cannot deadlock whatever the residency.  Every wait is bounded.  Data
+// Items are numbered (tickets) in exactly that order.  The grid never exceeds
+// the number of work-groups the GPU holds at once, so every work-group is
+// resident; work-group b starts on ticket b (a Stage 1 item) and then takes
+// tickets from a global counter.  An item only ever waits for items with
+// smaller tickets (P2 for all of P1, P3 for P2, P4 for P2 and the P3 items
+// of its range); those are held by running work-groups, and P1 items wait
+// for nothing, so the schedule cannot deadlock.  Every wait is bounded.  Data
 // passed between work-groups goes through agent-coherent accesses
 // (xstore/xload, sc1 buffer loads); the last work-group to leave resets the
 // ticket, the flags and the histogram for the next launch.
@@ -128,9 +130,11 @@ struct P3Smem {
 };
 struct P4Smem {
   float red[kFW][kDownCols];
-  int rs[kP4Ch];
-  float sv[kP4Ch];
+  int rs[kP4Ch];       // listed channels
+  unsigned rk[kP4Ch];  // their keys
+  float sv[kP4Ch];     // their s (0 when below the cut)
   unsigned wcnt[kFW];
+  unsigned bstar;
 };
 
 // ---------------------------------------------------------------------------
@@ -608,49 +612,42 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
 // P4: Stage 2b for one (range of 512 channels, 256-column chunk) item (Sec.
 // 4.1, Stage 2 equations; Sec. 3.1 weighted-sum view): the range's kept
 // channels, ascending, each scaled by its s; the last item of a column chunk
-// adds the range partials in range order.
+// adds the range partials in range order.  The rows of every channel that
+// may be kept (digit 1 >= b*) start loading before the range's P3 items and
+// the select are done; a bin-b* channel below the cut gets s = 0.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
-  constexpr int U = 16;  // rows per wave per batch
+  constexpr int U = BF16 ? 16 : 8;  // rows per wave per batch
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int QPR = kP4Ch / kP3Ch;  // P3 items per range
+  static_assert(QPR < 64, "one wave polls the range's P3 flags and the select flag");
   const int r = item / a.ncol, cc = item % a.ncol;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q0 = r * QPR;
-  const int q1 = min(a.n_p3, q0 + QPR) - 1;
-  if (tid < 64) {
-    // lanes 0..15: the range's P3 items; the others: the select (T and J)
-    const unsigned *f = lane < QPR ? &a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride]
-                                   : &a.sync[kSyncSelect];
-    wave_wait_flags(f, &a.sync[kSyncErr]);
-    if (lane == 0) stamp_wait(a);
+  const int n = a.d_ff;
+  // 1. b*, then the range's channels with digit 1 >= b* (the kept ones and
+  // the bin-b* ones that may drop), ascending, with their keys.
+  if (tid == 0) {
+    wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
+    sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
   }
   __syncthreads();
-  // Kept channels of the range -> LDS list (ascending), with their s.
   {
-    const unsigned T = xload_u(&a.sync[kSyncSelect + 1]);
-    const int J = (int)xload_u(&a.sync[kSyncSelect + 2]);
     const int ch = r * kP4Ch + tid;
-    const int q = min(q0 + tid / kP3Ch, q1);
-    const unsigned dmq = xload_u(&a.gmask[2 * q]), bmq = xload_u(&a.gmask[2 * q + 1]);
-    const unsigned key = __float_as_uint(xload(&a.sabs[min(ch, a.d_ff - 1)]));
-    const unsigned bit = 1u << (tid % kP3Ch);
-    const bool kept = ch < a.d_ff &&
-                      ((dmq & bit) || ((bmq & bit) && (key > T || (key == T && ch <= J))));
-    const float s = xload(&a.sdense[min(ch, a.d_ff - 1)]);
-    const uint64_t bw = __ballot(kept);
+    const unsigned key = __float_as_uint(xload(&a.sabs[min(ch, n - 1)]));
+    const bool cand = ch < n && (key >> 20) >= sm.bstar;
+    const uint64_t bw = __ballot(cand);
     if (lane == 0) sm.wcnt[wv] = (unsigned)__popcll(bw);
     __syncthreads();
     unsigned off = 0;
 #pragma unroll
     for (int i = 0; i < kFW; ++i) off += i < wv ? sm.wcnt[i] : 0u;
-    if (kept) {
+    if (cand) {
       const unsigned pos = off + __builtin_amdgcn_mbcnt_hi((unsigned)(bw >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((unsigned)bw, 0u));
       sm.rs[pos] = ch;
-      sm.sv[pos] = s;
+      sm.rk[pos] = key;
     }
   }
   __syncthreads();
@@ -662,9 +659,8 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
       make_rsrc((const char *)a.wd + cc * chunk_bytes, (uint32_t)chunk_bytes);
   const uint32_t voff = (uint32_t)lane * 4u * ESZ;
   using WT = typename std::conditional<BF16, u2, u4>::type;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int b0 = 0; b0 < nr; b0 += kFW * U) {
-    WT wr[U];
+  WT wr[U];
+  auto load_batch = [&](int b0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rr = min(b0 + wv + kFW * u, nr - 1);
@@ -675,6 +671,34 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
       else
         wr[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, kNT);
     }
+  };
+  // 2. the first rows stream in while the range's P3 items and the select
+  // finish.
+  if (nr > 0) load_batch(0);
+  if (tid < 64) {
+    // lanes 0..QPR-1: the range's P3 items; the others: the select (T, J)
+    const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
+    const unsigned *f = lane < QPR ? &a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride]
+                                   : &a.sync[kSyncSelect];
+    wave_wait_flags(f, &a.sync[kSyncErr]);
+    if (lane == 0) stamp_wait(a);
+  }
+  __syncthreads();
+  // 3. s of each listed channel, 0 for a bin-b* channel below the cut.
+  {
+    const unsigned T = xload_u(&a.sync[kSyncSelect + 1]);
+    const int J = (int)xload_u(&a.sync[kSyncSelect + 2]);
+    if (tid < nr) {
+      const int ch = sm.rs[tid];
+      const unsigned key = sm.rk[tid];
+      const float s = xload(&a.sdense[ch]);
+      sm.sv[tid] = (key > T || (key == T && ch <= J)) ? s : 0.0f;
+    }
+  }
+  __syncthreads();
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b0 = 0; b0 < nr; b0 += kFW * U) {
+    if (b0 > 0) load_batch(b0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rr = b0 + wv + kFW * u;
@@ -759,11 +783,19 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   } sm;
   __shared__ int s_ticket, s_flag;
   const int total = a.n_p1 + 1 + a.n_p3 + a.n_p4;
+  // The first min(grid, n_p1) tickets are the work-groups' own indices (all
+  // work-groups of the grid are resident at once, see the launcher), which
+  // spares the launch burst on the ticket counter; the rest come from it.
+  const int nfirst = min((int)gridDim.x, a.n_p1);
+  bool first = (int)blockIdx.x < nfirst;
   for (;;) {
     __syncthreads();  // the previous item is done with the LDS
     if (threadIdx.x == 0)
-      s_ticket = (int)__hip_atomic_fetch_add(&a.sync[kSyncTicket], 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+      s_ticket = first ? (int)blockIdx.x
+                       : nfirst + (int)__hip_atomic_fetch_add(&a.sync[kSyncTicket], 1u,
+                                                              __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT);
+    first = false;
     __syncthreads();
     const int t = s_ticket;
     if (t >= total) break;
