@@ -11,9 +11,11 @@ cannot serve a repeated layer: the bytes come from HBM.
 
 Printed: one JSON line.  value = achieved GB/s on the algorithmic bytes of a
 step (weights actually needed, x, y) over the measured step time; also
-microseconds per layer, the per-kernel breakdown (HIP events recorded by the
-library between its kernels, on the launch stream), the dense bf16 baseline on
-the same relaid weights, and the CPU oracle timed on the host cores.
+microseconds per layer, the duration of the step's one persistent kernel (HIP
+events recorded by the library around it, on the launch stream), the same
+step on the multi-kernel path with its per-kernel breakdown, the dense bf16
+baseline on the same relaid weights, and the CPU oracle timed on the host
+cores.
 
 Other workloads (--workload): 14b (k at 70%), 70b (batch 1/2/4/8), stack8b
 (32 layers x 128 sequential tokens, tokens/s), copy (a plain device copy of
@@ -32,12 +34,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-KERNEL_NAMES = ["stage1_proxy", "topk", "stage2_upgate", "stage2_down"]
+KERNEL_NAMES = ["stage1_proxy", "topk", "stage2_upgate", "stage2_down"]  # multi-kernel path
+FUSED_KERNEL = "ffn_fused_kernel"
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("prox_kernels.hip", "prox_api.hip", "prox_internal.h"):
+    for f in ("prox_kernels.hip", "prox_fused.hip", "prox_api.hip", "prox_internal.h",
+              "prox_device.h"):
         with open(os.path.join(ROOT, "free_sparse_swiglu_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -72,12 +76,17 @@ def algorithmic_bytes(cfg, n1, groups_touched, k, batch=1, union=None):
                 total=stage1 + upgate + down + io)
 
 
-def build_ring(cfg, ring, max_batch=1):
+def build_ring(cfg, ring, max_batch=1, path=None):
+    """Prepare `ring` seeded layers sharing one workspace.  path="multi"
+    prepares them for the multi-kernel path (one kernel per phase)."""
     import torch
 
     from free_sparse_swiglu_amd import prox, synth
     layers, taus = [], []
     ws = None
+    old = os.environ.get("PROX_PATH")
+    if path:
+        os.environ["PROX_PATH"] = path
     for l in range(ring):
         W = synth.make_layer(cfg, l, "cuda")
         L = prox.prox_prepare_layer(*W, cfg.group, max_batch, workspace=ws)
@@ -86,6 +95,11 @@ def build_ring(cfg, ring, max_batch=1):
         del W
         layers.append(L)
         taus.append(synth.layer_tau(cfg, l, "cuda"))
+    if path:
+        if old is None:
+            os.environ.pop("PROX_PATH", None)
+        else:
+            os.environ["PROX_PATH"] = old
     return layers, taus
 
 
@@ -226,20 +240,41 @@ def bench_single_layer(args, name):
                                                   GBps=round(ob / (oms * 1e-3) / 1e9, 1),
                                                   speedup_vs_dense=round(dms / oms, 3))
 
-    kern = {}
+    # The same step on the multi-kernel path (one kernel per phase), for the
+    # per-phase breakdown.
+    mlayers, _ = build_ring(cfg, R, path="multi")
+
+    def mstep(i):
+        l = i % R
+        prox.prox_ffn_forward(mlayers[l], X[l][(i // R) % NX], taus[l], k, y)
+    mms = time_loop(mstep, args.steps, args.warmup)
+
+    def mpstep(i, evs):
+        l = i % R
+        return prox.prox_ffn_forward_profiled(mlayers[l], X[l][(i // R) % NX][None], taus[l], k,
+                                              evs, y[None])[1]
+    mkms = profile_kernels(mpstep, min(args.steps, 200), 6)
+    del mlayers
+    torch.cuda.synchronize()
     kbytes = dict(stage1_proxy=ab["stage1"] + cfg.d_model * 2, topk=None,
                   stage2_upgate=ab["upgate"] + cfg.d_model * 2, stage2_down=ab["down"])
-    for nm, t in zip(KERNEL_NAMES, kms):
+    mkern = {}
+    for nm, t in zip(KERNEL_NAMES, mkms):
         b = kbytes.get(nm)
-        kern[nm] = dict(us=round(t * 1e3, 2),
-                        GBps=round(b / (t * 1e-3) / 1e9, 1) if b else None)
-    dom = "stage2_upgate"
+        mkern[nm] = dict(us=round(t * 1e3, 2),
+                         GBps=round(b / (t * 1e-3) / 1e9, 1) if b else None)
+
+    # The default path is one persistent kernel: the library records an
+    # event before and after it, so kms has one entry.
+    kern = {FUSED_KERNEL: dict(us=round(kms[0] * 1e3, 2),
+                               GBps=round(ab["total"] / (kms[0] * 1e-3) / 1e9, 1))}
+    dom = FUSED_KERNEL
     dom_us = kern[dom]["us"]
-    achieved = kbytes[dom] / (dom_us * 1e-6) / 1e9
+    achieved = ab["total"] / (dom_us * 1e-6) / 1e9
     traffic = load_traffic(name)
     roof = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
-                bytes_per_launch=int(kbytes[dom]),
+                bytes_per_launch=int(ab["total"]),
                 traffic=(traffic or {}).get("bytes_per_launch") if traffic else None)
 
     s1 = 1.0 - n1m / cfg.d_model
@@ -263,6 +298,7 @@ def bench_single_layer(args, name):
                     effective_sparsity=round(costmodel.effective_sparsity(s1, s2), 4),
                     bytes_per_step=int(ab["total"])),
         kernels=kern,
+        multi_kernel_path=dict(us_per_layer=round(mms * 1e3, 2), kernels=mkern),
         dense=dict(us_per_layer=round(dms * 1e3, 2),
                    GBps=round(3 * cfg.d_model * cfg.d_ff * 2 / (dms * 1e-3) / 1e9, 1),
                    kernels=dict(upgate_us=round(dkms[0] * 1e3, 2), down_us=round(dkms[1] * 1e3, 2))),

@@ -126,6 +126,7 @@ struct P2Smem {
   unsigned misc[8];
 };
 struct P3Smem {
+  u4 x[2048];  // x when d_model * element size <= 32 KB
   unsigned bstar;
 };
 struct P4Smem {
@@ -524,44 +525,60 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
 // elements), dot2 with x, s = u * SiLU(g), stored by channel.  The kept
 // channels are dealt to the 8 waves in ascending order.
 // ---------------------------------------------------------------------------
+// CH 16-byte steps of both rows in flight, then their dot products with x
+// (from LDS when xs is given, else from global memory).
 template <bool BF16, int CH>
-__device__ __forceinline__ void p3_pass(const FusedArgs &a, __amdgpu_buffer_rsrc_t rs, uint32_t ubase,
-                                        uint32_t rowb, int m0, int lane, float &au, float &ag) {
-  u4 wu[CH], wg[CH], xr[CH];
+__device__ __forceinline__ void p3_pass(const FusedArgs &a, const u4 *xs, __amdgpu_buffer_rsrc_t rs,
+                                        uint32_t ubase, uint32_t rowb, int m0, int lane, float &au,
+                                        float &ag) {
+  u4 wu[CH], wg[CH];
 #pragma unroll
   for (int m = 0; m < CH; ++m) {
     const uint32_t off = (uint32_t)((m0 + m) * 64 + lane) * 16u;
     wu[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase, kNT);
     wg[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase + rowb, kNT);
   }
+  if (xs) {
 #pragma unroll
-  for (int m = 0; m < CH; ++m) xr[m] = ((const u4 *)a.x)[(m0 + m) * 64 + lane];
-  __builtin_amdgcn_sched_barrier(0);
+    for (int m = 0; m < CH; ++m) {
+      const u4 xr = xs[(m0 + m) * 64 + lane];
+      au = dot16<BF16>(wu[m], xr, au);
+      ag = dot16<BF16>(wg[m], xr, ag);
+    }
+  } else {
+    u4 xr[CH];
 #pragma unroll
-  for (int m = 0; m < CH; ++m) {
-    au = dot16<BF16>(wu[m], xr[m], au);
-    ag = dot16<BF16>(wg[m], xr[m], ag);
+    for (int m = 0; m < CH; ++m) xr[m] = ((const u4 *)a.x)[(m0 + m) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < CH; ++m) {
+      au = dot16<BF16>(wu[m], xr[m], au);
+      ag = dot16<BF16>(wg[m], xr[m], ag);
+    }
   }
 }
 
 template <bool BF16>
-__device__ __forceinline__ void p3_channel(const FusedArgs &a, int j, int lane) {
+__device__ __forceinline__ void p3_channel(const FusedArgs &a, const u4 *xs, int j, int lane) {
   constexpr int ESZ = BF16 ? 2 : 4;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
   const uint32_t rowb = (uint32_t)a.d_model * ESZ;
   const uint32_t ubase = (uint32_t)j * 2u * rowb;
   // One 16-byte step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a
-  // multiple of 1024, so the steps tile the row exactly.  4 steps per pass:
-  // 8 KB in flight per wave at ~110 VGPRs (8 would spill with x in registers).
+  // multiple of 1024, so the steps tile the row exactly.  With x in LDS a
+  // pass holds 8 steps of both rows (16 KB per wave in flight); with x in
+  // registers 4 (8 would spill).
   const int nstep = (int)(rowb >> 10);
   float au = 0.0f, ag = 0.0f;
   int m0 = 0;
-  for (; m0 + 4 <= nstep; m0 += 4) p3_pass<BF16, 4>(a, rs, ubase, rowb, m0, lane, au, ag);
+  if (xs)
+    for (; m0 + 8 <= nstep; m0 += 8) p3_pass<BF16, 8>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
+  for (; m0 + 4 <= nstep; m0 += 4) p3_pass<BF16, 4>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
   if (m0 + 2 <= nstep) {
-    p3_pass<BF16, 2>(a, rs, ubase, rowb, m0, lane, au, ag);
+    p3_pass<BF16, 2>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
     m0 += 2;
   }
-  if (m0 < nstep) p3_pass<BF16, 1>(a, rs, ubase, rowb, m0, lane, au, ag);
+  if (m0 < nstep) p3_pass<BF16, 1>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
   const float u = wave_sum(au);
   const float g = wave_sum(ag);
   if (lane == 0) xstore(&a.sdense[j], u * silu(g));
@@ -598,7 +615,15 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   // nothing here waits for the select.
   const uint64_t cm = dm | bm;
   const int nc = (int)__popcll(cm);
-  for (int i = wv; i < nc; i += kFW) p3_channel<BF16>(a, c0 + nth_bit(cm, i, lane), lane);
+  // x to LDS when it fits (every item reads it, so it is L2-resident)
+  const uint32_t rowb = (uint32_t)a.d_model * (BF16 ? 2u : 4u);
+  const u4 *xs = nullptr;
+  if (rowb <= sizeof(sm.x)) {
+    for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) sm.x[i] = ((const u4 *)a.x)[i];
+    __syncthreads();
+    xs = sm.x;
+  }
+  for (int i = wv; i < nc; i += kFW) p3_channel<BF16>(a, xs, c0 + nth_bit(cm, i, lane), lane);
   if (threadIdx.x == 0) {
     xstore_u(&a.gmask[2 * item], (unsigned)dm);
     xstore_u(&a.gmask[2 * item + 1], (unsigned)bm);
