@@ -5,5 +5,6 @@ benchmark's CPU-baseline leg may import this package.  It is independent of
 the HIP library: the two share no code, and neither imports the other.
 """
 from .prox_oracle import (Layer, build, dense, dequantize, forward,  # noqa: F401
-                          forward_batch, input_mask, proxy, quantize,
-                          rmsnorm, round_bf16, stack_forward, stage2, topk)
+                          forward_batch, forward_ts, input_mask, proxy, quantize,
+                          rmsnorm, round_bf16, stack_forward, stage2, threshold_mask,
+                          topk)

@@ -155,6 +155,19 @@ int prox_oracle_topk(const double *z, int n, int k, int *sel) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Stage 2 threshold mask (Sec. 4.1, m_s equation): with a calibrated
+ * threshold tau_s the mask keeps channel j iff |s~_j| >= tau_s.  The GPU
+ * holds |s~| in float32, so the comparison is taken in float32 here too: the
+ * double |s~_j| is rounded to float32 first.  Writes the kept channels in
+ * ascending order to sel and returns their count.                          */
+int prox_oracle_threshold_mask(const double *z, int n, float tau, int *sel) {
+  int m = 0;
+  for (int j = 0; j < n; ++j)
+    if ((float)fabs(z[j]) >= tau) sel[m++] = j;
+  return m;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Stage 2 exact sparse computation (Sec. 4.1, Stage 2 equations):
  *   u_sp = Pi_out(x, W_up, m_s),  h_sp = SiLU(Pi_out(x, W_gate, m_s)),
  *   s_sp = u_sp . h_sp,           y = Pi_in(s_sp, W_down, m_s)

@@ -19,6 +19,8 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
                 are "parity unpinned".
   topk          brute-force rank definition; Laplace energy closed form
                 (App. A.2); popcount; ties to the lower index
+  threshold_mask  equals top-k when tau_s is the k-th largest value (no ties);
+                monotone in tau_s; Laplace energy closed form (App. A.2)
   stage2/dense  zero sparsity equals the dense FFN; brute force on tiny shapes
 """
 from __future__ import annotations
@@ -62,6 +64,8 @@ def _load():
         lib.prox_oracle_proxy.argtypes = [P, P, I, P, P, I, P, P, P]
         lib.prox_oracle_topk.argtypes = [P, I, I, P]
         lib.prox_oracle_topk.restype = I
+        lib.prox_oracle_threshold_mask.argtypes = [P, I, ctypes.c_float, P]
+        lib.prox_oracle_threshold_mask.restype = I
         lib.prox_oracle_stage2.argtypes = [P, I, I, P, P, P, P, I, P, P]
         lib.prox_oracle_dense.argtypes = [P, I, I, P, P, P, P, P]
         lib.prox_oracle_round_bf16.argtypes = [ctypes.c_float]
@@ -144,6 +148,15 @@ def topk(z, k: int) -> np.ndarray:
     return sel[:k].copy()
 
 
+def threshold_mask(z, tau_s: float) -> np.ndarray:
+    """Ascending channels with |z_j| >= tau_s, compared in float32 (Sec. 4.1,
+    m_s equation with the calibrated threshold tau_s)."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    sel = np.zeros(max(1, z.size), dtype=np.int32)
+    m = _load().prox_oracle_threshold_mask(_p(z), z.size, float(np.float32(tau_s)), _p(sel))
+    return sel[:m].copy()
+
+
 def stage2(x, W_up, W_gate, W_down, sel):
     """Exact Stage 2 over the selected channels (Sec. 4.1, Stage 2 equations).
 
@@ -219,6 +232,18 @@ def forward(layer: Layer, x, tau: float, k: int) -> dict:
     idx = input_mask(x, tau)
     u_t, g_t, s_t = proxy(x, idx, layer.Wt_up, layer.Wt_gate)
     sel = topk(s_t, k)
+    s_sp, y = stage2(x, layer.W_up, layer.W_gate, layer.W_down, sel)
+    return dict(idx=idx, u_t=u_t, g_t=g_t, s_t=s_t, sel=sel, s_sp=s_sp, y=y)
+
+
+def forward_ts(layer: Layer, x, tau_x: float, tau_s: float) -> dict:
+    """Prox FFN step with the calibrated Stage 2 threshold instead of top-k:
+    Stage 1 (input mask, proxy), the mask |s~| >= tau_s, then Stage 2 (Sec. 4.1).
+    Same dict as forward(); the number of kept channels is sel.size."""
+    x = _f32(x)
+    idx = input_mask(x, tau_x)
+    u_t, g_t, s_t = proxy(x, idx, layer.Wt_up, layer.Wt_gate)
+    sel = threshold_mask(s_t, tau_s)
     s_sp, y = stage2(x, layer.W_up, layer.W_gate, layer.W_down, sel)
     return dict(idx=idx, u_t=u_t, g_t=g_t, s_t=s_t, sel=sel, s_sp=s_sp, y=y)
 
