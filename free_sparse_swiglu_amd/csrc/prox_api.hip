@@ -359,8 +359,9 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
     if (batch == 1 && p.use_fused) {
       // the persistent kernel keeps per-range masks and s by channel
       int *selp = dbg->sel ? (int *)dbg->sel : b.sel;
-      if ((dbg->sel || dbg->s_sel) &&
-          (e = prox::launch_fused_list(p, b, k, selp, (float *)dbg->s_sel, s)) != hipSuccess)
+      if ((dbg->sel || dbg->s_sel || dbg->n_sel) &&
+          (e = prox::launch_fused_list(p, b, k, selp, (float *)dbg->s_sel, (int *)dbg->n_sel,
+                                       s)) != hipSuccess)
         return hip_fail(e, "list kernel");
       return PROX_OK;
     }
@@ -383,6 +384,66 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
         return hip_fail(e, "copy s");
     }
   }
+  return PROX_OK;
+}
+
+static prox_status check_ts_args(const prox_layer *layer, const void *x, float threshold_x,
+                                 float threshold_s, const void *y) {
+  prox_status st = check_forward_args(layer, x, 1, threshold_x, 0, y);
+  if (st != PROX_OK) return st;
+  if (isnan(threshold_s)) return fail(PROX_EINVAL, "threshold_s is NaN");
+  if (!layer->plan.use_fused)
+    return fail(PROX_EUNSUPPORTED,
+                "the Stage 2 threshold mask runs on the persistent kernel only (layer prepared "
+                "with PROX_PATH=multi)");
+  return PROX_OK;
+}
+
+prox_status prox_ffn_forward_ts(const prox_layer *layer, const void *x, float threshold_x,
+                                float threshold_s, void *y, void *stream) {
+  g_err.clear();
+  prox_status st = check_ts_args(layer, x, threshold_x, threshold_s, y);
+  if (st != PROX_OK) return st;
+  hipError_t e = prox::launch_fused(layer->plan, layer->bufs, x, threshold_x, 0, y, nullptr,
+                                    (hipStream_t)stream, nullptr, true, threshold_s);
+  if (e != hipSuccess) return hip_fail(e, "fused kernel");
+  return PROX_OK;
+}
+
+prox_status prox_ffn_forward_ts_debug(const prox_layer *layer, const void *x, float threshold_x,
+                                      float threshold_s, void *y, const prox_debug *dbg,
+                                      void *stream) {
+  g_err.clear();
+  prox_status st = check_ts_args(layer, x, threshold_x, threshold_s, y);
+  if (st != PROX_OK) return st;
+  if (!dbg) return fail(PROX_EINVAL, "dbg is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  const prox::Plan &p = layer->plan;
+  const prox::Bufs &b = layer->bufs;
+  hipError_t e = hipSuccess;
+  if (dbg->status &&
+      (e = hipMemsetAsync(b.sync + prox::kFusedErrWord, 0, sizeof(unsigned), s)) != hipSuccess)
+    return hip_fail(e, "clear status");
+  if ((e = prox::launch_fused(p, b, x, threshold_x, 0, y, nullptr, s, nullptr, true,
+                              threshold_s)) != hipSuccess)
+    return hip_fail(e, "fused kernel");
+  if (dbg->status &&
+      (e = hipMemcpyAsync(dbg->status, b.sync + prox::kFusedErrWord, sizeof(unsigned),
+                          hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return hip_fail(e, "copy status");
+  if (dbg->n1 || dbg->idx) {
+    if (!dbg->n1 || !dbg->idx) return fail(PROX_EINVAL, "n1 and idx must be given together");
+    e = prox::launch_compact_debug(p, x, 1, threshold_x, dbg->n1, dbg->idx, s);
+    if (e != hipSuccess) return hip_fail(e, "compaction debug kernel");
+  }
+  if (dbg->s_abs && (e = hipMemcpyAsync(dbg->s_abs, b.sabs, (size_t)p.d_ff * 4,
+                                        hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return hip_fail(e, "copy |s~|");
+  int *selp = dbg->sel ? (int *)dbg->sel : b.sel;
+  if ((dbg->sel || dbg->s_sel || dbg->n_sel) &&
+      (e = prox::launch_fused_list(p, b, p.d_ff, selp, (float *)dbg->s_sel, (int *)dbg->n_sel,
+                                   s)) != hipSuccess)
+    return hip_fail(e, "list kernel");
   return PROX_OK;
 }
 
@@ -453,7 +514,7 @@ prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x, floa
   if (k == 0) return fail(PROX_EINVAL, "k = 0 launches no persistent kernel");
   if (!counts) return fail(PROX_EINVAL, "counts is NULL");
   const int n_p1 = p.ntile * p.nchunk, n_p3 = prox::fused_p3_items(p);
-  const int total = prox::fused_items(p, k);
+  const int total = prox::fused_items(p, false);
   counts[0] = n_p1;
   counts[1] = 1;
   counts[2] = n_p3;

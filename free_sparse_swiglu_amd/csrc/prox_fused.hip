@@ -82,9 +82,12 @@ struct FusedArgs {
   float *ypart;
   unsigned *col_cnt;
   unsigned *sync;
+  unsigned *tflag;  // per P1 tile: |s~| written (word t * kSyncStride)
   unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
   unsigned *gmask;  // [n_p3][2] per P3 item: channels above bin b*, channels in it
-  int n_p1, n_p3, n_p4;
+  int ts_mode;      // 1: Stage 2 mask |s~| >= tau_s instead of top-k (no P2)
+  float tau_s;
+  int n_p1, n_p2, n_p3, n_p4;
   unsigned long long *trace;  // optional per-ticket timeline (nullptr: off)
 };
 
@@ -279,18 +282,22 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
     if (j < a.d_ff) {
       const float v = fabsf(u * silu(gg));
       xstore(&a.sabs[j], v);
-      atomicAdd(&h[__float_as_uint(v) >> 20], 1u);
+      if (!a.ts_mode) atomicAdd(&h[__float_as_uint(v) >> 20], 1u);
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 2048; i += kFT) {
-    const unsigned c = h[i];
-    if (c) __hip_atomic_fetch_add(&a.ghist[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!a.ts_mode) {
+    for (int i = threadIdx.x; i < 2048; i += kFT) {
+      const unsigned c = h[i];
+      if (c) __hip_atomic_fetch_add(&a.ghist[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
+    xstore_u(&a.tflag[t * kSyncStride], 1u);
     __hip_atomic_fetch_add(&a.sync[kSyncTiles], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -594,9 +601,15 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int i, int lane) {
 
 template <bool BF16>
 __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
+  const int c0 = item * kP3Ch;
   if (threadIdx.x == 0) {
-    wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
-    sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
+    if (a.ts_mode) {
+      wait_geq(&a.tflag[(c0 / kTile) * kSyncStride], 1u, &a.sync[kSyncErr]);
+      sm.bstar = 0u;
+    } else {
+      wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
+      sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
+    }
     stamp_wait(a);
   }
   __syncthreads();
@@ -604,12 +617,15 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = a.d_ff;
-  const int c0 = item * kP3Ch;
   const int j = c0 + lane;
   const bool valid = lane < kP3Ch && j < n;
-  const unsigned d1 = __float_as_uint(xload(&a.sabs[min(j, n - 1)])) >> 20;
-  const uint64_t dm = __ballot(valid && d1 > bstar);   // selected whatever T is
-  const uint64_t bm = __ballot(valid && d1 == bstar);  // decided later by T and J
+  const unsigned key = __float_as_uint(xload(&a.sabs[min(j, n - 1)]));
+  const unsigned d1 = key >> 20;
+  // top-k: selected whatever T is / decided later by T and J;
+  // threshold: kept iff |s~| >= tau_s, nothing left to decide
+  const uint64_t dm = a.ts_mode ? __ballot(valid && __uint_as_float(key) >= a.tau_s)
+                                : __ballot(valid && d1 > bstar);
+  const uint64_t bm = a.ts_mode ? 0ull : __ballot(valid && d1 == bstar);
   // s of both sets: the bin-b* channels are computed before T is known
   // (about twice the kept ones, a few percent of the step's bytes) so that
   // nothing here waits for the select.
@@ -651,9 +667,17 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.d_ff;
-  // 1. b*, then the range's channels with digit 1 >= b* (the kept ones and
-  // the bin-b* ones that may drop), ascending, with their keys.
-  if (tid == 0) {
+  // 1. b* (top-k) or the range's Stage 1 tiles (threshold), then the range's
+  // channels that may be kept (top-k: digit 1 >= b*, the kept ones and the
+  // bin-b* ones that may drop; threshold: |s~| >= tau_s), ascending, with
+  // their keys.
+  if (a.ts_mode) {
+    if (tid < 64) {
+      constexpr int TPR = kP4Ch / kTile;  // tiles per range
+      const int t0 = r * TPR, t1 = min(a.ntile, t0 + TPR) - 1;
+      wave_wait_flags(&a.tflag[min(t0 + lane, t1) * kSyncStride], &a.sync[kSyncErr]);
+    }
+  } else if (tid == 0) {
     wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
     sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
   }
@@ -661,7 +685,8 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
   {
     const int ch = r * kP4Ch + tid;
     const unsigned key = __float_as_uint(xload(&a.sabs[min(ch, n - 1)]));
-    const bool cand = ch < n && (key >> 20) >= sm.bstar;
+    const bool cand = ch < n && (a.ts_mode ? __uint_as_float(key) >= a.tau_s
+                                           : (key >> 20) >= sm.bstar);
     const uint64_t bw = __ballot(cand);
     if (lane == 0) sm.wcnt[wv] = (unsigned)__popcll(bw);
     __syncthreads();
@@ -701,18 +726,20 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
   // finish.
   if (nr > 0) load_batch(0);
   if (tid < 64) {
-    // lanes 0..QPR-1: the range's P3 items; the others: the select (T, J)
+    // lanes 0..QPR-1: the range's P3 items; the others: the select (T, J),
+    // which the threshold mode does not have
     const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
-    const unsigned *f = lane < QPR ? &a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride]
-                                   : &a.sync[kSyncSelect];
+    const unsigned *f = (lane < QPR || a.ts_mode)
+                            ? &a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride]
+                            : &a.sync[kSyncSelect];
     wave_wait_flags(f, &a.sync[kSyncErr]);
     if (lane == 0) stamp_wait(a);
   }
   __syncthreads();
   // 3. s of each listed channel, 0 for a bin-b* channel below the cut.
   {
-    const unsigned T = xload_u(&a.sync[kSyncSelect + 1]);
-    const int J = (int)xload_u(&a.sync[kSyncSelect + 2]);
+    const unsigned T = a.ts_mode ? 0u : xload_u(&a.sync[kSyncSelect + 1]);
+    const int J = a.ts_mode ? n : (int)xload_u(&a.sync[kSyncSelect + 2]);
     if (tid < nr) {
       const int ch = sm.rs[tid];
       const unsigned key = sm.rk[tid];
@@ -807,7 +834,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     P4Smem p4;
   } sm;
   __shared__ int s_ticket, s_flag;
-  const int total = a.n_p1 + 1 + a.n_p3 + a.n_p4;
+  const int total = a.n_p1 + a.n_p2 + a.n_p3 + a.n_p4;
   // The first min(grid, n_p1) tickets are the work-groups' own indices (all
   // work-groups of the grid are resident at once, see the launcher), which
   // spares the launch burst on the ticket counter; the rest come from it.
@@ -834,10 +861,10 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     if (r < a.n_p1) {
       phase = 1;
       p1_item<BF16>(a, r, sm.p1, &s_flag);
-    } else if ((r -= a.n_p1) == 0) {
+    } else if ((r -= a.n_p1) < a.n_p2) {
       phase = 2;
       p2_select(a, sm.p2);
-    } else if ((r -= 1) < a.n_p3) {
+    } else if ((r -= a.n_p2) < a.n_p3) {
       phase = 3;
       p3_item<BF16>(a, r, sm.p3);
     } else {
@@ -861,10 +888,9 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   __syncthreads();
   if (s_flag) {
     constexpr int kCtl = kSyncP3 / kSyncStride;  // control words before the P3 flags
-    for (int i = threadIdx.x; i < kCtl + a.n_p3; i += kFT) {
-      const int w = i < kCtl ? i * kSyncStride : kSyncP3 + (i - kCtl) * kSyncStride;
-      if (w != kSyncErr) xstore_u(&a.sync[w], 0u);
-    }
+    // control words, P3 flags and tile flags: consecutive lines
+    for (int i = threadIdx.x; i < kCtl + a.n_p3 + a.ntile; i += kFT)
+      if (i * kSyncStride != kSyncErr) xstore_u(&a.sync[i * kSyncStride], 0u);
     for (int i = threadIdx.x; i < 2048; i += kFT) xstore_u(&a.ghist[i], 0u);
   }
 }
@@ -875,7 +901,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, const unsigned *tj,
                                                          const float *sabs, const float *sdense,
                                                          int n_p3, int d_ff, int k, int *sel,
-                                                         float *ssel) {
+                                                         float *ssel, int *count) {
   __shared__ unsigned wsum[kFW];
   __shared__ unsigned base;
   if (threadIdx.x == 0) base = 0u;
@@ -912,6 +938,7 @@ __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, 
     if (threadIdx.x == 0) base += tot;
     __syncthreads();
   }
+  if (count && threadIdx.x == 0) *count = (int)base;
 }
 
 // ---------------------------------------------------------------------------
@@ -932,7 +959,7 @@ static hipError_t fused_go(FusedArgs &a, hipStream_t s) {
       per_cu = 1;
     cap = per_cu * cus;
   }
-  const int total = a.n_p1 + 1 + a.n_p3 + a.n_p4;
+  const int total = a.n_p1 + a.n_p2 + a.n_p3 + a.n_p4;
   const int grid = total < cap ? total : cap;
   fn<<<grid, kFT, 0, s>>>(a);
   return hipGetLastError();
@@ -944,26 +971,32 @@ bool fused_supported(const Plan &p) {
 
 static int fused_n_p3(const Plan &p) { return (p.d_ff + kP3Ch - 1) / kP3Ch; }
 
-// Sync block: control words, P3 flags, the digit-1 histogram, the P3 masks.
-static size_t fused_hist_word(const Plan &p) {
+// Sync block: control words, P3 flags, tile flags (one line each), the
+// digit-1 histogram, the P3 masks.
+static size_t fused_tflag_word(const Plan &p) {
   return (size_t)kSyncP3 + (size_t)fused_n_p3(p) * kSyncStride;
+}
+static size_t fused_hist_word(const Plan &p) {
+  return fused_tflag_word(p) + (size_t)p.ntile * kSyncStride;
 }
 
 size_t fused_sync_words(const Plan &p) { return fused_hist_word(p) + 2048 + 2 * fused_n_p3(p); }
 
 int fused_ypart_rows(const Plan &p) { return (p.d_ff + kP4Ch - 1) / kP4Ch; }
 
-int fused_items(const Plan &p, int k) {
-  (void)k;
-  return p.ntile * p.nchunk + 1 + fused_n_p3(p) + p.ncol * fused_ypart_rows(p);
+int fused_items(const Plan &p, bool ts_mode) {
+  return p.ntile * p.nchunk + (ts_mode ? 0 : 1) + fused_n_p3(p) + p.ncol * fused_ypart_rows(p);
 }
 
 int fused_p3_items(const Plan &p) { return fused_n_p3(p); }
 
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
-                        float *resid, hipStream_t s, unsigned long long *trace) {
+                        float *resid, hipStream_t s, unsigned long long *trace, bool ts_mode,
+                        float tau_s) {
   FusedArgs a{};
   a.trace = trace;
+  a.ts_mode = ts_mode ? 1 : 0;
+  a.tau_s = tau_s;
   a.pq = b.pq;
   a.psc = b.psc;
   a.wug = b.wug;
@@ -989,19 +1022,21 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.ypart = b.ypart;
   a.col_cnt = b.col_cnt;
   a.sync = b.sync;
+  a.tflag = b.sync + fused_tflag_word(p);
   a.ghist = b.sync + fused_hist_word(p);
   a.gmask = a.ghist + 2048;
   a.n_p1 = p.ntile * p.nchunk;
+  a.n_p2 = ts_mode ? 0 : 1;
   a.n_p3 = fused_n_p3(p);
   a.n_p4 = p.ncol * a.nrange;
   return p.bf16 ? fused_go<true>(a, s) : fused_go<false>(a, s);
 }
 
 hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,
-                             hipStream_t s) {
+                             int *count, hipStream_t s) {
   const unsigned *gmask = b.sync + fused_hist_word(p) + 2048;
   fused_list_kernel<<<1, kFT, 0, s>>>(gmask, b.sync + kSyncSelect, b.sabs, b.ssp, fused_n_p3(p),
-                                      p.d_ff, k, sel, ssel);
+                                      p.d_ff, k, sel, ssel, count);
   return hipGetLastError();
 }
 

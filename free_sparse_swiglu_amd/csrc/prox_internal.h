@@ -41,7 +41,7 @@ struct Bufs {
   uint8_t *umask;  // [d_ff]                        token bits per union entry
   float *ypart;    // [nrc][batch][d_model]         Stage 2 down partial sums
   unsigned *col_cnt;  // [ncol]                    Stage 2 arrival counters
-  unsigned *sync;  // [(5 + ceil(d_ff/8)) * 64]     fused kernel tickets and flags
+  unsigned *sync;  // fused kernel: tickets, flags, histogram, masks (fused_sync_words)
   void *xbuf;      // [batch][d_model] dtype         stack: normalized input
   void *ybuf;      // [batch][d_model] dtype         stack: layer output
 };
@@ -96,15 +96,19 @@ hipError_t launch_zero_y(const Plan &p, void *y, int batch, hipStream_t s);
 bool fused_supported(const Plan &p);
 size_t fused_sync_words(const Plan &p);
 int fused_ypart_rows(const Plan &p);  // partial-y rows the fused kernel needs
-// trace: optional [fused_items][4] u64 timeline (start, wait end, end, block).
+// trace: optional [fused_items][4] u64 timeline (start, wait end, end,
+// block | phase << 32).  ts_mode: Stage 2 mask |s~| >= tau_s instead of top-k
+// (k is then unused).
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
-                        float *resid, hipStream_t s, unsigned long long *trace = nullptr);
-int fused_items(const Plan &p, int k);
+                        float *resid, hipStream_t s, unsigned long long *trace = nullptr,
+                        bool ts_mode = false, float tau_s = 0.0f);
+int fused_items(const Plan &p, bool ts_mode);
 int fused_p3_items(const Plan &p);
-// After a fused forward: the ascending kept-channel list and its exact s
-// (k entries each; ssel may be null).
-hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,
-                             hipStream_t s);
+// After a fused forward: the ascending kept-channel list and its exact s (at
+// most cap entries each; ssel and count may be null; count gets the number
+// of kept channels).
+hipError_t launch_fused_list(const Plan &p, const Bufs &b, int cap, int *sel, float *ssel,
+                             int *count, hipStream_t s);
 // Words between two control words of the fused kernel (one 256-byte line each).
 #ifndef PROX_SYNC_STRIDE
 #define PROX_SYNC_STRIDE 64

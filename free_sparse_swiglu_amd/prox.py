@@ -40,7 +40,8 @@ class prox_debug(ctypes.Structure):
     _fields_ = [("n1", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("s_abs", ctypes.c_void_p), ("sel", ctypes.c_void_p),
                 ("s_sel", ctypes.c_void_p), ("n_union", ctypes.c_void_p),
-                ("union_idx", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("union_idx", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("n_sel", ctypes.c_void_p)]
 
 
 _lib = None
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH):
         "prox_dense_ffn_forward_profiled": ([P, P, I, P, ctypes.POINTER(P), I,
                                              ctypes.POINTER(I), P], I),
         "prox_ffn_forward_traced": ([P, P, F, I, P, P, I, ctypes.POINTER(I), P], I),
+        "prox_ffn_forward_ts": ([P, P, F, F, P, P], I),
+        "prox_ffn_forward_ts_debug": ([P, P, F, F, P, ctypes.POINTER(prox_debug), P], I),
         "prox_rmsnorm": ([P, P, I, F, P, P], I),
         "prox_destroy_layer": ([P], None),
         "prox_last_error": ([], ctypes.c_char_p),
@@ -208,8 +211,7 @@ def prox_ffn_forward_batch(layer: Layer, x, threshold: float, k: int, y=None):
     return y
 
 
-def prox_ffn_forward_debug(layer: Layer, x, threshold: float, k: int):
-    """Forward for x [batch][d_model] plus its intermediate results."""
+def _debug_buffers(layer: Layer, x):
     B = int(x.shape[0])
     dev = x.device
     out = dict(
@@ -222,12 +224,38 @@ def prox_ffn_forward_debug(layer: Layer, x, threshold: float, k: int):
         n_union=torch.zeros(1, dtype=torch.int32, device=dev),
         union_idx=torch.full((layer.d_ff,), -1, dtype=torch.int32, device=dev),
         status=torch.zeros(1, dtype=torch.int32, device=dev),
+        n_sel=torch.full((1,), -1, dtype=torch.int32, device=dev),
     )
     dbg = prox_debug(*(ctypes.c_void_p(out[k].data_ptr()) for k in
-                       ("n1", "idx", "s_abs", "sel", "s_sel", "n_union", "union_idx", "status")))
-    _check(load_library().prox_ffn_forward_debug(layer.handle, _ptr(x), B, float(threshold),
-                                                 int(k), _ptr(out["y"]), ctypes.byref(dbg),
-                                                 _stream()))
+                       ("n1", "idx", "s_abs", "sel", "s_sel", "n_union", "union_idx", "status",
+                        "n_sel")))
+    return out, dbg
+
+
+def prox_ffn_forward_debug(layer: Layer, x, threshold: float, k: int):
+    """Forward for x [batch][d_model] plus its intermediate results."""
+    out, dbg = _debug_buffers(layer, x)
+    _check(load_library().prox_ffn_forward_debug(layer.handle, _ptr(x), int(x.shape[0]),
+                                                 float(threshold), int(k), _ptr(out["y"]),
+                                                 ctypes.byref(dbg), _stream()))
+    return out
+
+
+def prox_ffn_forward_ts(layer: Layer, x, threshold_x: float, threshold_s: float, y=None):
+    """Batch-1 forward with the Stage 2 threshold mask |s~| >= threshold_s."""
+    y = _out_like(x, y)
+    _check(load_library().prox_ffn_forward_ts(layer.handle, _ptr(x), float(threshold_x),
+                                              float(threshold_s), _ptr(y), _stream()))
+    return y
+
+
+def prox_ffn_forward_ts_debug(layer: Layer, x, threshold_x: float, threshold_s: float):
+    """prox_ffn_forward_ts for x [1][d_model] plus its intermediate results
+    (n_sel holds the number of kept channels)."""
+    out, dbg = _debug_buffers(layer, x)
+    _check(load_library().prox_ffn_forward_ts_debug(layer.handle, _ptr(x), float(threshold_x),
+                                                    float(threshold_s), _ptr(out["y"]),
+                                                    ctypes.byref(dbg), _stream()))
     return out
 
 

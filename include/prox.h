@@ -137,12 +137,34 @@ typedef struct {
   int32_t *status;   /* [1]  0, or bit 0: a bounded wait of the fused batch-1
                         kernel timed out (results invalid); bit 1: its top-k
                         took the slow exact path (results valid)             */
+  int32_t *n_sel;    /* [1]  number of kept channels (batch-1 persistent kernel:
+                        k for top-k, the count for the threshold mask)      */
 } prox_debug;
 
 /* prox_ffn_forward_batch plus a copy of its intermediate results into `dbg`. */
 prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x,
                                    int batch, float threshold, int k, void *y,
                                    const prox_debug *dbg, void *stream);
+
+/* Batch-1 forward with the calibrated Stage 2 threshold of Sec. 4.1 instead
+ * of the per-token top-k: channel j is kept iff |s~_j| >= threshold_s (|s~|
+ * in float32), so the number of kept channels varies per token.  Stage 1 is
+ * as in prox_ffn_forward (input mask |x_i| >= threshold_x, INT4 proxy).  Runs
+ * on the persistent kernel without its select phase: each Stage 2 item
+ * starts as soon as the Stage 1 tile holding its channels is done.
+ * Errors: PROX_EINVAL for a NaN threshold or bad pointers; PROX_EUNSUPPORTED
+ * for a layer prepared with PROX_PATH=multi.                                 */
+prox_status prox_ffn_forward_ts(const prox_layer *layer, const void *x,
+                                float threshold_x, float threshold_s, void *y,
+                                void *stream);
+
+/* prox_ffn_forward_ts plus its intermediate results: n1, idx, s_abs, sel (the
+ * kept channels, ascending, up to d_ff), s_sel (their exact s), n_sel (their
+ * count) and status; n_union and union_idx are not written.                 */
+prox_status prox_ffn_forward_ts_debug(const prox_layer *layer, const void *x,
+                                      float threshold_x, float threshold_s,
+                                      void *y, const prox_debug *dbg,
+                                      void *stream);
 
 /* Dense SwiGLU FFN on the same relaid weights (Sec. 2.1), the baseline:
  * y = (x W_up . SiLU(x W_gate)) W_down for `batch` tokens.                   */

@@ -40,6 +40,25 @@ def check_mask(sel_gpu, sel_or, s_t_or, k: int) -> dict:
     return dict(band=int(band.sum()), diff=int(diff.size))
 
 
+def check_threshold_mask(sel_gpu, sel_or, s_t_or, tau_s: float) -> dict:
+    """Stage 2 threshold mask |s~| >= tau_s: the GPU list must be strictly
+    ascending and in range, and may differ from the oracle's only at channels
+    whose oracle |s~| lies within BAND_REL (relative) of tau_s, where the
+    float32 summation order of the GPU can move a channel across the line."""
+    sel_gpu = np.asarray(sel_gpu, dtype=np.int64)
+    sel_or = np.asarray(sel_or, dtype=np.int64)
+    a = np.abs(np.asarray(s_t_or, dtype=np.float64))
+    n = a.size
+    if sel_gpu.size:
+        assert np.all(np.diff(sel_gpu) > 0), "GPU selection not strictly ascending"
+        assert sel_gpu.min() >= 0 and sel_gpu.max() < n, "GPU selection out of range"
+    diff = np.setxor1d(sel_gpu, sel_or)
+    band = np.abs(a - tau_s) <= BAND_REL * abs(tau_s)
+    outside = [int(j) for j in diff if not band[j]]
+    assert not outside, f"mask differs outside the threshold band at channels {outside[:10]}"
+    return dict(band=int(band.sum()), diff=int(diff.size))
+
+
 def expected_y(sel_gpu, sel_or, y_or, s_exact_all, W_down) -> np.ndarray:
     sel_gpu = np.asarray(sel_gpu, dtype=np.int64)
     if np.array_equal(sel_gpu, np.asarray(sel_or, dtype=np.int64)):

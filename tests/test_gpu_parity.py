@@ -22,7 +22,7 @@ import torch
 
 import oracle
 from free_sparse_swiglu_amd import prox, synth
-from tests.parity_utils import check_mask, expected_y, rel_err
+from tests.parity_utils import check_mask, check_threshold_mask, expected_y, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -343,3 +343,85 @@ def test_fused_path_repeated_launches_are_identical():
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Stage 2 threshold mask (|s~| >= tau_s) instead of top-k
+# ---------------------------------------------------------------------------
+def _check_ts(case, xd, x_np, tau_x, tau_s, out, stats=None):
+    cfg = case.cfg
+    assert int(out["status"][0]) == 0
+    ref = oracle.forward_ts(case.ol, x_np, tau_x, tau_s)
+    n1 = int(out["n1"][0])
+    assert out["idx"][0, :n1].cpu().numpy().tolist() == ref["idx"].tolist()
+    if np.max(np.abs(ref["s_t"])) > 0:
+        assert rel_err(out["s_abs"][0].cpu().numpy(), np.abs(ref["s_t"])) <= 1e-4
+    m = int(out["n_sel"][0])
+    sel = out["sel"][0, :m].cpu().numpy()
+    mk = check_threshold_mask(sel, ref["sel"], ref["s_t"], tau_s)
+    y = out["y"][0].float().cpu().numpy().astype(np.float64)
+    if m == 0:
+        assert ref["sel"].size == 0 and not np.any(y)
+        return
+    s_exact, _ = oracle.dense(x_np, *case.Wnp)
+    s_sel = out["s_sel"][0, :m].cpu().numpy().astype(np.float64)
+    assert rel_err(s_sel, s_exact[sel]) <= 1e-4
+    y_ref = expected_y(sel, ref["sel"], ref["y"], s_exact, case.Wnp[2])
+    e_y = rel_err(y, y_ref)
+    assert e_y <= _tol(cfg), f"y error {e_y:.3e} (tau_s={tau_s})"
+    if stats is not None:
+        stats.append(dict(m=m, band=mk["band"], diff=mk["diff"], e_y=e_y))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "8b"])
+def test_threshold_mask_parity(name):
+    cfg = RAGGED if name == "ragged" else synth.CONFIGS[name]
+    gen = DEV if name == "8b" else "cpu"
+    case = get_case(cfg, gen)
+    X = synth.make_inputs(cfg, 3, "ts", 0, gen)
+    stats = []
+    for t in range(X.shape[0]):
+        x_np = X[t].float().cpu().numpy()
+        s_t = oracle.forward(case.ol, x_np, case.tau, 1)["s_t"]
+        for q in (0.5, 0.7, 0.9):
+            tau_s = float(np.quantile(np.abs(s_t), q))
+            xd = X[t:t + 1].to(DEV)
+            out = prox.prox_ffn_forward_ts_debug(case.L, xd, case.tau, tau_s)
+            torch.cuda.synchronize()
+            _check_ts(case, xd, x_np, case.tau, tau_s, out, stats)
+    print(name, stats)
+    # the product entry gives the debug entry's bits
+    xd = X[:1].to(DEV)
+    tau_s = float(np.quantile(np.abs(oracle.forward(case.ol, X[0].float().cpu().numpy(),
+                                                    case.tau, 1)["s_t"]), 0.7))
+    y1 = prox.prox_ffn_forward_ts(case.L, xd[0], case.tau, tau_s)
+    yd = prox.prox_ffn_forward_ts_debug(case.L, xd, case.tau, tau_s)["y"][0]
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), yd.view(torch.int16))
+
+
+@pytest.mark.parametrize("tau_s", [0.0, float("inf"), 1e30])
+def test_threshold_mask_edges(tau_s):
+    case = get_case(RAGGED)
+    X = case.inputs(2, "ts-edges")
+    for t in range(X.shape[0]):
+        xd = X[t:t + 1].to(DEV)
+        out = prox.prox_ffn_forward_ts_debug(case.L, xd, case.tau, tau_s)
+        torch.cuda.synchronize()
+        _check_ts(case, xd, X[t].float().numpy(), case.tau, tau_s, out)
+        if tau_s == 0.0:
+            assert int(out["n_sel"][0]) == RAGGED.d_ff
+
+
+def test_threshold_mask_rejects_nan_and_multi_path(monkeypatch):
+    case = get_case(RAGGED)
+    x = case.inputs(1)[0].to(DEV)
+    with pytest.raises(prox.ProxError) as e:
+        prox.prox_ffn_forward_ts(case.L, x, case.tau, float("nan"))
+    assert e.value.status == prox.PROX_EINVAL
+    monkeypatch.setenv("PROX_PATH", "multi")
+    multi = Case(RAGGED, 0, "cpu", 1)
+    monkeypatch.delenv("PROX_PATH")
+    with pytest.raises(prox.ProxError) as e:
+        prox.prox_ffn_forward_ts(multi.L, x, case.tau, 0.1)
+    assert e.value.status == prox.PROX_EUNSUPPORTED
