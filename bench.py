@@ -378,6 +378,35 @@ def bench_stack(args):
     run_tokens(k)
     sec = run_tokens(k)
     dsec = run_tokens(-1)
+
+    # The pages' own operating mode: calibrated thresholds for both stages
+    # (Sec. 4.1 masks), allocated for a 70% effective sparsity target (Sec. 4.2:
+    # s1 = 0.7, s2 = 0.767), calibrated sequentially (App. A.7, Algorithm 1)
+    # on 64 tokens, timed on the same 128 tokens, runtime sparsity measured on
+    # 16 other tokens.
+    from free_sparse_swiglu_amd import costmodel
+    s1, s2 = costmodel.allocate(0.7)
+    tx, ts = calibrate.sequential_thresholds_ts(layers, calib[:64], s1, s2)
+
+    def run_tokens_ts():
+        r.copy_(R0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(ntok):
+            prox.prox_stack_forward_ts(layers, tx, ts, r[t])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    run_tokens_ts()
+    tsec = run_tokens_ts()
+    held = synth.make_inputs(cfg, 16, "held-out", 0, "cuda").float()
+    rs = calibrate.runtime_sparsity(layers, tx, ts, held)
+    threshold_mode = dict(
+        target_e=0.7, s1=round(s1, 4), s2=round(s2, 4),
+        tokens_per_s=round(ntok / tsec, 1), speedup_vs_dense=round(dsec / tsec, 3),
+        us_per_layer=round(tsec / ntok / cfg.layers * 1e6, 2),
+        runtime=dict(s1=round(rs["s1"], 4), s2=round(rs["s2"], 4), e=round(rs["e"], 4)),
+        thresholds_x=[round(t, 5) for t in tx], thresholds_s=[float("%.5g" % t) for t in ts])
     return dict(metric="tokens/s of a 32-layer 8B-shaped FFN stack, batch 1, 70% sparsity",
                 value=round(ntok / sec, 1), unit="tokens/s", n_gpus=1, dtype="bf16",
                 data="synthetic", higher_is_better=True,
@@ -385,7 +414,8 @@ def bench_stack(args):
                                      "128 sequential tokens", k=k, layers=cfg.layers),
                 dense_tokens_per_s=round(ntok / dsec, 1), speedup_vs_dense=round(dsec / sec, 3),
                 us_per_layer=round(sec / ntok / cfg.layers * 1e6, 2),
-                thresholds=[round(t, 5) for t in taus])
+                thresholds=[round(t, 5) for t in taus],
+                threshold_mode=threshold_mode)
 
 
 def bench_copy(args):

@@ -488,6 +488,37 @@ prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
   return PROX_OK;
 }
 
+prox_status prox_stack_forward_ts(const prox_layer *const *layers, int n_layers,
+                                  const float *thresholds_x, const float *thresholds_s,
+                                  float *resid, float eps, void *stream) {
+  g_err.clear();
+  if (!layers || n_layers <= 0 || !resid || !thresholds_x || !thresholds_s)
+    return fail(PROX_EINVAL, "layers, n_layers > 0, both threshold arrays and resid are required");
+  if (!(eps >= 0.0f)) return fail(PROX_EINVAL, "eps must be >= 0");
+  if (!aligned(resid, 16)) return fail(PROX_EINVAL, "resid must be 16-byte aligned");
+  const prox::Plan &p0 = layers[0] ? layers[0]->plan : prox::Plan{};
+  for (int l = 0; l < n_layers; ++l) {
+    const prox_layer *L = layers[l];
+    if (!L) return fail(PROX_EINVAL, "layer %d is NULL", l);
+    if (L->plan.d_model != p0.d_model || L->plan.bf16 != p0.bf16)
+      return fail(PROX_EINVAL, "layer %d has a different d_model or dtype", l);
+    if (!L->plan.use_fused)
+      return fail(PROX_EUNSUPPORTED, "layer %d was prepared with PROX_PATH=multi", l);
+    if (isnan(thresholds_x[l]) || isnan(thresholds_s[l]))
+      return fail(PROX_EINVAL, "threshold of layer %d is NaN", l);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    const prox_layer *L = layers[l];
+    hipError_t e = prox::launch_rmsnorm(L->plan, resid, 1, eps, L->bufs.xbuf, s);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel");
+    e = prox::launch_fused(L->plan, L->bufs, L->bufs.xbuf, thresholds_x[l], 0, L->bufs.ybuf, resid,
+                           s, nullptr, true, thresholds_s[l]);
+    if (e != hipSuccess) return hip_fail(e, "fused kernel");
+  }
+  return PROX_OK;
+}
+
 prox_status prox_ffn_forward_profiled(const prox_layer *layer, const void *x, int batch,
                                       float threshold, int k, void *y,
                                       void *const *events, int n_events, int *n_recorded,

@@ -73,6 +73,8 @@ def load_library(path: str = LIB_PATH):
                                              ctypes.POINTER(I), P], I),
         "prox_ffn_forward_traced": ([P, P, F, I, P, P, I, ctypes.POINTER(I), P], I),
         "prox_ffn_forward_ts": ([P, P, F, F, P, P], I),
+        "prox_stack_forward_ts": ([ctypes.POINTER(P), I, ctypes.POINTER(F), ctypes.POINTER(F), P,
+                                   F, P], I),
         "prox_ffn_forward_ts_debug": ([P, P, F, F, P, ctypes.POINTER(prox_debug), P], I),
         "prox_rmsnorm": ([P, P, I, F, P, P], I),
         "prox_destroy_layer": ([P], None),
@@ -332,4 +334,15 @@ def prox_stack_forward(layers, thresholds, k: int, resid, eps: float = 1e-5):
     B = 1 if resid.dim() == 1 else int(resid.shape[0])
     _check(load_library().prox_stack_forward(arr, n, th, int(k), _ptr(resid), B, float(eps),
                                              _stream()))
+    return resid
+
+
+def prox_stack_forward_ts(layers, thresholds_x, thresholds_s, resid, eps: float = 1e-5):
+    """Run the FFN stack with Stage 2 threshold masks on the float32 residual
+    resid [d_model] (one token) in place."""
+    n = len(layers)
+    arr = (ctypes.c_void_p * n)(*[L.handle for L in layers])
+    tx = (ctypes.c_float * n)(*[float(t) for t in thresholds_x])
+    ts = (ctypes.c_float * n)(*[float(t) for t in thresholds_s])
+    _check(load_library().prox_stack_forward_ts(arr, n, tx, ts, _ptr(resid), float(eps), _stream()))
     return resid

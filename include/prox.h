@@ -181,6 +181,16 @@ prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
                                const float *thresholds, int k, float *resid,
                                int batch, float eps, void *stream);
 
+/* prox_stack_forward with the Stage 2 threshold mask of every layer (batch
+ * 1): x = cast(RMSNorm(r)), y = Prox-FFN_l(x) with |x_i| >= thresholds_x[l]
+ * and |s~_j| >= thresholds_s[l], r = r + y.  Both threshold arrays are HOST
+ * arrays [n_layers].  PROX_EUNSUPPORTED if a layer was prepared with
+ * PROX_PATH=multi.                                                          */
+prox_status prox_stack_forward_ts(const prox_layer *const *layers, int n_layers,
+                                  const float *thresholds_x,
+                                  const float *thresholds_s, float *resid,
+                                  float eps, void *stream);
+
 /* The stack's normalization alone: x = cast(r / sqrt(mean(r^2) + eps)) for
  * `batch` (1..8) rows of the float32 residual r [batch][d_model], written in
  * the layer dtype.  Used to collect layer inputs for threshold calibration

@@ -26,6 +26,7 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -269,3 +270,62 @@ def stack_forward(layers, taus, k: int, r0, eps: float = 1e-5, to_bf16=True):
         o["x"] = x
         outs.append(o)
     return r, outs
+
+
+# --------------------------------------------------------------------------
+# Stack with Stage 2 threshold masks, and its sequential calibration
+# (App. A.7, Algorithm 1).
+# --------------------------------------------------------------------------
+def lower_quantile(values, q: float) -> float:
+    """Lower empirical quantile: the sorted values at position floor(q (N - 1))."""
+    v = np.sort(np.asarray(values, dtype=np.float64).ravel())
+    return float(v[int(math.floor(q * (v.size - 1)))])
+
+
+def stack_forward_ts(layers, taus_x, taus_s, r0, eps: float = 1e-5, to_bf16=True):
+    """Pre-norm residual stack with the Stage 2 threshold mask in every layer:
+    x_l = cast(RMSNorm(r_l)), y_l = forward_ts(x_l), r_{l+1} = r_l + cast(y_l).
+    Returns (r_L, per-layer dicts)."""
+    r = np.asarray(r0, dtype=np.float64).copy()
+    outs = []
+    for layer, tx, ts in zip(layers, taus_x, taus_s):
+        x = rmsnorm(r, eps, to_bf16)
+        o = forward_ts(layer, x, tx, ts)
+        yc = o["y"].astype(np.float32)
+        if to_bf16:
+            yc = round_bf16(yc)
+        r = r + yc.astype(np.float64)
+        o["x"] = x
+        outs.append(o)
+    return r, outs
+
+
+def calibrate_sequential(layers, calib_r0, s1: float, s2: float, eps: float = 1e-5,
+                         to_bf16=True):
+    """Algorithm 1 of App. A.7, layer by layer in depth order: the calibration
+    tokens' inputs x_l are collected after layers 1..l-1 ran with their final
+    thresholds; tau_x,l is the s1 quantile of the pooled |x_l|; s~_l is the
+    INT4 proxy state under that input mask; tau_s,l is the s2 quantile of the
+    pooled float32 |s~_l|; then the tokens pass layer l with both thresholds.
+
+    calib_r0: [N][d_model] residual-stream tokens.  Returns (taus_x, taus_s,
+    per-layer inputs [N][d_model] float32)."""
+    R = [np.asarray(r, dtype=np.float64).copy() for r in calib_r0]
+    taus_x, taus_s, inputs = [], [], []
+    for layer in layers:
+        X = np.stack([rmsnorm(r, eps, to_bf16) for r in R])
+        tx = lower_quantile(np.abs(X.astype(np.float32)), s1)
+        S = []
+        for x in X:
+            _, _, s_t = proxy(x, input_mask(x, tx), layer.Wt_up, layer.Wt_gate)
+            S.append(np.abs(s_t).astype(np.float32))
+        ts = lower_quantile(np.concatenate(S), s2)
+        for t, x in enumerate(X):
+            yc = forward_ts(layer, x, tx, ts)["y"].astype(np.float32)
+            if to_bf16:
+                yc = round_bf16(yc)
+            R[t] = R[t] + yc.astype(np.float64)
+        taus_x.append(tx)
+        taus_s.append(ts)
+        inputs.append(X)
+    return taus_x, taus_s, inputs

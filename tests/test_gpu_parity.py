@@ -425,3 +425,66 @@ def test_threshold_mask_rejects_nan_and_multi_path(monkeypatch):
     with pytest.raises(prox.ProxError) as e:
         prox.prox_ffn_forward_ts(multi.L, x, case.tau, 0.1)
     assert e.value.status == prox.PROX_EUNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# Threshold-mask stack and its sequential calibration (App. A.7, Alg. 1)
+# ---------------------------------------------------------------------------
+STACK_SMALL = synth.Config("stacksmall", 1024, 2816, 128, "bf16", "student_t", 0.5, 32, (0.7,))
+
+
+def _small_stack(nl):
+    layers, olayers = [], []
+    ws = None
+    for l in range(nl):
+        W = synth.make_layer(STACK_SMALL, l, "cpu")
+        L = prox.prox_prepare_layer(*[w.to(DEV) for w in W], STACK_SMALL.group, 8, workspace=ws)
+        ws = L.workspace
+        layers.append(L)
+        olayers.append(oracle.Layer(*[w.float().numpy() for w in W], STACK_SMALL.group))
+    return layers, olayers
+
+
+def test_sequential_calibration_matches_oracle():
+    """Both thresholds of every layer, teacher-forced: given the inputs the GPU
+    calibration collected for a layer, the oracle's quantiles of |x| and of its
+    own |s~| give the same tau_x (bit-equal) and tau_s (float32 vs double
+    summation only)."""
+    from free_sparse_swiglu_amd import calibrate, costmodel
+    s1, s2 = costmodel.allocate(0.7)  # App. A.4: s1 = 0.7, s2 = 0.767
+    layers, olayers = _small_stack(3)
+    R0 = synth.make_inputs(STACK_SMALL, 24, "calib", 0, "cpu").float()
+    tx, ts, X = calibrate.sequential_thresholds_ts(layers, R0.to(DEV), s1, s2,
+                                                   return_inputs=True)
+    torch.cuda.synchronize()
+    for l, L in enumerate(olayers):
+        Xl = X[l].float().cpu().numpy()
+        assert oracle.lower_quantile(np.abs(Xl), s1) == tx[l]
+        S = []
+        for x in Xl:
+            _, _, s_t = oracle.proxy(x, oracle.input_mask(x, tx[l]), L.Wt_up, L.Wt_gate)
+            S.append(np.abs(s_t).astype(np.float32))
+        ts_or = oracle.lower_quantile(np.concatenate(S), s2)
+        assert abs(ts[l] - ts_or) <= 1e-3 * ts_or, (l, ts[l], ts_or)
+
+
+def test_stack_ts_parity_and_runtime_sparsity():
+    from free_sparse_swiglu_amd import calibrate, costmodel
+    s1, s2 = costmodel.allocate(0.7)
+    layers, olayers = _small_stack(4)
+    R0 = synth.make_inputs(STACK_SMALL, 16, "calib", 0, "cpu").float()
+    tx, ts, _ = oracle.calibrate_sequential(olayers, R0.numpy(), s1, s2)
+    T = synth.make_inputs(STACK_SMALL, 3, "stack", 0, "cpu").float()
+    n1s, nss = 0, 0
+    for t in range(T.shape[0]):
+        r = T[t].clone().to(DEV)
+        prox.prox_stack_forward_ts(layers, tx, ts, r)
+        torch.cuda.synchronize()
+        r_ref, outs = oracle.stack_forward_ts(olayers, tx, ts, T[t].numpy())
+        assert rel_err(r.cpu().numpy(), r_ref) <= 2e-2
+        n1s += sum(o["idx"].size for o in outs)
+        nss += sum(o["sel"].size for o in outs)
+    rs = calibrate.runtime_sparsity(layers, tx, ts, T.to(DEV))
+    e_or = costmodel.effective_sparsity(1 - n1s / (3 * 4 * STACK_SMALL.d_model),
+                                        1 - nss / (3 * 4 * STACK_SMALL.d_ff))
+    assert abs(rs["e"] - e_or) <= 0.01, (rs, e_or)

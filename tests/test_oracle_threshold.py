@@ -100,3 +100,75 @@ def test_forward_ts_matches_topk_forward_at_kth_proxy_value():
         np.testing.assert_array_equal(ts["y"], tk["y"])
         checked += 1
     assert checked >= 3
+
+
+# ---------------------------------------------------------------------------
+# Sequential calibration (App. A.7, Algorithm 1)
+# ---------------------------------------------------------------------------
+def test_lower_quantile_counts():
+    """With N distinct values, the threshold at quantile q keeps exactly
+    N - floor(q (N - 1)) of them under the >= rule: the realized sparsity on
+    the calibration set is q up to one part in N."""
+    rng = np.random.default_rng(13)
+    v = np.abs(_distinct_f32(rng, 1000))
+    for q in (0.0, 0.3, 0.5, 0.7, 0.767, 1.0):
+        t = oracle.lower_quantile(v, q)
+        kept = int(np.sum(v >= t))
+        assert kept == 1000 - math.floor(q * 999)
+        assert abs((1 - kept / 1000) - q) <= 1 / 1000 + 1e-12
+
+
+def _stack(nl=3, d_model=64, d_ff=96, G=16, seed=20):
+    rng = np.random.default_rng(seed)
+    layers = []
+    for _ in range(nl):
+        Wu = rng.normal(0, 0.05, (d_model, d_ff)).astype(np.float32)
+        Wg = rng.normal(0, 0.05, (d_model, d_ff)).astype(np.float32)
+        Wd = rng.normal(0, 0.05, (d_ff, d_model)).astype(np.float32)
+        layers.append(oracle.Layer(Wu, Wg, Wd, G))
+    R0 = rng.standard_t(4, size=(12, d_model))
+    return layers, R0
+
+
+def test_calibration_keeps_everything_at_zero_targets_and_is_dense():
+    """s1 = s2 = 0: every threshold is the smallest value seen, nothing is
+    pruned on the calibration tokens, and the calibrated stack equals the
+    dense stack (k = d_ff, tau_x = 0) on them."""
+    layers, R0 = _stack()
+    tx, ts, X = oracle.calibrate_sequential(layers, R0, 0.0, 0.0)
+    for t in range(R0.shape[0]):
+        r_ts, _ = oracle.stack_forward_ts(layers, tx, ts, R0[t])
+        r_dense, _ = oracle.stack_forward(layers, [0.0] * len(layers), layers[0].d_ff, R0[t])
+        np.testing.assert_allclose(r_ts, r_dense, rtol=0, atol=1e-12 * np.max(np.abs(r_dense)))
+
+
+def test_calibration_realizes_targets_on_its_tokens():
+    """Each layer's thresholds, applied to the inputs that layer saw during
+    calibration, prune the target fractions (up to quantile granularity), and
+    those inputs are what the calibrated earlier layers produce."""
+    layers, R0 = _stack(nl=3)
+    s1, s2 = 0.5, 0.7
+    tx, ts, X = oracle.calibrate_sequential(layers, R0, s1, s2)
+    def quantile_counts(v, t, q):
+        # lower empirical quantile t at q: at most floor(q (N-1)) values lie
+        # strictly below it and at least floor(q (N-1)) + 1 lie at or below
+        m = math.floor(q * (v.size - 1))
+        assert np.sum(v < t) <= m < np.sum(v <= t)
+
+    for l in range(len(layers)):
+        ax = np.abs(X[l].astype(np.float32)).ravel()
+        quantile_counts(ax, np.float32(tx[l]), s1)
+        sv, kept_s = [], 0
+        for x in X[l]:
+            o = oracle.forward_ts(layers[l], x, tx[l], ts[l])
+            sv.append(np.abs(o["s_t"]).astype(np.float32))
+            kept_s += o["sel"].size
+        sv = np.concatenate(sv)
+        quantile_counts(sv, np.float32(ts[l]), s2)
+        assert kept_s == int(np.sum(sv >= np.float32(ts[l])))
+        assert abs((1 - kept_s / sv.size) - s2) <= 0.02
+    # depth order: layer l's inputs are the stack's inputs with layers < l calibrated
+    for t in range(R0.shape[0]):
+        _, outs = oracle.stack_forward_ts(layers, tx, ts, R0[t])
+        for l in range(len(layers)):
+            np.testing.assert_array_equal(outs[l]["x"], X[l][t])
