@@ -38,6 +38,17 @@
 /* SiLU, the gate nonlinearity of SwiGLU (Sec. 2.1, FFN equation).           */
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* Gate activation of the gated FFN: act 0 is SiLU (SwiGLU, the pages' FFN);
+ * act 1 is GELU in its tanh form, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715
+ * z^3))) (GeGLU, as in Gemma-3 style models).                                */
+double prox_oracle_gate_act(double z, int act) {
+  if (act == 1) {
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+  }
+  return silu(z);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Symmetric INT4 proxy quantization of one weight matrix (Sec. 4.3).
  *
@@ -109,7 +120,7 @@ int prox_oracle_input_mask(const float *x, int d_model, float tau, int *idx) {
  * Outputs u_t, g_t (pre-activation gate) and s_t, each [d_ff].             */
 void prox_oracle_proxy(const float *x, const int *idx, int n1,
                        const double *Wt_up, const double *Wt_gate, int d_ff,
-                       double *u_t, double *g_t, double *s_t) {
+                       double *u_t, double *g_t, double *s_t, int act) {
   for (int j = 0; j < d_ff; ++j) { u_t[j] = 0.0; g_t[j] = 0.0; }
   for (int n = 0; n < n1; ++n) {
     int i = idx[n];
@@ -121,7 +132,7 @@ void prox_oracle_proxy(const float *x, const int *idx, int n1,
       g_t[j] += xi * rg[j];
     }
   }
-  for (int j = 0; j < d_ff; ++j) s_t[j] = u_t[j] * silu(g_t[j]);
+  for (int j = 0; j < d_ff; ++j) s_t[j] = u_t[j] * prox_oracle_gate_act(g_t[j], act);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -177,7 +188,7 @@ int prox_oracle_threshold_mask(const double *z, int n, float tau, int *sel) {
 void prox_oracle_stage2(const float *x, int d_model, int d_ff,
                         const float *W_up, const float *W_gate,
                         const float *W_down, const int *sel, int k,
-                        double *s_sp, double *y) {
+                        double *s_sp, double *y, int act) {
   double *u = (double *)calloc((size_t)(k > 0 ? k : 1), sizeof(double));
   double *g = (double *)calloc((size_t)(k > 0 ? k : 1), sizeof(double));
   for (int i = 0; i < d_model; ++i) {
@@ -189,7 +200,7 @@ void prox_oracle_stage2(const float *x, int d_model, int d_ff,
       g[t] += xi * (double)rg[sel[t]];
     }
   }
-  for (int t = 0; t < k; ++t) s_sp[t] = u[t] * silu(g[t]);
+  for (int t = 0; t < k; ++t) s_sp[t] = u[t] * prox_oracle_gate_act(g[t], act);
   for (int c = 0; c < d_model; ++c) y[c] = 0.0;
   for (int t = 0; t < k; ++t) {
     const float *rd = W_down + (size_t)sel[t] * d_model;
@@ -205,7 +216,7 @@ void prox_oracle_stage2(const float *x, int d_model, int d_ff,
  * it is the exact intermediate state the oracle-s diagnostic ranks (Sec. 3.1). */
 void prox_oracle_dense(const float *x, int d_model, int d_ff,
                        const float *W_up, const float *W_gate,
-                       const float *W_down, double *s_out, double *y) {
+                       const float *W_down, double *s_out, double *y, int act) {
   double *u = (double *)calloc((size_t)d_ff, sizeof(double));
   double *g = (double *)calloc((size_t)d_ff, sizeof(double));
   double *s = (double *)calloc((size_t)d_ff, sizeof(double));
@@ -218,7 +229,7 @@ void prox_oracle_dense(const float *x, int d_model, int d_ff,
       g[j] += xi * (double)rg[j];
     }
   }
-  for (int j = 0; j < d_ff; ++j) s[j] = u[j] * silu(g[j]);
+  for (int j = 0; j < d_ff; ++j) s[j] = u[j] * prox_oracle_gate_act(g[j], act);
   for (int c = 0; c < d_model; ++c) y[c] = 0.0;
   for (int j = 0; j < d_ff; ++j) {
     const float *rd = W_down + (size_t)j * d_model;

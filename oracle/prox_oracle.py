@@ -62,13 +62,15 @@ def _load():
         lib.prox_oracle_dequantize.argtypes = [P, P, I, I, I, P]
         lib.prox_oracle_input_mask.argtypes = [P, I, ctypes.c_float, P]
         lib.prox_oracle_input_mask.restype = I
-        lib.prox_oracle_proxy.argtypes = [P, P, I, P, P, I, P, P, P]
+        lib.prox_oracle_proxy.argtypes = [P, P, I, P, P, I, P, P, P, I]
         lib.prox_oracle_topk.argtypes = [P, I, I, P]
         lib.prox_oracle_topk.restype = I
         lib.prox_oracle_threshold_mask.argtypes = [P, I, ctypes.c_float, P]
         lib.prox_oracle_threshold_mask.restype = I
-        lib.prox_oracle_stage2.argtypes = [P, I, I, P, P, P, P, I, P, P]
-        lib.prox_oracle_dense.argtypes = [P, I, I, P, P, P, P, P]
+        lib.prox_oracle_stage2.argtypes = [P, I, I, P, P, P, P, I, P, P, I]
+        lib.prox_oracle_dense.argtypes = [P, I, I, P, P, P, P, P, I]
+        lib.prox_oracle_gate_act.argtypes = [ctypes.c_double, I]
+        lib.prox_oracle_gate_act.restype = ctypes.c_double
         lib.prox_oracle_round_bf16.argtypes = [ctypes.c_float]
         lib.prox_oracle_round_bf16.restype = ctypes.c_float
         lib.prox_oracle_round_bf16_array.argtypes = [P, ctypes.c_long]
@@ -121,8 +123,14 @@ def input_mask(x, tau: float) -> np.ndarray:
     return idx[:n1].copy()
 
 
-def proxy(x, idx, Wt_up, Wt_gate):
-    """Stage 1 proxy state u~, g~ (pre-SiLU), s~ (Sec. 4.1, u~/h~ equations).
+def gate_act(z: float, act: int = 0) -> float:
+    """Gate activation: 0 = SiLU (SwiGLU), 1 = GELU, tanh form (GeGLU)."""
+    return float(_load().prox_oracle_gate_act(float(z), int(act)))
+
+
+def proxy(x, idx, Wt_up, Wt_gate, act: int = 0):
+    """Stage 1 proxy state u~, g~ (pre-activation), s~ (Sec. 4.1, u~/h~
+    equations; act 1 swaps SiLU for the tanh form of GELU).
 
     Wt_up / Wt_gate are [d_model][d_ff] proxy weights (dequantized INT4, or the
     original weights for the full-precision proxy)."""
@@ -135,7 +143,7 @@ def proxy(x, idx, Wt_up, Wt_gate):
     g = np.empty(d_ff)
     s = np.empty(d_ff)
     _load().prox_oracle_proxy(_p(x), _p(idx), idx.size, _p(Wt_up), _p(Wt_gate),
-                              d_ff, _p(u), _p(g), _p(s))
+                              d_ff, _p(u), _p(g), _p(s), int(act))
     return u, g, s
 
 
@@ -158,7 +166,7 @@ def threshold_mask(z, tau_s: float) -> np.ndarray:
     return sel[:m].copy()
 
 
-def stage2(x, W_up, W_gate, W_down, sel):
+def stage2(x, W_up, W_gate, W_down, sel, act: int = 0):
     """Exact Stage 2 over the selected channels (Sec. 4.1, Stage 2 equations).
 
     Returns (s_sp [k] double, y [d_model] double)."""
@@ -170,19 +178,20 @@ def stage2(x, W_up, W_gate, W_down, sel):
     s_sp = np.zeros(max(1, k))
     y = np.zeros(d_model)
     _load().prox_oracle_stage2(_p(x), d_model, d_ff, _p(W_up), _p(W_gate),
-                               _p(W_down), _p(sel), k, _p(s_sp), _p(y))
+                               _p(W_down), _p(sel), k, _p(s_sp), _p(y), int(act))
     return s_sp[:k].copy(), y
 
 
-def dense(x, W_up, W_gate, W_down):
-    """Dense SwiGLU FFN (Sec. 2.1).  Returns (s [d_ff] double, y [d_model] double)."""
+def dense(x, W_up, W_gate, W_down, act: int = 0):
+    """Dense gated FFN (Sec. 2.1; act 0 SwiGLU, 1 GeGLU).  Returns (s [d_ff]
+    double, y [d_model] double)."""
     x = _f32(x)
     W_up, W_gate, W_down = _f32(W_up), _f32(W_gate), _f32(W_down)
     d_model, d_ff = W_up.shape
     s = np.empty(d_ff)
     y = np.empty(d_model)
     _load().prox_oracle_dense(_p(x), d_model, d_ff, _p(W_up), _p(W_gate),
-                              _p(W_down), _p(s), _p(y))
+                              _p(W_down), _p(s), _p(y), int(act))
     return s, y
 
 
@@ -208,7 +217,8 @@ class Layer:
     """One FFN layer as the oracle sees it: original weights (paper layout,
     float32 values) plus its own INT4 proxy, computed here."""
 
-    def __init__(self, W_up, W_gate, W_down, G: int, full_precision_proxy=False):
+    def __init__(self, W_up, W_gate, W_down, G: int, full_precision_proxy=False, act: int = 0):
+        self.act = int(act)
         self.W_up = _f32(W_up)
         self.W_gate = _f32(W_gate)
         self.W_down = _f32(W_down)
@@ -231,9 +241,9 @@ def forward(layer: Layer, x, tau: float, k: int) -> dict:
     Returns a dict with idx (survivors), u_t/g_t/s_t (proxy), sel, s_sp, y."""
     x = _f32(x)
     idx = input_mask(x, tau)
-    u_t, g_t, s_t = proxy(x, idx, layer.Wt_up, layer.Wt_gate)
+    u_t, g_t, s_t = proxy(x, idx, layer.Wt_up, layer.Wt_gate, layer.act)
     sel = topk(s_t, k)
-    s_sp, y = stage2(x, layer.W_up, layer.W_gate, layer.W_down, sel)
+    s_sp, y = stage2(x, layer.W_up, layer.W_gate, layer.W_down, sel, layer.act)
     return dict(idx=idx, u_t=u_t, g_t=g_t, s_t=s_t, sel=sel, s_sp=s_sp, y=y)
 
 
@@ -243,9 +253,9 @@ def forward_ts(layer: Layer, x, tau_x: float, tau_s: float) -> dict:
     Same dict as forward(); the number of kept channels is sel.size."""
     x = _f32(x)
     idx = input_mask(x, tau_x)
-    u_t, g_t, s_t = proxy(x, idx, layer.Wt_up, layer.Wt_gate)
+    u_t, g_t, s_t = proxy(x, idx, layer.Wt_up, layer.Wt_gate, layer.act)
     sel = threshold_mask(s_t, tau_s)
-    s_sp, y = stage2(x, layer.W_up, layer.W_gate, layer.W_down, sel)
+    s_sp, y = stage2(x, layer.W_up, layer.W_gate, layer.W_down, sel, layer.act)
     return dict(idx=idx, u_t=u_t, g_t=g_t, s_t=s_t, sel=sel, s_sp=s_sp, y=y)
 
 
@@ -317,7 +327,7 @@ def calibrate_sequential(layers, calib_r0, s1: float, s2: float, eps: float = 1e
         tx = lower_quantile(np.abs(X.astype(np.float32)), s1)
         S = []
         for x in X:
-            _, _, s_t = proxy(x, input_mask(x, tx), layer.Wt_up, layer.Wt_gate)
+            _, _, s_t = proxy(x, input_mask(x, tx), layer.Wt_up, layer.Wt_gate, layer.act)
             S.append(np.abs(s_t).astype(np.float32))
         ts = lower_quantile(np.concatenate(S), s2)
         for t, x in enumerate(X):
