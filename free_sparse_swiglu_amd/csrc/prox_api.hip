@@ -52,6 +52,8 @@ prox_status check_shape(const prox_shape *sh) {
                 sh->d_model, sh->d_ff, sh->group_size, sh->max_batch);
   if (sh->dtype != PROX_F32 && sh->dtype != PROX_BF16)
     return fail(PROX_EINVAL, "unknown dtype %d", sh->dtype);
+  if (sh->activation != PROX_ACT_SILU && sh->activation != PROX_ACT_GELU_TANH)
+    return fail(PROX_EINVAL, "unknown activation %d", sh->activation);
   if (sh->d_model % sh->group_size != 0)
     return fail(PROX_EINVAL, "d_model (%d) is not a multiple of group_size (%d)",
                 sh->d_model, sh->group_size);
@@ -81,8 +83,9 @@ prox_status check_shape(const prox_shape *sh) {
 
 namespace prox {
 
-Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch) {
+Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act) {
   Plan p{};
+  p.act = act;
   p.d_model = d_model;
   p.d_ff = d_ff;
   p.G = G;
@@ -238,7 +241,8 @@ prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
   if (!weights_bytes || !proxy_bytes || !workspace_bytes)
     return fail(PROX_EINVAL, "output size pointers must be non-NULL");
   const prox::Plan p = prox::make_plan(shape->d_model, shape->d_ff, shape->group_size,
-                                       shape->dtype == PROX_BF16, shape->max_batch);
+                                       shape->dtype == PROX_BF16, shape->max_batch,
+                                       shape->activation);
   const prox::Layout L = prox::make_layout(p);
   *weights_bytes = L.weights;
   *proxy_bytes = L.proxy;
@@ -266,7 +270,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   prox_layer *L = new (std::nothrow) prox_layer;
   if (!L) return fail(PROX_EINVAL, "out of host memory");
   L->plan = prox::make_plan(shape->d_model, shape->d_ff, shape->group_size,
-                            shape->dtype == PROX_BF16, shape->max_batch);
+                            shape->dtype == PROX_BF16, shape->max_batch, shape->activation);
   const prox::Layout lay = prox::make_layout(L->plan);
   char *wb = (char *)weights_buf, *pb = (char *)proxy_buf, *ws = (char *)workspace_buf;
   prox::Bufs &b = L->bufs;

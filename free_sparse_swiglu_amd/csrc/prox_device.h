@@ -132,6 +132,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Gate activation: SiLU (act 0, SwiGLU) or the tanh form of GELU (act 1,
+// GeGLU), 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float u = 0.7978845608028654f * (z + 0.044715f * z * z * z);
+  return 0.5f * z * (1.0f + tanhf(u));
+}
+__device__ __forceinline__ float gate_act(float z, int act) { return act ? gelu_tanh(z) : silu(z); }
+
 // Reinterpret 32 bits as two bf16 lanes.  (Written with memcpy: a
 // __builtin_bit_cast of a single element of a 4 x u32 vector was folded back
 // to element 0 by the optimizer in this toolchain.)

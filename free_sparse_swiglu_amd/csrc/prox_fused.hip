@@ -86,6 +86,7 @@ struct FusedArgs {
   unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
   unsigned *gmask;  // [n_p3][2] per P3 item: channels above bin b*, channels in it
   int ts_mode;      // 1: Stage 2 mask |s~| >= tau_s instead of top-k (no P2)
+  int act;          // gate activation (gate_act)
   float tau_s;
   int n_p1, n_p2, n_p3, n_p4;
   unsigned long long *trace;  // optional per-ticket timeline (nullptr: off)
@@ -280,7 +281,7 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
     const float gg = xsum_strided(&tp[256 + col], a.nchunk, 512);
     const int j = t * kTile + col;
     if (j < a.d_ff) {
-      const float v = fabsf(u * silu(gg));
+      const float v = fabsf(u * gate_act(gg, a.act));
       xstore(&a.sabs[j], v);
       if (!a.ts_mode) atomicAdd(&h[__float_as_uint(v) >> 20], 1u);
     }
@@ -588,7 +589,7 @@ __device__ __forceinline__ void p3_channel(const FusedArgs &a, const u4 *xs, int
   if (m0 < nstep) p3_pass<BF16, 1>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
   const float u = wave_sum(au);
   const float g = wave_sum(ag);
-  if (lane == 0) xstore(&a.sdense[j], u * silu(g));
+  if (lane == 0) xstore(&a.sdense[j], u * gate_act(g, a.act));
 }
 
 // The i-th set bit (0-based) of a wave-uniform mask, found by all lanes.
@@ -996,6 +997,7 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   FusedArgs a{};
   a.trace = trace;
   a.ts_mode = ts_mode ? 1 : 0;
+  a.act = p.act;
   a.tau_s = tau_s;
   a.pq = b.pq;
   a.psc = b.psc;

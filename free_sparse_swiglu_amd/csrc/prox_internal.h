@@ -56,6 +56,7 @@ struct Plan {
   int nrc;          // row chunks of the down projection
   int upgate_cap;   // max work-groups of the up/gate kernel
   int use_fused;    // batch-1 forwards run the persistent fused kernel
+  int act;          // gate activation: 0 SiLU, 1 GELU (tanh form)
 };
 
 struct Layout {
@@ -65,7 +66,7 @@ struct Layout {
       o_ypart, o_col_cnt, o_sync, o_xbuf, o_ybuf;
 };
 
-Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch);
+Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act);
 Layout make_layout(const Plan &p);
 
 // Kernel launchers (prox_kernels.hip).  Each returns hipSuccess or the launch

@@ -141,6 +141,7 @@ struct ProxyArgs {
   float *part;
   unsigned *tile_cnt;
   float *sabs;
+  int act;  // gate activation (gate_act)
 };
 
 template <int NB, bool BF16>
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(512) void proxy_kernel(ProxyArgs a) {
     const float u = xsum_strided(&tp[(size_t)b * 512 + col], a.nchunk, (size_t)NB * 512);
     const float gg = xsum_strided(&tp[(size_t)b * 512 + 256 + col], a.nchunk, (size_t)NB * 512);
     const int j = t * kTile + col;
-    if (j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(u * silu(gg));
+    if (j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(u * gate_act(gg, a.act));
   }
 }
 
@@ -540,6 +541,7 @@ struct UpGateArgs {
   const int *list;
   const uint8_t *umask;
   float *ssp;
+  int act;  // gate activation (gate_act)
 };
 
 template <int NB, bool BF16, int MODE>
@@ -594,7 +596,7 @@ __global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
       const float u = wave_sum(au[b]);
       const float g = wave_sum(ag[b]);
       if (lane == 0)
-        a.ssp[(size_t)b * a.d_ff + p] = ((tok >> b) & 1u) ? u * silu(g) : 0.0f;
+        a.ssp[(size_t)b * a.d_ff + p] = ((tok >> b) & 1u) ? u * gate_act(g, a.act) : 0.0f;
     }
   }
 }
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(256) void upgate1_kernel(UpGateArgs a, int per) {
     }
     const float u = wave_sum(au);
     const float g = wave_sum(ag);
-    if (lane == 0) a.ssp[p] = u * silu(g);
+    if (lane == 0) a.ssp[p] = u * gate_act(g, a.act);
   }
 }
 
@@ -875,7 +877,7 @@ hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
 hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
                         float tau, hipStream_t s) {
   ProxyArgs a{b.pq, b.psc, x, tau, p.d_model, p.d_ff, p.G, p.ngroups,
-              p.nchunk, b.part, b.tile_cnt, b.sabs};
+              p.nchunk, b.part, b.tile_cnt, b.sabs, p.act};
   dim3 g(p.nchunk, p.ntile);
   if (p.bf16) {
     PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true><<<g, 512, 0, s>>>(a)));
@@ -972,7 +974,7 @@ hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
                          int mode, int n, hipStream_t s) {
   UpGateArgs a{b.wug, (uint32_t)((size_t)p.d_ff * 2 * p.d_model * p.esz), x,
                p.d_model, p.d_ff, n, nullptr,
-               mode == 0 ? b.sel : b.uni, b.umask, b.ssp};
+               mode == 0 ? b.sel : b.uni, b.umask, b.ssp, p.act};
   if (mode == 1) a.n_ptr = b.nuni;
   const int maxn = (mode == 1) ? p.d_ff : n;
   if (maxn <= 0) return hipSuccess;

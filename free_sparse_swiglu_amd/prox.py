@@ -21,6 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "prox.h")
 
 PROX_OK, PROX_EINVAL, PROX_EUNSUPPORTED, PROX_EHIP = 0, -1, -2, -3
 PROX_F32, PROX_BF16 = 0, 1
+PROX_ACT_SILU, PROX_ACT_GELU_TANH = 0, 1
 _STATUS = {0: "PROX_OK", -1: "PROX_EINVAL", -2: "PROX_EUNSUPPORTED", -3: "PROX_EHIP"}
 
 
@@ -33,7 +34,7 @@ class ProxError(RuntimeError):
 class prox_shape(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int), ("d_ff", ctypes.c_int),
                 ("group_size", ctypes.c_int), ("dtype", ctypes.c_int),
-                ("max_batch", ctypes.c_int)]
+                ("max_batch", ctypes.c_int), ("activation", ctypes.c_int)]
 
 
 class prox_debug(ctypes.Structure):
@@ -123,9 +124,10 @@ def prox_last_error() -> str:
     return msg.decode() if msg else ""
 
 
-def prox_query_sizes(d_model: int, d_ff: int, group_size: int, dtype, max_batch: int = 1):
+def prox_query_sizes(d_model: int, d_ff: int, group_size: int, dtype, max_batch: int = 1,
+                     activation: int = 0):
     """(weights_bytes, proxy_bytes, workspace_bytes) for a layer shape."""
-    sh = prox_shape(d_model, d_ff, group_size, _dtype_code(dtype), max_batch)
+    sh = prox_shape(d_model, d_ff, group_size, _dtype_code(dtype), max_batch, activation)
     w, p, ws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(load_library().prox_query_sizes(ctypes.byref(sh), ctypes.byref(w),
                                            ctypes.byref(p), ctypes.byref(ws)))
@@ -159,10 +161,11 @@ class Layer:
 
 
 def prox_prepare_layer(w_up, w_gate, w_down, group_size: int, max_batch: int = 1,
-                       workspace=None) -> Layer:
+                       workspace=None, activation: int = 0) -> Layer:
     """Relayout and quantize one layer (weights in the x.W layout, on the GPU).
 
-    A workspace tensor may be shared by layers that run on one stream."""
+    A workspace tensor may be shared by layers that run on one stream.
+    activation: PROX_ACT_SILU (SwiGLU, default) or PROX_ACT_GELU_TANH (GeGLU)."""
     d_model, d_ff = w_up.shape
     dt = _dtype_code(w_up.dtype)
     for t in (w_up, w_gate, w_down):
@@ -170,13 +173,13 @@ def prox_prepare_layer(w_up, w_gate, w_down, group_size: int, max_batch: int = 1
             raise ProxError(PROX_EINVAL, "weights must be contiguous CUDA tensors of one dtype")
     if tuple(w_gate.shape) != (d_model, d_ff) or tuple(w_down.shape) != (d_ff, d_model):
         raise ProxError(PROX_EINVAL, "weight shapes do not match")
-    wb, pb, wsb = prox_query_sizes(d_model, d_ff, group_size, w_up.dtype, max_batch)
+    wb, pb, wsb = prox_query_sizes(d_model, d_ff, group_size, w_up.dtype, max_batch, activation)
     dev = w_up.device
     weights = torch.empty(wb, dtype=torch.uint8, device=dev)
     proxy = torch.empty(pb, dtype=torch.uint8, device=dev)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    sh = prox_shape(d_model, d_ff, group_size, dt, max_batch)
+    sh = prox_shape(d_model, d_ff, group_size, dt, max_batch, activation)
     h = ctypes.c_void_p()
     _check(load_library().prox_prepare_layer(
         ctypes.byref(sh), _ptr(w_up), _ptr(w_gate), _ptr(w_down), _ptr(weights),

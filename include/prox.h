@@ -49,6 +49,13 @@ typedef enum {
 
 typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
 
+/* Gate activation of the gated FFN: SwiGLU, SiLU(z) = z / (1 + e^-z) (the
+ * pages' FFN, Sec. 2.1), or GeGLU with the tanh form of GELU,
+ * 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) (Gemma-3 style models,
+ * evaluated in Sec. 5).  Both the proxy state s~ and the exact state s use
+ * the layer's activation.                                                  */
+typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
+
 /* Shape of one FFN layer.
  *   d_model     input/output width, at most 16384, a multiple of group_size
  *               and of 512 (bf16) or 256 (f32); batch * d_model activations
@@ -63,6 +70,7 @@ typedef struct {
   int group_size;
   int dtype;
   int max_batch;
+  int activation;    /* prox_activation (0: SiLU, the default)            */
 } prox_shape;
 
 /* Opaque host-side handle: shape, launch plan and the caller's buffers. */

@@ -63,6 +63,19 @@ def test_query_sizes_rejects(lib, args, status):
     assert prox.prox_last_error() != ""
 
 
+def test_query_sizes_activation(lib):
+    for act in (prox.PROX_ACT_SILU, prox.PROX_ACT_GELU_TANH):
+        sh = prox.prox_shape(1024, 2816, 128, prox.PROX_BF16, 1, act)
+        w, p, ws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        assert lib.prox_query_sizes(ctypes.byref(sh), ctypes.byref(w), ctypes.byref(p),
+                                    ctypes.byref(ws)) == prox.PROX_OK
+    sh = prox.prox_shape(1024, 2816, 128, prox.PROX_BF16, 1, 2)
+    w, p, ws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.prox_query_sizes(ctypes.byref(sh), ctypes.byref(w), ctypes.byref(p),
+                                ctypes.byref(ws)) == prox.PROX_EINVAL
+    assert "activation" in prox.prox_last_error()
+
+
 def test_query_sizes_rejects_batch(lib):
     assert _q(4096, 14336, 128, prox.PROX_BF16, 9)[0] == prox.PROX_EUNSUPPORTED
     assert _q(4096, 14336, 128, prox.PROX_BF16, 0)[0] == prox.PROX_EINVAL

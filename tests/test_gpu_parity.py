@@ -37,13 +37,14 @@ def _tol(cfg):
 class Case:
     """A layer on both sides: GPU prepared layer + oracle layer (+ dense s)."""
 
-    def __init__(self, cfg, layer=0, gen_device="cpu", max_batch=1):
+    def __init__(self, cfg, layer=0, gen_device="cpu", max_batch=1, act=0):
         self.cfg = cfg
+        self.act = act
         W = synth.make_layer(cfg, layer, gen_device)
         self.Wg_dev = [w.to(DEV) for w in W]
-        self.L = prox.prox_prepare_layer(*self.Wg_dev, cfg.group, max_batch)
+        self.L = prox.prox_prepare_layer(*self.Wg_dev, cfg.group, max_batch, activation=act)
         self.Wnp = [w.float().cpu().numpy() for w in W]
-        self.ol = oracle.Layer(*self.Wnp, cfg.group)
+        self.ol = oracle.Layer(*self.Wnp, cfg.group, act=act)
         calib = synth.make_inputs(cfg, cfg.n_calib, "calib", layer, gen_device)
         self.tau = synth.calibrate_tau(calib, cfg.tau_quantile)
 
@@ -54,13 +55,13 @@ class Case:
 _CASES = {}
 
 
-def get_case(cfg, gen_device="cpu", max_batch=1):
-    key = (cfg, gen_device, max_batch)
+def get_case(cfg, gen_device="cpu", max_batch=1, act=0):
+    key = (cfg, gen_device, max_batch, act)
     if key not in _CASES:
         if cfg.d_model >= 4096:  # keep at most one full-size layer alive
             for k2 in [k for k in _CASES if k[0].d_model >= 4096]:
                 del _CASES[k2]
-        _CASES[key] = Case(cfg, 0, gen_device, max_batch)
+        _CASES[key] = Case(cfg, 0, gen_device, max_batch, act)
     return _CASES[key]
 
 
@@ -85,7 +86,7 @@ def _check_token(case, x_row_dev, x_np, tau, k, out, t=0, stats=None):
         assert not np.any(s_abs)
     sel = out["sel"][t, :k].cpu().numpy()
     m = check_mask(sel, ref["sel"], ref["s_t"], k)
-    s_exact, _ = oracle.dense(x_np, *case.Wnp)
+    s_exact, _ = oracle.dense(x_np, *case.Wnp, act=case.act)
     y_ref = expected_y(sel, ref["sel"], ref["y"], s_exact, case.Wnp[2])
     e_y = rel_err(y, y_ref)
     assert e_y <= _tol(cfg), f"y error {e_y:.3e} (k={k}, tau={tau})"
@@ -363,7 +364,7 @@ def _check_ts(case, xd, x_np, tau_x, tau_s, out, stats=None):
     if m == 0:
         assert ref["sel"].size == 0 and not np.any(y)
         return
-    s_exact, _ = oracle.dense(x_np, *case.Wnp)
+    s_exact, _ = oracle.dense(x_np, *case.Wnp, act=case.act)
     s_sel = out["s_sel"][0, :m].cpu().numpy().astype(np.float64)
     assert rel_err(s_sel, s_exact[sel]) <= 1e-4
     y_ref = expected_y(sel, ref["sel"], ref["y"], s_exact, case.Wnp[2])
@@ -488,3 +489,31 @@ def test_stack_ts_parity_and_runtime_sparsity():
     e_or = costmodel.effective_sparsity(1 - n1s / (3 * 4 * STACK_SMALL.d_model),
                                         1 - nss / (3 * 4 * STACK_SMALL.d_ff))
     assert abs(rs["e"] - e_or) <= 0.01, (rs, e_or)
+
+
+
+# ---------------------------------------------------------------------------
+# GeGLU (tanh-form GELU gate) instead of SwiGLU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "ragged", "8b"])
+def test_geglu_parity(name):
+    cfg = RAGGED if name == "ragged" else synth.CONFIGS[name]
+    gen = DEV if name == "8b" else "cpu"
+    case = get_case(cfg, gen, 1, act=prox.PROX_ACT_GELU_TANH)
+    k = synth.k_for(cfg.d_ff, 0.7)
+    X = synth.make_inputs(cfg, 3, "geglu", 0, gen)
+    for t in range(X.shape[0]):
+        xd = X[t:t + 1].to(DEV)
+        x_np = X[t].float().cpu().numpy()
+        out = prox.prox_ffn_forward_debug(case.L, xd, case.tau, k)
+        torch.cuda.synchronize()
+        _check_token(case, xd, x_np, case.tau, k, out)
+        s_t = oracle.forward(case.ol, x_np, case.tau, 1)["s_t"]
+        tau_s = float(np.quantile(np.abs(s_t), 0.7))
+        out = prox.prox_ffn_forward_ts_debug(case.L, xd, case.tau, tau_s)
+        torch.cuda.synchronize()
+        _check_ts(case, xd, x_np, case.tau, tau_s, out)
+    y = prox.prox_dense_ffn_forward(case.L, X[:1].to(DEV))
+    torch.cuda.synchronize()
+    _, y_ref = oracle.dense(X[0].float().cpu().numpy(), *case.Wnp, act=case.act)
+    assert rel_err(y[0].float().cpu().numpy(), y_ref) <= _tol(cfg)
