@@ -18,8 +18,10 @@ baseline on the same relaid weights, and the CPU oracle timed on the host
 cores.
 
 Other workloads (--workload): 14b (k at 70%), 70b (batch 1/2/4/8), stack8b
-(32 layers x 128 sequential tokens, tokens/s), copy (a plain device copy of
-known size, used to scale rocprofv3 byte counters).
+(32 layers x 128 sequential tokens, tokens/s; top-k and the calibrated
+threshold mode), alpha (INT4 proxy GEMV over bf16 input-sparse GEMV time, the
+alpha of the allocation model), copy (a plain device copy of known size, used
+to scale rocprofv3 byte counters).
 """
 from __future__ import annotations
 
@@ -76,9 +78,10 @@ def algorithmic_bytes(cfg, n1, groups_touched, k, batch=1, union=None):
                 total=stage1 + upgate + down + io)
 
 
-def build_ring(cfg, ring, max_batch=1, path=None):
+def build_ring(cfg, ring, max_batch=1, path=None, activation=0):
     """Prepare `ring` seeded layers sharing one workspace.  path="multi"
-    prepares them for the multi-kernel path (one kernel per phase)."""
+    prepares them for the multi-kernel path (one kernel per phase);
+    activation 1 makes them GeGLU layers."""
     import torch
 
     from free_sparse_swiglu_amd import prox, synth
@@ -89,7 +92,8 @@ def build_ring(cfg, ring, max_batch=1, path=None):
         os.environ["PROX_PATH"] = path
     for l in range(ring):
         W = synth.make_layer(cfg, l, "cuda")
-        L = prox.prox_prepare_layer(*W, cfg.group, max_batch, workspace=ws)
+        L = prox.prox_prepare_layer(*W, cfg.group, max_batch, workspace=ws,
+                                    activation=activation)
         ws = L.workspace
         torch.cuda.synchronize()
         del W
@@ -256,6 +260,39 @@ def bench_single_layer(args, name):
     mkms = profile_kernels(mpstep, min(args.steps, 200), 6)
     del mlayers
     torch.cuda.synchronize()
+    # The Stage 2 threshold mask (Sec. 4.1) instead of top-k: tau_s per layer
+    # is the 0.7 quantile of |s~| over 32 calibration inputs of the layer, so
+    # about 30% of the channels are kept, as with k = 30% of d_ff.
+    from free_sparse_swiglu_amd import calibrate
+    tss = []
+    for l in range(R):
+        xc = synth.make_inputs(cfg, 32, "calib", l, "cuda")
+        S = torch.empty(32, cfg.d_ff, device="cuda")
+        for t in range(32):
+            calibrate._abs_proxy_state(layers[l], xc[t:t + 1], taus[l], S[t], y[None])
+        tss.append(synth.calibrate_tau(S, 0.7))
+
+    def tstep(i):
+        l = i % R
+        prox.prox_ffn_forward_ts(layers[l], X[l][(i // R) % NX], taus[l], tss[l], y)
+    tms = time_loop(tstep, args.steps, args.warmup)
+    kept = []
+    for l in range(R):
+        for t in range(NX):
+            o = prox.prox_ffn_forward_ts_debug(layers[l], X[l][t:t + 1], taus[l], tss[l])
+            kept.append(int(o["n_sel"][0]))
+    mkept = float(np.mean(kept))
+    tbytes = algorithmic_bytes(cfg, n1m, gtm, mkept)["total"]
+
+    # The same step on GeGLU layers (tanh-form GELU gate), same weights.
+    glayers, _ = build_ring(cfg, R, activation=1)
+
+    def gstep(i):
+        l = i % R
+        prox.prox_ffn_forward(glayers[l], X[l][(i // R) % NX], taus[l], k, y)
+    gms = time_loop(gstep, args.steps, args.warmup)
+    del glayers
+    torch.cuda.synchronize()
     kbytes = dict(stage1_proxy=ab["stage1"] + cfg.d_model * 2, topk=None,
                   stage2_upgate=ab["upgate"] + cfg.d_model * 2, stage2_down=ab["down"])
     mkern = {}
@@ -299,6 +336,11 @@ def bench_single_layer(args, name):
                     bytes_per_step=int(ab["total"])),
         kernels=kern,
         multi_kernel_path=dict(us_per_layer=round(mms * 1e3, 2), kernels=mkern),
+        threshold_mask=dict(us_per_layer=round(tms * 1e3, 2), mean_kept=round(mkept, 1),
+                            GBps=round(tbytes / (tms * 1e-3) / 1e9, 1),
+                            speedup_vs_dense=round(dms / tms, 3)),
+        geglu=dict(us_per_layer=round(gms * 1e3, 2),
+                   GBps=round(ab["total"] / (gms * 1e-3) / 1e9, 1)),
         dense=dict(us_per_layer=round(dms * 1e3, 2),
                    GBps=round(3 * cfg.d_model * cfg.d_ff * 2 / (dms * 1e-3) / 1e9, 1),
                    kernels=dict(upgate_us=round(dkms[0] * 1e3, 2), down_us=round(dkms[1] * 1e3, 2))),
@@ -418,6 +460,71 @@ def bench_stack(args):
                 threshold_mode=threshold_mode)
 
 
+def bench_alpha(args):
+    """alpha of the allocation model (Sec. 4.2; App. A.3 measures it on NVIDIA
+    GPUs): the INT4 proxy GEMV time over the bf16 input-sparse GEMV time at
+    the same input sparsity s1, both for the up and gate projections of one
+    token.  INT4: prox_stage1 (Stage 1 kernel, activation epilogue included);
+    bf16: prox_sparse_gemv on the layer's row-major bf16 weights."""
+    import numpy as np
+    import torch
+
+    from free_sparse_swiglu_amd import prox, synth
+    out = {}
+    R = 4
+    for name in ("8b", "14b", "70b"):
+        cfg = synth.CONFIGS[name]
+        Ws, layers = [], []
+        ws = None
+        for l in range(R):
+            W = synth.make_layer(cfg, l, "cuda")
+            L = prox.prox_prepare_layer(*W, cfg.group, 1, workspace=ws)
+            ws = L.workspace
+            Ws.append((W[0], W[1]))
+            del W
+            layers.append(L)
+        torch.cuda.synchronize()
+        gws = prox.prox_sparse_gemv_workspace(cfg.d_model, cfg.d_ff)
+        u = torch.empty(cfg.d_ff, device="cuda")
+        g = torch.empty(cfg.d_ff, device="cuda")
+        X = [synth.make_inputs(cfg, 8, "bench", l, "cuda") for l in range(R)]
+        calib = [synth.make_inputs(cfg, 64, "calib", l, "cuda") for l in range(R)]
+        rows = {}
+        for s1 in (0.4, 0.5, 0.6, 0.7):
+            taus = [synth.calibrate_tau(calib[l], s1) for l in range(R)]
+            n1 = [float((X[l].abs() >= taus[l]).sum(dim=1).float().mean()) for l in range(R)]
+
+            def i4(i):
+                prox.prox_stage1(layers[i % R], X[i % R][(i // R) % 8], taus[i % R])
+
+            def bf(i):
+                l = i % R
+                prox.prox_sparse_gemv(Ws[l][0], Ws[l][1], X[l][(i // R) % 8], taus[l], gws, u, g)
+            t4 = time_loop(i4, args.steps, args.warmup)
+            tb = time_loop(bf, args.steps, args.warmup)
+            m = float(np.mean(n1))
+            rows[f"s1={s1}"] = dict(
+                realized_s1=round(1 - m / cfg.d_model, 4),
+                int4_us=round(t4 * 1e3, 2), bf16_us=round(tb * 1e3, 2),
+                alpha=round(t4 / tb, 3),
+                int4_GBps=round(m * cfg.d_ff / (t4 * 1e-3) / 1e9, 1),
+                bf16_GBps=round(m * cfg.d_ff * 4 / (tb * 1e-3) / 1e9, 1))
+        out[name] = rows
+        del layers, Ws, X, calib
+        torch.cuda.synchronize()
+    alphas = [r["alpha"] for rows in out.values() for r in rows.values()]
+    return dict(metric="alpha = INT4 proxy GEMV time / bf16 input-sparse GEMV time, "
+                       "batch 1, same input sparsity",
+                value=round(float(np.mean(alphas)), 3), unit="ratio", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, higher_is_better=False, dtype="bf16",
+                data="synthetic",
+                config=dict(workload="up+gate GEMVs of 8B/14B/70B-shaped layers at s1 = 0.4, "
+                                     "0.5, 0.6, 0.7", ring_layers=R),
+                pages_alpha=dict(model_value=1 / 3, measured_range=[0.234, 0.351],
+                                 pooled_mean=0.285),
+                shapes=out)
+
+
 def bench_copy(args):
     import torch
     n = 1 << 30
@@ -434,7 +541,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="8b", choices=["8b", "14b", "70b", "stack8b", "copy"])
+    ap.add_argument("--workload", default="8b",
+                    choices=["8b", "14b", "70b", "stack8b", "alpha", "copy"])
     ap.add_argument("--sparsity", type=float, default=0.7)
     ap.add_argument("--ring", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -455,6 +563,8 @@ def main():
         res = bench_batch(args)
     elif args.workload == "stack8b":
         res = bench_stack(args)
+    elif args.workload == "alpha":
+        res = bench_alpha(args)
     else:
         res = bench_copy(args)
     print(json.dumps(res), flush=True)

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libprox.so")
-SOURCES = ["prox_kernels.hip", "prox_fused.hip", "prox_api.hip"]
+SOURCES = ["prox_kernels.hip", "prox_fused.hip", "prox_sgemv.hip", "prox_api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -451,6 +451,47 @@ prox_status prox_ffn_forward_ts_debug(const prox_layer *layer, const void *x, fl
   return PROX_OK;
 }
 
+prox_status prox_stage1(const prox_layer *layer, const void *x, float threshold, float *s_abs,
+                        void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, 1, threshold, 0, x);
+  if (st != PROX_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = prox::launch_proxy(layer->plan, layer->bufs, x, 1, threshold, s);
+  if (e != hipSuccess) return hip_fail(e, "stage 1 proxy kernel");
+  if (s_abs && (e = hipMemcpyAsync(s_abs, layer->bufs.sabs, (size_t)layer->plan.d_ff * 4,
+                                   hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return hip_fail(e, "copy |s~|");
+  return PROX_OK;
+}
+
+size_t prox_sparse_gemv_workspace_bytes(int d_model, int d_ff) {
+  if (d_model <= 0 || d_ff <= 0) return 0;
+  return prox::sgemv_workspace_bytes(d_model, d_ff);
+}
+
+prox_status prox_sparse_gemv(const void *w_up, const void *w_gate, int d_model, int d_ff,
+                             const void *x, float threshold, float *u, float *g, void *workspace,
+                             void *stream) {
+  g_err.clear();
+  if (!w_up || !w_gate || !x || !u || !g || !workspace)
+    return fail(PROX_EINVAL, "all pointers are required");
+  if (d_model <= 0 || d_model % 64 != 0 || d_model > prox::kMaxDmodel)
+    return fail(PROX_EINVAL, "d_model must be a positive multiple of 64, at most %d",
+                prox::kMaxDmodel);
+  if (d_ff <= 0 || d_ff % 8 != 0 || d_ff > prox::kMaxDff)
+    return fail(PROX_EINVAL, "d_ff must be a positive multiple of 8, at most %d", prox::kMaxDff);
+  if ((size_t)d_model * d_ff * 2 > 0xffffffffull)
+    return fail(PROX_EUNSUPPORTED, "one weight matrix must be below 4 GiB");
+  if (isnan(threshold)) return fail(PROX_EINVAL, "threshold is NaN");
+  if (!aligned(w_up, 16) || !aligned(w_gate, 16) || !aligned(x, 16) || !aligned(workspace, 256))
+    return fail(PROX_EINVAL, "weights and x must be 16-byte, workspace 256-byte aligned");
+  hipError_t e = prox::launch_sgemv(w_up, w_gate, d_model, d_ff, x, threshold, u, g, workspace,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse gemv kernel");
+  return PROX_OK;
+}
+
 prox_status prox_dense_ffn_forward(const prox_layer *layer, const void *x, int batch,
                                    void *y, void *stream) {
   g_err.clear();

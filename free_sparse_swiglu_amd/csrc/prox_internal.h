@@ -105,6 +105,11 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
                         bool ts_mode = false, float tau_s = 0.0f);
 int fused_items(const Plan &p, bool ts_mode);
 int fused_p3_items(const Plan &p);
+
+// Input-sparse bf16 GEMV of the up and gate projections (prox_sgemv.hip).
+size_t sgemv_workspace_bytes(int d_model, int d_ff);
+hipError_t launch_sgemv(const void *w_up, const void *w_gate, int d_model, int d_ff, const void *x,
+                        float tau, float *u, float *g, void *workspace, hipStream_t s);
 // After a fused forward: the ascending kept-channel list and its exact s (at
 // most cap entries each; ssel and count may be null; count gets the number
 // of kept channels).

@@ -74,6 +74,9 @@ def load_library(path: str = LIB_PATH):
                                              ctypes.POINTER(I), P], I),
         "prox_ffn_forward_traced": ([P, P, F, I, P, P, I, ctypes.POINTER(I), P], I),
         "prox_ffn_forward_ts": ([P, P, F, F, P, P], I),
+        "prox_stage1": ([P, P, F, P, P], I),
+        "prox_sparse_gemv_workspace_bytes": ([I, I], ctypes.c_size_t),
+        "prox_sparse_gemv": ([P, P, I, I, P, F, P, P, P, P], I),
         "prox_stack_forward_ts": ([ctypes.POINTER(P), I, ctypes.POINTER(F), ctypes.POINTER(F), P,
                                    F, P], I),
         "prox_ffn_forward_ts_debug": ([P, P, F, F, P, ctypes.POINTER(prox_debug), P], I),
@@ -93,7 +96,7 @@ def header_symbols(path: str = HEADER_PATH):
     """Names of the functions include/prox.h declares."""
     with open(path) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:prox_status|void|const char \*)\s*(prox_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:prox_status|void|size_t|const char \*)\s*(prox_\w+)\s*\(",
                                  text, re.M)))
 
 
@@ -349,3 +352,28 @@ def prox_stack_forward_ts(layers, thresholds_x, thresholds_s, resid, eps: float 
     ts = (ctypes.c_float * n)(*[float(t) for t in thresholds_s])
     _check(load_library().prox_stack_forward_ts(arr, n, tx, ts, _ptr(resid), float(eps), _stream()))
     return resid
+
+
+def prox_stage1(layer: Layer, x, threshold: float, s_abs=None):
+    """Stage 1 alone for one token; returns s_abs (or None when not asked)."""
+    _check(load_library().prox_stage1(layer.handle, _ptr(x), float(threshold), _ptr(s_abs),
+                                      _stream()))
+    return s_abs
+
+
+def prox_sparse_gemv_workspace(d_model: int, d_ff: int, device="cuda"):
+    n = load_library().prox_sparse_gemv_workspace_bytes(int(d_model), int(d_ff))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def prox_sparse_gemv(w_up, w_gate, x, threshold: float, workspace, u=None, g=None):
+    """Input-sparse bf16 GEMV: (u, g) = x_S W_up, x_S W_gate over |x_i| >= threshold."""
+    d_model, d_ff = w_up.shape
+    if u is None:
+        u = torch.empty(d_ff, dtype=torch.float32, device=x.device)
+    if g is None:
+        g = torch.empty(d_ff, dtype=torch.float32, device=x.device)
+    _check(load_library().prox_sparse_gemv(_ptr(w_up), _ptr(w_gate), int(d_model), int(d_ff),
+                                           _ptr(x), float(threshold), _ptr(u), _ptr(g),
+                                           _ptr(workspace), _stream()))
+    return u, g

@@ -242,6 +242,29 @@ prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x,
                                    unsigned long long *trace, int trace_items,
                                    int *counts, void *stream);
 
+/* Stage 1 alone (Sec. 4.1: input mask |x_i| >= threshold and the INT4 proxy
+ * GEMV of W_up and W_gate with the activation epilogue) for one token, on
+ * the multi-kernel path's Stage 1 kernel.  s_abs (device float [d_ff]) may be
+ * NULL: the result then stays in the layer workspace.  Used to time the INT4
+ * proxy GEMV against prox_sparse_gemv (the ratio alpha of Sec. 4.2).        */
+prox_status prox_stage1(const prox_layer *layer, const void *x, float threshold,
+                        float *s_abs, void *stream);
+
+/* Input-sparse bf16 GEMV of both gate projections, the full-precision
+ * counterpart of Stage 1 (the FP16 GEMV at the same input sparsity that
+ * App. A.3 times against the INT4 proxy):
+ *   u_j = sum over i with |x_i| >= threshold of x_i W_up[i][j], likewise g,
+ * float32 accumulation.  w_up, w_gate: bf16 [d_model][d_ff] row-major (x.W
+ * layout, the caller's tensors, read in place); x bf16 [d_model]; u, g float
+ * [d_ff].  d_model a multiple of 64 (<= 16384), d_ff a multiple of 8
+ * (<= 32768).  workspace: device, 256-byte aligned,
+ * prox_sparse_gemv_workspace_bytes(d_model, d_ff) bytes, zeroed before its
+ * first use (every call leaves it zeroed); calls sharing it must not overlap. */
+size_t prox_sparse_gemv_workspace_bytes(int d_model, int d_ff);
+prox_status prox_sparse_gemv(const void *w_up, const void *w_gate, int d_model,
+                             int d_ff, const void *x, float threshold, float *u,
+                             float *g, void *workspace, void *stream);
+
 /* Release a handle (host memory only; the caller's buffers are untouched). */
 void prox_destroy_layer(prox_layer *layer);
 

@@ -517,3 +517,44 @@ def test_geglu_parity(name):
     torch.cuda.synchronize()
     _, y_ref = oracle.dense(X[0].float().cpu().numpy(), *case.Wnp, act=case.act)
     assert rel_err(y[0].float().cpu().numpy(), y_ref) <= _tol(cfg)
+
+
+# ---------------------------------------------------------------------------
+# The alpha measurement pair: Stage 1 alone and the input-sparse bf16 GEMV
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["ragged", "8b"])
+def test_sparse_gemv_parity(name):
+    """u, g = x_S W_up, x_S W_gate over |x_i| >= tau: the oracle's proxy step
+    with the original weights as proxy weights computes exactly that."""
+    cfg = RAGGED if name == "ragged" else synth.CONFIGS[name]
+    gen = DEV if name == "8b" else "cpu"
+    case = get_case(cfg, gen)
+    Wu, Wg = case.Wg_dev[0], case.Wg_dev[1]
+    Wu64 = case.Wnp[0].astype(np.float64)
+    Wg64 = case.Wnp[1].astype(np.float64)
+    ws = prox.prox_sparse_gemv_workspace(cfg.d_model, cfg.d_ff)
+    X = synth.make_inputs(cfg, 2, "sgemv", 0, gen)
+    for t in range(X.shape[0]):
+        x_np = X[t].float().cpu().numpy()
+        for tau in (case.tau, 0.0, float("inf")):
+            for _ in range(2):  # the workspace is left ready for the next call
+                u, g = prox.prox_sparse_gemv(Wu, Wg, X[t].to(DEV), tau, ws)
+                torch.cuda.synchronize()
+            idx = oracle.input_mask(x_np, tau)
+            u_r, g_r, _ = oracle.proxy(x_np, idx, Wu64, Wg64)
+            if idx.size == 0:
+                assert not torch.any(u) and not torch.any(g)
+                continue
+            assert rel_err(u.cpu().numpy(), u_r) <= 1e-4
+            assert rel_err(g.cpu().numpy(), g_r) <= 1e-4
+
+
+def test_stage1_entry_matches_oracle():
+    case = get_case(RAGGED)
+    X = case.inputs(2, "stage1")
+    out = torch.empty(RAGGED.d_ff, device=DEV)
+    for t in range(X.shape[0]):
+        prox.prox_stage1(case.L, X[t].to(DEV), case.tau, out)
+        torch.cuda.synchronize()
+        ref = oracle.forward(case.ol, X[t].float().numpy(), case.tau, 1)["s_t"]
+        assert rel_err(out.cpu().numpy(), np.abs(ref)) <= 1e-4
