@@ -59,7 +59,7 @@ constexpr int kWaveCand = 256;     // top-k candidates per wave held in LDS (fas
 constexpr int kMaxPer = 64;        // key slots per thread: d_ff <= 64 * 512
 constexpr int kGroups = kMaxPer * kFW;  // groups of 64 channels: d_ff <= 512 * 64
 constexpr int kKC = 32;            // key slots loaded per round of a select pass
-constexpr int kP3Ch = 32;          // channels per P3 item
+constexpr int kP3Ch = 32;          // channels per P3 item (at most 64: one per lane of a mask)
 constexpr int kP4Ch = 512;         // channels per P4 item (kP4Ch / kP3Ch P3 items)
 constexpr int kSelBits = 16;       // buffer-load aux bit: sc1 (agent-coherent)
 
@@ -84,7 +84,8 @@ struct FusedArgs {
   unsigned *sync;
   unsigned *tflag;  // per P1 tile: |s~| written (word t * kSyncStride)
   unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
-  unsigned *gmask;  // [n_p3][2] per P3 item: channels above bin b*, channels in it
+  unsigned *gmask;  // [n_p3][4] per P3 item: 64-bit masks of the channels above bin b*
+                    // and of those in it (low word first)
   int ts_mode;      // 1: Stage 2 mask |s~| >= tau_s instead of top-k (no P2)
   int act;          // gate activation (gate_act)
   float tau_s;
@@ -131,6 +132,7 @@ struct P2Smem {
 };
 struct P3Smem {
   u4 x[2048];  // x when d_model * element size <= 32 KB
+  float ured[2 * kP3Ch];  // dot product of each unit (row) of the item
   unsigned bstar;
 };
 struct P4Smem {
@@ -533,25 +535,26 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
 // elements), dot2 with x, s = u * SiLU(g), stored by channel.  The kept
 // channels are dealt to the 8 waves in ascending order.
 // ---------------------------------------------------------------------------
-// CH 16-byte steps of both rows in flight, then their dot products with x
-// (from LDS when xs is given, else from global memory).
-template <bool BF16, int CH>
+// CH 16-byte steps of ROWS rows (byte offsets base0, base1 in the up/gate
+// weights) in flight, then their dot products with x (from LDS when xs is
+// given, else from global memory).
+template <bool BF16, int CH, int ROWS>
 __device__ __forceinline__ void p3_pass(const FusedArgs &a, const u4 *xs, __amdgpu_buffer_rsrc_t rs,
-                                        uint32_t ubase, uint32_t rowb, int m0, int lane, float &au,
-                                        float &ag) {
-  u4 wu[CH], wg[CH];
+                                        uint32_t base0, uint32_t base1, int m0, int lane,
+                                        float &acc0, float &acc1) {
+  u4 w0[CH], w1[CH];
 #pragma unroll
   for (int m = 0; m < CH; ++m) {
     const uint32_t off = (uint32_t)((m0 + m) * 64 + lane) * 16u;
-    wu[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase, kNT);
-    wg[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, ubase + rowb, kNT);
+    w0[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, base0, kNT);
+    if (ROWS == 2) w1[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, base1, kNT);
   }
   if (xs) {
 #pragma unroll
     for (int m = 0; m < CH; ++m) {
       const u4 xr = xs[(m0 + m) * 64 + lane];
-      au = dot16<BF16>(wu[m], xr, au);
-      ag = dot16<BF16>(wg[m], xr, ag);
+      acc0 = dot16<BF16>(w0[m], xr, acc0);
+      if (ROWS == 2) acc1 = dot16<BF16>(w1[m], xr, acc1);
     }
   } else {
     u4 xr[CH];
@@ -560,36 +563,35 @@ __device__ __forceinline__ void p3_pass(const FusedArgs &a, const u4 *xs, __amdg
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < CH; ++m) {
-      au = dot16<BF16>(wu[m], xr[m], au);
-      ag = dot16<BF16>(wg[m], xr[m], ag);
+      acc0 = dot16<BF16>(w0[m], xr[m], acc0);
+      if (ROWS == 2) acc1 = dot16<BF16>(w1[m], xr[m], acc1);
     }
   }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void p3_channel(const FusedArgs &a, const u4 *xs, int j, int lane) {
-  constexpr int ESZ = BF16 ? 2 : 4;
+// Dot products of x with one or two whole rows of the up/gate weights.  One
+// 16-byte step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a
+// multiple of 1024, so the steps tile the row exactly.  With x in LDS a pass
+// holds 8 steps of two rows (16 KB per wave in flight); with x in registers 4.
+template <bool BF16, int ROWS>
+__device__ __forceinline__ void p3_rows(const FusedArgs &a, const u4 *xs, uint32_t base0,
+                                        uint32_t base1, int lane, float &r0, float &r1) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
-  const uint32_t rowb = (uint32_t)a.d_model * ESZ;
-  const uint32_t ubase = (uint32_t)j * 2u * rowb;
-  // One 16-byte step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a
-  // multiple of 1024, so the steps tile the row exactly.  With x in LDS a
-  // pass holds 8 steps of both rows (16 KB per wave in flight); with x in
-  // registers 4 (8 would spill).
-  const int nstep = (int)(rowb >> 10);
-  float au = 0.0f, ag = 0.0f;
+  const int nstep = (int)(((uint32_t)a.d_model * (BF16 ? 2u : 4u)) >> 10);
+  float acc0 = 0.0f, acc1 = 0.0f;
   int m0 = 0;
   if (xs)
-    for (; m0 + 8 <= nstep; m0 += 8) p3_pass<BF16, 8>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
-  for (; m0 + 4 <= nstep; m0 += 4) p3_pass<BF16, 4>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
+    for (; m0 + 8 <= nstep; m0 += 8)
+      p3_pass<BF16, 8, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
+  for (; m0 + 4 <= nstep; m0 += 4)
+    p3_pass<BF16, 4, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
   if (m0 + 2 <= nstep) {
-    p3_pass<BF16, 2>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
+    p3_pass<BF16, 2, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
     m0 += 2;
   }
-  if (m0 < nstep) p3_pass<BF16, 1>(a, xs, rs, ubase, rowb, m0, lane, au, ag);
-  const float u = wave_sum(au);
-  const float g = wave_sum(ag);
-  if (lane == 0) xstore(&a.sdense[j], u * gate_act(g, a.act));
+  if (m0 < nstep) p3_pass<BF16, 1, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
+  r0 = wave_sum(acc0);
+  r1 = ROWS == 2 ? wave_sum(acc1) : 0.0f;
 }
 
 // The i-th set bit (0-based) of a wave-uniform mask, found by all lanes.
@@ -640,10 +642,39 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
     __syncthreads();
     xs = sm.x;
   }
-  for (int i = wv; i < nc; i += kFW) p3_channel<BF16>(a, xs, c0 + nth_bit(cm, i, lane), lane);
+  // Work units are rows: unit 2m is the up row, unit 2m + 1 the gate row of
+  // the m-th computed channel.  Wave w takes units w, w + 8, ..., two at a
+  // time, so every wave streams about the same number of bytes.
+  const int nu = 2 * nc;
+  auto unit_base = [&](int u) {
+    const int ch = c0 + nth_bit(cm, u >> 1, lane);
+    return ((uint32_t)ch * 2u + (uint32_t)(u & 1)) * rowb;
+  };
+  for (int u0 = wv; u0 < nu; u0 += 2 * kFW) {
+    const int u1 = u0 + kFW;
+    float r0, r1;
+    if (u1 < nu) {
+      p3_rows<BF16, 2>(a, xs, unit_base(u0), unit_base(u1), lane, r0, r1);
+      if (lane == 0) {
+        sm.ured[u0] = r0;
+        sm.ured[u1] = r1;
+      }
+    } else {
+      p3_rows<BF16, 1>(a, xs, unit_base(u0), 0u, lane, r0, r1);
+      if (lane == 0) sm.ured[u0] = r0;
+    }
+  }
+  __syncthreads();
+  if (wv == 0 && ((cm >> lane) & 1ull)) {
+    const unsigned m = __builtin_amdgcn_mbcnt_hi((unsigned)(cm >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((unsigned)cm, 0u));
+    xstore(&a.sdense[c0 + lane], sm.ured[2 * m] * gate_act(sm.ured[2 * m + 1], a.act));
+  }
   if (threadIdx.x == 0) {
-    xstore_u(&a.gmask[2 * item], (unsigned)dm);
-    xstore_u(&a.gmask[2 * item + 1], (unsigned)bm);
+    xstore_u(&a.gmask[4 * item], (unsigned)dm);
+    xstore_u(&a.gmask[4 * item + 1], (unsigned)(dm >> 32));
+    xstore_u(&a.gmask[4 * item + 2], (unsigned)bm);
+    xstore_u(&a.gmask[4 * item + 3], (unsigned)(bm >> 32));
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -660,7 +691,7 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
-  constexpr int U = BF16 ? 16 : 8;  // rows per wave per batch
+  constexpr int U = BF16 ? 20 : 8;  // rows per wave per batch
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int QPR = kP4Ch / kP3Ch;  // P3 items per range
   static_assert(QPR < 64, "one wave polls the range's P3 flags and the select flag");
@@ -911,23 +942,23 @@ __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, 
   const int J = (int)tj[2];
   for (int q0 = 0; q0 < n_p3; q0 += kFT) {
     const int q = q0 + (int)threadIdx.x;
-    unsigned m = 0u;
+    uint64_t m = 0ull;
     if (q < n_p3) {
-      m = gmask[2 * q];
-      unsigned bm = gmask[2 * q + 1];
+      m = (uint64_t)gmask[4 * q] | ((uint64_t)gmask[4 * q + 1] << 32);
+      uint64_t bm = (uint64_t)gmask[4 * q + 2] | ((uint64_t)gmask[4 * q + 3] << 32);
       while (bm) {
-        const int b = __builtin_ctz(bm);
-        bm &= bm - 1u;
+        const int b = __builtin_ctzll(bm);
+        bm &= bm - 1ull;
         const int ch = q * kP3Ch + b;
         const unsigned key = __float_as_uint(sabs[ch]);
-        if (key > T || (key == T && ch <= J)) m |= 1u << b;
+        if (key > T || (key == T && ch <= J)) m |= 1ull << b;
       }
     }
     unsigned tot;
-    unsigned pos = base + block_excl_scan<kFW>((unsigned)__popc(m), wsum, tot);
+    unsigned pos = base + block_excl_scan<kFW>((unsigned)__popcll(m), wsum, tot);
     while (m) {
-      const int b = __builtin_ctz(m);
-      m &= m - 1u;
+      const int b = __builtin_ctzll(m);
+      m &= m - 1ull;
       const int ch = q * kP3Ch + b;
       if (pos < (unsigned)k && ch < d_ff) {
         sel[pos] = ch;
@@ -981,7 +1012,7 @@ static size_t fused_hist_word(const Plan &p) {
   return fused_tflag_word(p) + (size_t)p.ntile * kSyncStride;
 }
 
-size_t fused_sync_words(const Plan &p) { return fused_hist_word(p) + 2048 + 2 * fused_n_p3(p); }
+size_t fused_sync_words(const Plan &p) { return fused_hist_word(p) + 2048 + 4 * fused_n_p3(p); }
 
 int fused_ypart_rows(const Plan &p) { return (p.d_ff + kP4Ch - 1) / kP4Ch; }
 
