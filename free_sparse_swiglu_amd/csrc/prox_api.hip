@@ -103,6 +103,8 @@ Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act) {
   p.upgate_cap = 4096;
   const char *path = getenv("PROX_PATH");
   p.use_fused = fused_supported(p) && !(path && strcmp(path, "multi") == 0);
+  const char *bg = getenv("PROX_BATCH_GEMV");
+  p.batch_mfma = bg && strcmp(bg, "mfma") == 0;
   return p;
 }
 
@@ -120,7 +122,8 @@ Layout make_layout(const Plan &p) {
   L.o_tile_cnt = o;  o = align256(o + (size_t)p.ntile * sizeof(unsigned));
   L.o_sabs = o;      o = align256(o + B * p.d_ff * sizeof(float));
   L.o_sel = o;       o = align256(o + B * p.d_ff * sizeof(int));
-  L.o_ssp = o;       o = align256(o + B * p.d_ff * sizeof(float));
+  L.o_selw = o;      o = align256(o + B * ((p.d_ff + 31) / 32) * sizeof(unsigned));
+  L.o_ssp = o;       o = align256(o + ((B + 3) & ~(size_t)3) * p.d_ff * sizeof(float));
   L.o_uni = o;       o = align256(o + (size_t)p.d_ff * sizeof(int));
   L.o_nuni = o;      o = align256(o + sizeof(int));
   L.o_umask = o;     o = align256(o + (size_t)p.d_ff);
@@ -154,7 +157,7 @@ struct EventLog {
 // Stage 1, top-k and Stage 2 for `batch` tokens; writes y.
 prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau,
                         int k, void *y, float *resid, hipStream_t s,
-                        EventLog *log = nullptr) {
+                        EventLog *log = nullptr, bool lists = false) {
   const prox::Plan &p = L->plan;
   const prox::Bufs &b = L->bufs;
   EventLog none{nullptr, 0, 0};
@@ -176,7 +179,9 @@ prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau
   if ((e = prox::launch_proxy(p, b, x, batch, tau, s)) != hipSuccess)
     return hip_fail(e, "stage 1 proxy kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = prox::launch_topk(p, b, batch, k, s)) != hipSuccess)
+  // Several tokens: Stage 2 runs over the union, built from mask words, so
+  // the per-token lists are written only when asked for.
+  if ((e = prox::launch_topk(p, b, batch, k, batch == 1 || lists, s)) != hipSuccess)
     return hip_fail(e, "top-k kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   const int mode = batch == 1 ? 0 : 1;
@@ -282,6 +287,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.tile_cnt = (unsigned *)(ws + lay.o_tile_cnt);
   b.sabs = (float *)(ws + lay.o_sabs);
   b.sel = (int *)(ws + lay.o_sel);
+  b.selw = (unsigned *)(ws + lay.o_selw);
   b.ssp = (float *)(ws + lay.o_ssp);
   b.uni = (int *)(ws + lay.o_uni);
   b.nuni = (int *)(ws + lay.o_nuni);
@@ -344,7 +350,7 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
   if (dbg->status &&
       (e = hipMemsetAsync(b.sync + prox::kFusedErrWord, 0, sizeof(unsigned), s)) != hipSuccess)
     return hip_fail(e, "clear status");
-  st = run_forward(layer, x, batch, threshold, k, y, nullptr, s);
+  st = run_forward(layer, x, batch, threshold, k, y, nullptr, s, nullptr, true);
   if (st != PROX_OK) return st;
   if (dbg->status &&
       (e = hipMemcpyAsync(dbg->status, b.sync + prox::kFusedErrWord, sizeof(unsigned),
@@ -383,9 +389,13 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
           (e = hipMemcpyAsync(dbg->union_idx, b.uni, (size_t)p.d_ff * 4,
                               hipMemcpyDeviceToDevice, s)) != hipSuccess)
         return hip_fail(e, "copy union");
-      if (dbg->s_sel &&
-          (e = hipMemcpyAsync(dbg->s_sel, b.ssp, nf * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
-        return hip_fail(e, "copy s");
+      // s is kept as [position][token] (row stride nbp): copy out token-major
+      const size_t nbp = (size_t)((batch + 3) & ~3);
+      for (int t = 0; t < batch && dbg->s_sel; ++t)
+        if ((e = hipMemcpy2DAsync((float *)dbg->s_sel + (size_t)t * p.d_ff, 4, b.ssp + t,
+                                  nbp * 4, 4, (size_t)p.d_ff, hipMemcpyDeviceToDevice, s)) !=
+            hipSuccess)
+          return hip_fail(e, "copy s");
     }
   }
   return PROX_OK;

@@ -35,7 +35,9 @@ struct Bufs {
   unsigned *tile_cnt;  // [ntile]                  Stage 1 arrival counters
   float *sabs;     // [batch][d_ff]                 |s~|
   int *sel;        // [batch][d_ff]                 top-k channels, ascending
-  float *ssp;      // [batch][d_ff]                 exact s by list position
+  unsigned *selw;  // [batch][ceil(d_ff/32)]        the same masks as bit words
+  float *ssp;      // [d_ff][nbp]                   exact s by list position and token
+                   //   (nbp = 1 for one token, else batch rounded up to 4)
   int *uni;        // [d_ff]                        union of the masks
   int *nuni;       // [1]
   uint8_t *umask;  // [d_ff]                        token bits per union entry
@@ -57,12 +59,13 @@ struct Plan {
   int upgate_cap;   // max work-groups of the up/gate kernel
   int use_fused;    // batch-1 forwards run the persistent fused kernel
   int act;          // gate activation: 0 SiLU, 1 GELU (tanh form)
+  int batch_mfma;   // bf16 batches of 2..8 tokens: up/gate on MFMA (default: VALU dot2)
 };
 
 struct Layout {
   size_t weights, proxy, workspace;
   size_t o_wd, o_psc;
-  size_t o_part, o_tile_cnt, o_sabs, o_sel, o_ssp, o_uni, o_nuni, o_umask,
+  size_t o_part, o_tile_cnt, o_sabs, o_sel, o_selw, o_ssp, o_uni, o_nuni, o_umask,
       o_ypart, o_col_cnt, o_sync, o_xbuf, o_ybuf;
 };
 
@@ -78,7 +81,7 @@ hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
                                int8_t *codes, float *scales, hipStream_t s);
 hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
                         float tau, hipStream_t s);
-hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k,
+hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
                        hipStream_t s);
 hipError_t launch_union(const Plan &p, const Bufs &b, int batch, int k,
                         hipStream_t s);

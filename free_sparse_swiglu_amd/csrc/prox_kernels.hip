@@ -7,7 +7,9 @@
 // (top-k mask).
 //
 // Batch-1 decode is a chain of matrix-vector products, so every kernel here
-// is bound by HBM bandwidth, not by arithmetic: no MFMA.  The weight layouts
+// is bound by HBM bandwidth, not by arithmetic: no MFMA at batch 1.  For 2..8
+// tokens the exact up/gate step has an MFMA form (a 16-channel x 16-token
+// tile per instruction) beside the VALU one.  The weight layouts
 // make each read a long contiguous run (see prox_internal.h), reads go
 // through buffer loads with scalar row offsets, and every reduction across
 // work-groups is deterministic (partials + last-arriving work-group, fixed
@@ -379,7 +381,7 @@ __device__ __forceinline__ void pick_bin(const unsigned *hist, unsigned kk,
 
 template <int PER>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff, int k,
-                                                    int *sel) {
+                                                    int *sel, unsigned *selw) {
   __shared__ unsigned h1[2048];
   __shared__ unsigned h2[2048];
   __shared__ unsigned h3[512];
@@ -389,7 +391,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   if (k <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float *z = sabs + (size_t)b * d_ff;
-  int *out = sel + (size_t)b * d_ff;
+  int *out = sel ? sel + (size_t)b * d_ff : nullptr;
+  const int words = (d_ff + 31) >> 5;
+  unsigned *outw = selw + (size_t)b * words;
   unsigned key[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -431,6 +435,20 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   const unsigned T = (p2 << 9) | s_bin;
   kk = s_kk;  // keys equal to T that are kept (the lowest-index ones)
 
+  // No list wanted and every key equal to T kept (h3 counts the keys equal
+  // to T): the mask is key >= T, written as bit words only.
+  if (!sel && kk == h3[s_bin]) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = e * 1024 + tid;
+      const uint64_t km = __ballot(j < d_ff && key[e] >= T);
+      const int wi = e * 32 + w * 2;
+      if (lane == 0 && wi < words) outw[wi] = (unsigned)km;
+      if (lane == 1 && wi + 1 < words) outw[wi + 1] = (unsigned)(km >> 32);
+    }
+    return;
+  }
+
   // Compaction.  Pass A: per (slot, wave) counts of keys > T and == T.
   uint64_t mgt[PER], meq[PER];
 #pragma unroll
@@ -469,58 +487,49 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
     const unsigned base = cnt[e * 16 + w];
     const unsigned gt_b = (base & 0xffffu) + (unsigned)__popcll(mgt[e] & below);
     const unsigned eq_b = (base >> 16) + (unsigned)__popcll(meq[e] & below);
-    if (j < d_ff) {
-      if (key[e] > T)
-        out[gt_b + min(eq_b, kk)] = j;
-      else if (key[e] == T && eq_b < kk)
-        out[gt_b + eq_b] = j;
-    }
+    const bool kept = j < d_ff && (key[e] > T || (key[e] == T && eq_b < kk));
+    if (kept && out) out[key[e] > T ? gt_b + min(eq_b, kk) : gt_b + eq_b] = j;
+    // The same mask as bit words: this wave's 64 channels are words
+    // 32 e + 2 w and 32 e + 2 w + 1.
+    const uint64_t km = __ballot(kept);
+    const int wi = e * 32 + w * 2;
+    if (lane == 0 && wi < words) outw[wi] = (unsigned)km;
+    if (lane == 1 && wi + 1 < words) outw[wi + 1] = (unsigned)(km >> 32);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Union of the per-token masks (batch path): U ascending, plus for each entry
-// the bit set of tokens whose mask holds it.  One 1024-thread work-group.
+// the bit set of tokens whose mask holds it.  One 1024-thread work-group;
+// thread w owns mask word w (channels 32 w .. 32 w + 31, d_ff <= 32768), reads
+// that word of every token, and writes its union entries at its exclusive
+// prefix of the word popcounts.
 // ---------------------------------------------------------------------------
-template <int PER>
-__global__ __launch_bounds__(1024) void union_kernel(const int *sel, int d_ff,
-                                                     int k, int nb, int *uni,
+template <int NB>
+__global__ __launch_bounds__(1024) void union_kernel(const unsigned *selw, int d_ff, int *uni,
                                                      int *nuni, uint8_t *umask) {
-  __shared__ unsigned bits[kMaxBatch][kMaxDff / 32];
   __shared__ unsigned wsum[16];
-  const int tid = threadIdx.x;
+  const int w = threadIdx.x;
   const int words = (d_ff + 31) >> 5;
-  for (int b = 0; b < nb; ++b)
-    for (int i = tid; i < words; i += 1024) bits[b][i] = 0u;
-  __syncthreads();
-  for (int b = 0; b < nb; ++b)
-    for (int i = tid; i < k; i += 1024) {
-      const int j = sel[(size_t)b * d_ff + i];
-      if ((unsigned)j < (unsigned)d_ff) atomicOr(&bits[b][j >> 5], 1u << (j & 31));
-    }
-  __syncthreads();
-  const int j0 = tid * PER;
-  unsigned tm[PER];
-  unsigned cnt = 0u;
+  unsigned tw[NB], u = 0u;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int j = j0 + e;
-    unsigned m = 0u;
-    if (j < d_ff)
-      for (int b = 0; b < nb; ++b) m |= ((bits[b][j >> 5] >> (j & 31)) & 1u) << b;
-    tm[e] = m;
-    cnt += (m != 0u);
+  for (int b = 0; b < NB; ++b) {
+    tw[b] = w < words ? selw[(size_t)b * words + w] : 0u;
+    u |= tw[b];
   }
   unsigned total;
-  unsigned pos = block_excl_scan<16>(cnt, wsum, total);
+  unsigned pos = block_excl_scan<16>((unsigned)__popc(u), wsum, total);
+  while (u) {
+    const int bit = __builtin_ctz(u);
+    u &= u - 1u;
+    unsigned m = 0u;
 #pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (tm[e]) {
-      uni[pos] = j0 + e;
-      umask[pos] = (uint8_t)tm[e];
-      ++pos;
-    }
-  if (tid == 0) *nuni = (int)total;
+    for (int b = 0; b < NB; ++b) m |= ((tw[b] >> bit) & 1u) << b;
+    uni[pos] = w * 32 + bit;
+    umask[pos] = (uint8_t)m;
+    ++pos;
+  }
+  if (w == 0) *nuni = (int)total;
 }
 
 // ---------------------------------------------------------------------------
@@ -532,6 +541,12 @@ __global__ __launch_bounds__(1024) void union_kernel(const int *sel, int d_ff,
 // (channel-major layout), read 16 bytes per lane per step; x sits in LDS.
 // mode 0: position p -> channel sel[p] (one token); mode 1: channel uni[p],
 // s zeroed for tokens whose own mask lacks it; mode 2: dense, channel p.
+// Exact s of the selected channels: one token, ssp[p] for list position p;
+// NB >= 2 tokens, ssp[p * sstride(NB) + b], the tokens of a position side by
+// side (stride rounded up to 4 floats, so a row's values are whole 16-byte
+// loads for the down projection).
+__host__ __device__ constexpr int sstride(int nb) { return nb == 1 ? 1 : (nb + 3) & ~3; }
+
 struct UpGateArgs {
   const void *wug;
   uint32_t wug_bytes;
@@ -544,8 +559,8 @@ struct UpGateArgs {
   int act;  // gate activation (gate_act)
 };
 
-template <int NB, bool BF16, int MODE>
-__global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
+template <int NB, bool BF16, int MODE, int NWV>
+__global__ __launch_bounds__(NWV * 64) void upgate_kernel(UpGateArgs a) {
   extern __shared__ u4 xs[];
   constexpr int EPL = BF16 ? 8 : 4;   // elements per 16-byte load
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -553,14 +568,14 @@ __global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = a.d_model / EPL;  // 16-byte units per row
-  for (int i = threadIdx.x; i < NB * row16; i += 256) xs[i] = ((const u4 *)a.x)[i];
+  for (int i = threadIdx.x; i < NB * row16; i += NWV * 64) xs[i] = ((const u4 *)a.x)[i];
   __syncthreads();
 
   const int n = a.n_ptr ? *a.n_ptr : a.n;
   const int nsteps = row16 / 64;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
-  const int W = gridDim.x * 4;
-  for (int p = blockIdx.x * 4 + wv; p < n; p += W) {
+  const int W = gridDim.x * NWV;
+  for (int p = blockIdx.x * NWV + wv; p < n; p += W) {
     const int j = (MODE == 2) ? p : a.list[p];
     const uint32_t ubase = (uint32_t)j * 2u * (uint32_t)a.d_model * ESZ;
     const uint32_t gbase = ubase + (uint32_t)a.d_model * ESZ;
@@ -596,7 +611,7 @@ __global__ __launch_bounds__(256) void upgate_kernel(UpGateArgs a) {
       const float u = wave_sum(au[b]);
       const float g = wave_sum(ag[b]);
       if (lane == 0)
-        a.ssp[(size_t)b * a.d_ff + p] = ((tok >> b) & 1u) ? u * gate_act(g, a.act) : 0.0f;
+        a.ssp[(size_t)p * sstride(NB) + b] = ((tok >> b) & 1u) ? u * gate_act(g, a.act) : 0.0f;
     }
   }
 }
@@ -647,10 +662,12 @@ __global__ __launch_bounds__(256) void upgate1_kernel(UpGateArgs a, int per) {
 // K-f  Stage 2b: input-sparse down projection y = s_sp W_down[sel, :]
 //      (Sec. 4.1, Stage 2 equations; Sec. 3.1, weighted-sum view)
 // ---------------------------------------------------------------------------
-// Grid (ncol, nrc), 4 waves.  Work-group (c, r) covers output columns
-// [256c, 256c + 256) and list positions [rR, rR + R); lane l owns 4 columns
-// and walks its wave's rows (8 bytes bf16 / 16 bytes f32 per row), with the
-// row index and s value uniform across the wave.  W_down is stored in
+// Grid (ncol, nrc), NW waves.  Work-group (c, r) covers output columns
+// [256c, 256c + 256) and list positions [rR, rR + R).  float32: lane l owns 4
+// columns of the wave's row (16 bytes), row index and s uniform across the
+// wave.  bfloat16: a 512-byte row is half a wave, so one load covers two
+// rows, lane l owning 8 columns of row l / 32; the halves are folded at the
+// end.  Waves split the rows and add up in LDS.  W_down is stored in
 // 256-column chunks (see retile_down_kernel), so a chunk's rows are
 // contiguous and a dense pass streams each chunk sequentially.  The last work-group of a
 // column chunk adds the nrc partials in order, casts y to the layer dtype
@@ -668,10 +685,33 @@ struct DownArgs {
   float *resid;
 };
 
+// s of list position pc for NB tokens (zeros unless ok): one float for one
+// token, else whole 16-byte loads of the position's row of ssp.
+template <int NB>
+__device__ __forceinline__ void load_s(const float *ssp, int pc, bool ok, float (&sv)[NB]) {
+  if constexpr (NB == 1) {
+    const float v = ssp[pc];
+    sv[0] = ok ? v : 0.0f;
+  } else {
+    const float4 *r = (const float4 *)(ssp + (size_t)pc * sstride(NB));
+#pragma unroll
+    for (int q = 0; q < (NB + 3) / 4; ++q) {
+      const float4 v = r[q];
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < NB) sv[4 * q + i] = ok ? e[i] : 0.0f;
+    }
+  }
+}
+
 template <int NB, bool BF16, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) void down_kernel(DownArgs a) {
-  constexpr int U = 8;   // rows in flight per wave
+__global__ __launch_bounds__(NW * 64, NW == 16 ? 8 : 4) void down_kernel(DownArgs a) {
+  // rows in flight per wave: float32 one row per load (16 bytes a lane);
+  // bfloat16 two rows per load (lanes 0-31 and 32-63, 16 bytes a lane)
+  constexpr int U = BF16 ? (NB > 6 ? 3 : NB > 4 ? 4 : NB != 2 ? 6 : 8) : 8;
   constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int CPL = BF16 ? 8 : 4;      // columns per lane
   __shared__ float red[NW][NB][kDownCols];
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
@@ -685,54 +725,108 @@ __global__ __launch_bounds__(NW * 64) void down_kernel(DownArgs a) {
   const size_t chunk_bytes = (size_t)a.d_ff * kDownCols * ESZ;
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc((const char *)a.wd + cc * chunk_bytes, (uint32_t)chunk_bytes);
-  const uint32_t voff = (uint32_t)lane * 4u * ESZ;
 
-  float acc[NB][4];
+  float acc[NB][CPL];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[b][c] = 0.0f;
+    for (int c = 0; c < CPL; ++c) acc[b][c] = 0.0f;
 
-  // Rows p0+wv, p0+wv+NW, ... of this chunk; an out-of-range slot re-reads a
-  // valid row and gets s = 0, so the loop body has no branches.
-  for (int p = p0 + wv; p < p1; p += NW * U) {
-    float wf[U][4];
-    float sv[U][NB];
+  if constexpr (BF16) {
+    // Wave wv takes row pairs wv, wv+NW, ...; half h = lane / 32 of the wave
+    // takes the pair's row h, lane % 32 its columns 8 (lane % 32) .. +7.  An
+    // out-of-range slot re-reads row p0 and gets s = 0 (no branches).
+    const int h = lane >> 5;
+    const uint32_t voff = (uint32_t)(lane & 31) * 16u;
+    constexpr int STEP = 2 * NW * U;
+    // Channel numbers of the next step are fetched while this step's rows
+    // are in flight, so a step waits for one memory round trip, not two
+    // (list entry, then row).
+    int jn[U];
+    auto fetch_j = [&](int pb) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int pp = p + NW * u;
-      const bool ok = pp < p1;
-      const int ppc = ok ? pp : p;
-      const int j = (MODE == 2) ? ppc : a.list[ppc];
+      for (int u = 0; u < U; ++u) {
+        const int pp = pb + 2 * NW * u + h;
+        const int ppc = pp < p1 ? pp : p0;
+        jn[u] = (MODE == 2) ? ppc : a.list[ppc];
+      }
+    };
+    const int pstart = p0 + 2 * wv;
+    if (pstart < p1) fetch_j(pstart);
+    for (int p = pstart; p < p1; p += STEP) {
+      u4 w[U];
+      float sv[U][NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) sv[u][b] = ok ? a.ssp[(size_t)b * a.d_ff + ppc] : 0.0f;
-      const uint32_t rowoff = (uint32_t)j * (uint32_t)(kDownCols * ESZ);
-      if constexpr (BF16) {
-        const u2 w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, rowoff, kNT);
-        wf[u][0] = bf16_to_f32(w.x & 0xffffu);
-        wf[u][1] = bf16_to_f32(w.x >> 16);
-        wf[u][2] = bf16_to_f32(w.y & 0xffffu);
-        wf[u][3] = bf16_to_f32(w.y >> 16);
-      } else {
+      for (int u = 0; u < U; ++u)
+        w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + (uint32_t)jn[u] * (kDownCols * 2u), 0, kNT);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pp = p + 2 * NW * u + h;
+        const bool ok = pp < p1;
+        // unconditional loads of a valid slot, then select: no branch
+        load_s<NB>(a.ssp, ok ? pp : p0, ok, sv[u]);
+      }
+      fetch_j(p + STEP);  // past the end: clamped, valid, unused
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = __uint_as_float(ww[q] << 16), hi = __uint_as_float(ww[q] & 0xffff0000u);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            acc[b][2 * q] = fmaf(sv[u][b], lo, acc[b][2 * q]);
+            acc[b][2 * q + 1] = fmaf(sv[u][b], hi, acc[b][2 * q + 1]);
+          }
+        }
+      }
+    }
+    // The two halves hold the same columns: fold the upper into the lower.
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[b][c] += __shfl_xor(acc[b][c], 32);
+    if (lane < 32) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        *(float4 *)&red[wv][b][lane * 8] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+        *(float4 *)&red[wv][b][lane * 8 + 4] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+      }
+    }
+  } else {
+    const uint32_t voff = (uint32_t)lane * 16u;
+    // Rows p0+wv, p0+wv+NW, ... of this chunk; an out-of-range slot re-reads a
+    // valid row and gets s = 0, so the loop body has no branches.
+    for (int p = p0 + wv; p < p1; p += NW * U) {
+      float wf[U][4];
+      float sv[U][NB];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pp = p + NW * u;
+        const bool ok = pp < p1;
+        const int ppc = ok ? pp : p;
+        const int j = (MODE == 2) ? ppc : a.list[ppc];
+        load_s<NB>(a.ssp, ppc, ok, sv[u]);
+        const uint32_t rowoff = (uint32_t)j * (uint32_t)(kDownCols * ESZ);
         const u4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, kNT);
         wf[u][0] = __uint_as_float(w.x);
         wf[u][1] = __uint_as_float(w.y);
         wf[u][2] = __uint_as_float(w.z);
         wf[u][3] = __uint_as_float(w.w);
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[b][c] = fmaf(sv[u][b], wf[u][c], acc[b][c]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[b][c] = fmaf(sv[u][b], wf[u][c], acc[b][c]);
+    for (int b = 0; b < NB; ++b)
+      *(float4 *)&red[wv][b][lane * 4] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
   }
-
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-    *(float4 *)&red[wv][b][lane * 4] =
-        make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
   __syncthreads();
   float *yp = a.ypart + (size_t)rc * NB * a.d_model;
   for (int e = threadIdx.x; e < NB * kDownCols; e += NW * 64) {
@@ -888,45 +982,124 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
 }
 
 template <int PER>
-static void topk_launch(const Plan &p, const Bufs &b, int batch, int k, hipStream_t s) {
-  topk_kernel<PER><<<batch, 1024, 0, s>>>(b.sabs, p.d_ff, k, b.sel);
+static void topk_launch(const Plan &p, const Bufs &b, int batch, int k, bool lists,
+                        hipStream_t s) {
+  topk_kernel<PER><<<batch, 1024, 0, s>>>(b.sabs, p.d_ff, k, lists ? b.sel : nullptr, b.selw);
 }
 
-hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, hipStream_t s) {
+hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
+                       hipStream_t s) {
   const int per = (p.d_ff + 1023) / 1024;
-  if (per <= 1) topk_launch<1>(p, b, batch, k, s);
-  else if (per <= 4) topk_launch<4>(p, b, batch, k, s);
-  else if (per <= 8) topk_launch<8>(p, b, batch, k, s);
-  else if (per <= 16) topk_launch<16>(p, b, batch, k, s);
-  else if (per <= 32) topk_launch<32>(p, b, batch, k, s);
+  if (per <= 1) topk_launch<1>(p, b, batch, k, lists, s);
+  else if (per <= 4) topk_launch<4>(p, b, batch, k, lists, s);
+  else if (per <= 8) topk_launch<8>(p, b, batch, k, lists, s);
+  else if (per <= 16) topk_launch<16>(p, b, batch, k, lists, s);
+  else if (per <= 32) topk_launch<32>(p, b, batch, k, lists, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_union(const Plan &p, const Bufs &b, int batch, int k, hipStream_t s) {
-  const int per = (p.d_ff + 1023) / 1024;
-  if (per <= 8)
-    union_kernel<8><<<1, 1024, 0, s>>>(b.sel, p.d_ff, k, batch, b.uni, b.nuni, b.umask);
-  else if (per <= 16)
-    union_kernel<16><<<1, 1024, 0, s>>>(b.sel, p.d_ff, k, batch, b.uni, b.nuni, b.umask);
-  else if (per <= 32)
-    union_kernel<32><<<1, 1024, 0, s>>>(b.sel, p.d_ff, k, batch, b.uni, b.nuni, b.umask);
-  else
-    return hipErrorInvalidValue;
+  (void)k;
+  if (p.d_ff > 32 * 1024) return hipErrorInvalidValue;
+  PROX_DISPATCH_NB(batch, (union_kernel<NB><<<1, 1024, 0, s>>>(b.selw, p.d_ff, b.uni, b.nuni, b.umask)));
   return hipGetLastError();
 }
 
-template <int NB, bool BF16, int MODE>
-static hipError_t upgate_go(const UpGateArgs &a, int grid, size_t lds, hipStream_t s) {
-  auto fn = upgate_kernel<NB, BF16, MODE>;
+// MFMA form of the batched up/gate step (bf16, 2 <= NB <= 8 tokens): one
+// wave per tile of 16 list positions.  v_mfma_f32_16x16x32_bf16 computes
+// D[m][n] = sum_k A[m][k] B[k][n] with A = 16 channel rows (lane l holds row
+// l%16, k = 8 (l/16) .. +7: 16 contiguous bytes of that row) and B = x of the
+// tokens (lane l holds token l%16, same k), so D holds u (or g) of channel
+// 4 (l/16) + i for token l%16 in element i of lane l.  Column n of D depends
+// on column n of B alone, so lanes of tokens >= NB load token NB-1 and their
+// results are dropped.  UK = 8 steps of K = 32 keep 16 KB of weights per wave
+// in flight; x comes from L2.  Each load instruction reads 64 bytes from each
+// of 16 rows, against 1 KB of one row in the VALU form, and measured slower
+// than the VALU form at 2, 4 and 8 tokens, so it runs only on request.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int NB, int MODE>
+__global__ __launch_bounds__(256) void upgate_mfma_kernel(UpGateArgs a) {
+  constexpr int UK = 8;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int n = a.n_ptr ? *a.n_ptr : a.n;
+  const int ntiles = (n + 15) >> 4;
+  const uint32_t rowb = (uint32_t)a.d_model * 2u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)NB * rowb);
+  const uint32_t xbase = (uint32_t)min(m, NB - 1) * rowb;
+  for (int tile = blockIdx.x * 4 + wv; tile < ntiles; tile += gridDim.x * 4) {
+    const int pc = min(tile * 16 + m, n - 1);
+    const int j = (MODE == 2) ? pc : a.list[pc];
+    const uint32_t ubase = (uint32_t)j * 2u * rowb;
+    const uint32_t gbase = ubase + rowb;
+    f32x4_t au = {0.0f, 0.0f, 0.0f, 0.0f}, ag = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < a.d_model; k0 += 32 * UK) {
+      u4 wu[UK], wg[UK], xv[UK];
+#pragma unroll
+      for (int u = 0; u < UK; ++u) {
+        const uint32_t off = (uint32_t)(k0 + 32 * u + 8 * g) * 2u;
+        wu[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, ubase + off, 0, kNT);
+        wg[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, gbase + off, 0, kNT);
+        xv[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, xbase + off, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UK; ++u) {
+        bf16x8_t A, B, G;
+        __builtin_memcpy(&A, &wu[u], 16);
+        __builtin_memcpy(&G, &wg[u], 16);
+        __builtin_memcpy(&B, &xv[u], 16);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, au, 0, 0, 0);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G, B, ag, 0, 0, 0);
+      }
+    }
+    if (m < NB) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = tile * 16 + 4 * g + i;
+        if (p < n) {
+          const unsigned tok = (MODE == 1) ? a.umask[p] : 0xffu;
+          a.ssp[(size_t)p * sstride(NB) + m] = ((tok >> m) & 1u) ? au[i] * gate_act(ag[i], a.act) : 0.0f;
+        }
+      }
+    }
+  }
+}
+
+template <int NB, int MODE>
+static hipError_t upgate_mfma_go(const UpGateArgs &a, int maxn, int cap, hipStream_t s) {
+  int grid = ((maxn + 15) / 16 + 3) / 4;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  upgate_mfma_kernel<NB, MODE><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// x of all tokens sits in LDS, so once it takes more than a quarter of a
+// CU's LDS the kernel runs 16-wave work-groups to keep the CU's waves up.
+template <int NWV, int NB, bool BF16, int MODE>
+static hipError_t upgate_go_w(const UpGateArgs &a, int maxn, int cap, size_t lds, hipStream_t s) {
+  auto fn = upgate_kernel<NB, BF16, MODE, NWV>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void *)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  fn<<<grid, 256, lds, s>>>(a);
+  int grid = (maxn + NWV - 1) / NWV;
+  if (grid > cap * 4 / NWV) grid = cap * 4 / NWV;
+  fn<<<grid, NWV * 64, lds, s>>>(a);
   return hipGetLastError();
+}
+
+template <int NB, bool BF16, int MODE>
+static hipError_t upgate_go(const UpGateArgs &a, int maxn, int cap, size_t lds, hipStream_t s) {
+  if (lds > kMaxLds / 4) return upgate_go_w<16, NB, BF16, MODE>(a, maxn, cap, lds, s);
+  return upgate_go_w<4, NB, BF16, MODE>(a, maxn, cap, lds, s);
 }
 
 // Waves of a kernel that fit on the device at once (occupancy x CUs).
@@ -987,20 +1160,41 @@ hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
       done = mode == 0 ? upgate1_dispatch<false, 0>(p, a, s, e1) : upgate1_dispatch<false, 2>(p, a, s, e1);
     if (done) return e1;
   }
-  int grid = (maxn + 3) / 4;
-  if (grid > p.upgate_cap) grid = p.upgate_cap;
-  const size_t lds = (size_t)batch * p.d_model * p.esz;
   hipError_t e = hipErrorInvalidValue;
+  if (p.bf16 && batch >= 2 && mode != 0 && p.batch_mfma) {
+#define PROX_MFMA_NB(MD)                                                     \
+  switch (batch) {                                                           \
+    case 2: return upgate_mfma_go<2, MD>(a, maxn, p.upgate_cap, s);          \
+    case 3: return upgate_mfma_go<3, MD>(a, maxn, p.upgate_cap, s);          \
+    case 4: return upgate_mfma_go<4, MD>(a, maxn, p.upgate_cap, s);          \
+    case 5: return upgate_mfma_go<5, MD>(a, maxn, p.upgate_cap, s);          \
+    case 6: return upgate_mfma_go<6, MD>(a, maxn, p.upgate_cap, s);          \
+    case 7: return upgate_mfma_go<7, MD>(a, maxn, p.upgate_cap, s);          \
+    case 8: return upgate_mfma_go<8, MD>(a, maxn, p.upgate_cap, s);          \
+    default: return hipErrorInvalidValue;                                    \
+  }
+    if (mode == 1) { PROX_MFMA_NB(1) } else { PROX_MFMA_NB(2) }
+#undef PROX_MFMA_NB
+  }
+  const int cap = p.upgate_cap;
+  const size_t lds = (size_t)batch * p.d_model * p.esz;
   if (p.bf16) {
-    if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 0>(a, grid, lds, s))); }
-    else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 1>(a, grid, lds, s))); }
-    else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 2>(a, grid, lds, s))); }
+    if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 0>(a, maxn, cap, lds, s))); }
+    else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 1>(a, maxn, cap, lds, s))); }
+    else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 2>(a, maxn, cap, lds, s))); }
   } else {
-    if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 0>(a, grid, lds, s))); }
-    else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 1>(a, grid, lds, s))); }
-    else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 2>(a, grid, lds, s))); }
+    if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 0>(a, maxn, cap, lds, s))); }
+    else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 1>(a, maxn, cap, lds, s))); }
+    else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 2>(a, maxn, cap, lds, s))); }
   }
   return e;
+}
+
+template <int NB, bool BF, int MD>
+static void down_go(const DownArgs &a, dim3 g, hipStream_t s) {
+  if constexpr (NB == 1 || (NB == 2 && !BF)) down_kernel<NB, BF, MD, 16><<<g, 1024, 0, s>>>(a);
+  else if constexpr (NB <= 4 || BF) down_kernel<NB, BF, MD, 8><<<g, 512, 0, s>>>(a);
+  else down_kernel<NB, BF, MD, 4><<<g, 256, 0, s>>>(a);
 }
 
 hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
@@ -1010,12 +1204,11 @@ hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
              b.ypart, b.col_cnt, y, resid};
   if (mode == 1) a.n_ptr = b.nuni;
   dim3 g(p.ncol, p.nrc);
-  // Waves per work-group: 16 for one or two tokens (more loads in flight),
-  // fewer for larger batches to bound the LDS reduction buffer.
-#define PROX_DOWN(BF, MD)                                                              \
-  PROX_DISPATCH_NB(batch, (NB <= 2 ? (down_kernel<NB, BF, MD, 16><<<g, 1024, 0, s>>>(a), 0)   \
-                           : NB <= 4 ? (down_kernel<NB, BF, MD, 8><<<g, 512, 0, s>>>(a), 0)  \
-                                     : (down_kernel<NB, BF, MD, 4><<<g, 256, 0, s>>>(a), 0)))
+  // Waves per work-group: 16 for one token (two for float32), else 8, so
+  // that two work-groups fit a CU; float32 layers of 5..8 tokens take 4
+  // waves to bound the LDS reduction buffer (32 KiB).
+#define PROX_DOWN(BF, MD)                                                       \
+  PROX_DISPATCH_NB(batch, (down_go<NB, BF, MD>(a, g, s)))
   if (p.bf16) {
     if (mode == 0) { PROX_DOWN(true, 0); }
     else if (mode == 1) { PROX_DOWN(true, 1); }
