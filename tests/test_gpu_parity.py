@@ -242,6 +242,60 @@ def test_batch_equals_independent_tokens(B):
         _check_token(case, xd[t], X[t].float().numpy(), case.tau, k, out, t=t)
         sels.append(set(out["sel"][t, :k].cpu().tolist()))
     nu = int(out["n_union"][0])
+    uni = out["union_idx"][:nu].cpu().tolist()
+    assert uni == sorted(set.union(*sels))
+    # exact s by union position: token t's value where its own mask holds
+    # the channel, else 0
+    for t in range(B):
+        s_exact, _ = oracle.dense(X[t].float().numpy(), *case.Wnp, act=case.act)
+        want = np.array([s_exact[j] if j in sels[t] else 0.0 for j in uni])
+        got = out["s_sel"][t, :nu].cpu().numpy().astype(np.float64)
+        assert not np.any(got[want == 0.0])
+        assert rel_err(got, want) <= 1e-4
+    yb = prox.prox_ffn_forward_batch(case.L, xd, case.tau, k)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int16), out["y"].view(torch.int16))
+
+
+@pytest.mark.parametrize("B", [2, 5, 8])
+def test_batch_mfma_form_parity(B, monkeypatch):
+    """The MFMA form of the batched up/gate step (chosen at prepare time)
+    against the oracle, token by token, and against the VALU form."""
+    monkeypatch.setenv("PROX_BATCH_GEMV", "mfma")
+    case = Case(RAGGED, 0, "cpu", 8)
+    monkeypatch.delenv("PROX_BATCH_GEMV")
+    valu = get_case(RAGGED, max_batch=8)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    X = case.inputs(B, "mfma")
+    xd = X.to(DEV)
+    out = prox.prox_ffn_forward_debug(case.L, xd, case.tau, k)
+    yv = prox.prox_ffn_forward_batch(valu.L, xd, valu.tau, k)
+    yd = prox.prox_dense_ffn_forward(case.L, xd)
+    torch.cuda.synchronize()
+    for t in range(B):
+        _check_token(case, xd[t], X[t].float().numpy(), case.tau, k, out, t=t)
+        _, y_ref = oracle.dense(X[t].float().numpy(), *case.Wnp)
+        assert rel_err(yd[t].float().cpu().numpy(), y_ref) <= _tol(RAGGED)
+    assert rel_err(yv.float().cpu().numpy(), out["y"].float().cpu().numpy()) <= _tol(RAGGED)
+
+
+def test_batch_split_tie():
+    """A zero token has |s~| = 0 everywhere: its mask is the k lowest
+    channels (ties to the lower index), the product path (mask words only)
+    takes its tie branch and must agree with the list path."""
+    case = get_case(RAGGED, max_batch=8)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    X = case.inputs(3, "tie")
+    X[1].zero_()
+    xd = X.to(DEV)
+    out = prox.prox_ffn_forward_debug(case.L, xd, case.tau, k)
+    torch.cuda.synchronize()
+    assert out["sel"][1, :k].cpu().tolist() == list(range(k))
+    assert not torch.any(out["y"][1].float())
+    for t in (0, 2):
+        _check_token(case, xd[t], X[t].float().numpy(), case.tau, k, out, t=t)
+    sels = [set(out["sel"][t, :k].cpu().tolist()) for t in range(3)]
+    nu = int(out["n_union"][0])
     assert out["union_idx"][:nu].cpu().tolist() == sorted(set.union(*sels))
     yb = prox.prox_ffn_forward_batch(case.L, xd, case.tau, k)
     torch.cuda.synchronize()
