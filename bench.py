@@ -381,6 +381,7 @@ def bench_batch(args):
                             mean_union=float(np.mean(unions)),
                             union_frac=round(float(np.mean(unions)) / cfg.d_ff, 4))
     return dict(metric="us per batched FFN step, 70B-shaped, 70% sparsity", unit="us",
+                batch_gemv=args.batch_gemv,
                 n_gpus=1, steps=args.steps, warmup=args.warmup, dtype="bf16",
                 data="synthetic", config=dict(workload="70B-shaped single FFN layer, "
                                                        "batch 1/2/4/8", k=k, ring_layers=R),
@@ -547,7 +548,11 @@ def main():
     ap.add_argument("--ring", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--batch-gemv", choices=["valu", "mfma"], default="valu",
+                    help="form of the batched up/gate step the layers are prepared with")
     args = ap.parse_args()
+    # read by the library when a layer is prepared
+    os.environ["PROX_BATCH_GEMV"] = args.batch_gemv
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
               "supported (the multi-GPU split is a design note, not a measured path)",
