@@ -393,7 +393,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   const float *z = sabs + (size_t)b * d_ff;
   int *out = sel ? sel + (size_t)b * d_ff : nullptr;
   const int words = (d_ff + 31) >> 5;
-  unsigned *outw = selw + (size_t)b * words;
+  unsigned *outw = selw ? selw + (size_t)b * words : nullptr;
   unsigned key[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
 
   // No list wanted and every key equal to T kept (h3 counts the keys equal
   // to T): the mask is key >= T, written as bit words only.
-  if (!sel && kk == h3[s_bin]) {
+  if (!sel && outw && kk == h3[s_bin]) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int j = e * 1024 + tid;
@@ -491,10 +491,12 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
     if (kept && out) out[key[e] > T ? gt_b + min(eq_b, kk) : gt_b + eq_b] = j;
     // The same mask as bit words: this wave's 64 channels are words
     // 32 e + 2 w and 32 e + 2 w + 1.
-    const uint64_t km = __ballot(kept);
-    const int wi = e * 32 + w * 2;
-    if (lane == 0 && wi < words) outw[wi] = (unsigned)km;
-    if (lane == 1 && wi + 1 < words) outw[wi + 1] = (unsigned)(km >> 32);
+    if (outw) {
+      const uint64_t km = __ballot(kept);
+      const int wi = e * 32 + w * 2;
+      if (lane == 0 && wi < words) outw[wi] = (unsigned)km;
+      if (lane == 1 && wi + 1 < words) outw[wi + 1] = (unsigned)(km >> 32);
+    }
   }
 }
 
@@ -984,7 +986,10 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
 template <int PER>
 static void topk_launch(const Plan &p, const Bufs &b, int batch, int k, bool lists,
                         hipStream_t s) {
-  topk_kernel<PER><<<batch, 1024, 0, s>>>(b.sabs, p.d_ff, k, lists ? b.sel : nullptr, b.selw);
+  // one token: the list only (it drives Stage 2); several: the mask words
+  // drive the union, the lists only when asked for
+  topk_kernel<PER><<<batch, 1024, 0, s>>>(b.sabs, p.d_ff, k, lists ? b.sel : nullptr,
+                                          batch > 1 ? b.selw : nullptr);
 }
 
 hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
