@@ -116,7 +116,8 @@ Layout make_layout(const Plan &p) {
   L.weights = align256(L.o_wd + (size_t)p.d_ff * p.d_model * p.esz);
   const size_t pq = (size_t)p.ntile * p.d_model * kTileBytes;
   L.o_psc = align256(pq);
-  L.proxy = align256(L.o_psc + (size_t)p.ntile * p.ngroups * 512 * sizeof(float));
+  L.o_pred = align256(L.o_psc + (size_t)p.ntile * p.ngroups * 512 * sizeof(float));
+  L.proxy = L.o_pred + 256;
   size_t o = 0;
   L.o_part = o;      o = align256(o + (size_t)p.ntile * p.nchunk * B * 512 * sizeof(float));
   L.o_tile_cnt = o;  o = align256(o + (size_t)p.ntile * sizeof(unsigned));
@@ -283,6 +284,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.wd = wb + lay.o_wd;
   b.pq = (uint8_t *)pb;
   b.psc = (float *)(pb + lay.o_psc);
+  b.pred = (unsigned *)(pb + lay.o_pred);
   b.part = (float *)(ws + lay.o_part);
   b.tile_cnt = (unsigned *)(ws + lay.o_tile_cnt);
   b.sabs = (float *)(ws + lay.o_sabs);
@@ -301,6 +303,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   if (e == hipSuccess)
     e = hipMemsetAsync(b.sync, 0, prox::fused_sync_words(L->plan) * sizeof(unsigned),
                        (hipStream_t)stream);
+  if (e == hipSuccess) e = hipMemsetAsync(b.pred, 0, sizeof(unsigned), (hipStream_t)stream);
   if (e != hipSuccess) {
     delete L;
     return hip_fail(e, "prepare kernels");

@@ -15,7 +15,13 @@
 //       then give the exact k-th key T and the tie cutoff J;
 //   P3  Stage 2 up/gate + SwiGLU, one item per 32 consecutive channels: the
 //       channels with digit 1 above b* (selected whatever T is) and those in
-//       bin b* (about twice as many as will be kept), so nothing waits for T;
+//       bin b* (about twice as many as will be kept), so nothing waits for T.
+//       Once the layer has run a top-k call, an item does not wait for b*
+//       either: as soon as its Stage 1 tile is done it computes every channel
+//       from one bin below the previous call's b* up (a guess of the cut kept
+//       per layer), then, when b* is out, any channel of digit 1 >= b* that
+//       the guess missed.  The guess moves work earlier; it never changes
+//       which channels are kept or any value;
 //   P4  Stage 2 down projection, one item per (512 channels, 256 columns):
 //       with T and J known, the kept channels of the range, ascending, give a
 //       partial y; the last item of a column chunk adds the partials in range
@@ -27,8 +33,8 @@
 // the number of work-groups the GPU holds at once, so every work-group is
 // resident; work-group b starts on ticket b (a Stage 1 item) and then takes
 // tickets from a global counter.  An item only ever waits for items with
-// smaller tickets (P2 for all of P1, P3 for P2, P4 for P2 and the P3 items
-// of its range); those are held by running work-groups, and P1 items wait
+// smaller tickets (P2 for all of P1, P3 for its P1 tile and P2, P4 for P2 and
+// the P3 items of its range); those are held by running work-groups, and P1 items wait
 // for nothing, so the schedule cannot deadlock.  Every wait is bounded.  Data
 // passed between work-groups goes through agent-coherent accesses
 // (xstore/xload, sc1 buffer loads); the last work-group to leave resets the
@@ -86,6 +92,7 @@ struct FusedArgs {
   unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
   unsigned *gmask;  // [n_p3][4] per P3 item: 64-bit masks of the channels above bin b*
                     // and of those in it (low word first)
+  unsigned *pred;   // per layer, kept across calls: b* of the last top-k call + 1 (0: none)
   int ts_mode;      // 1: Stage 2 mask |s~| >= tau_s instead of top-k (no P2)
   int act;          // gate activation (gate_act)
   float tau_s;
@@ -133,7 +140,7 @@ struct P2Smem {
 struct P3Smem {
   u4 x[2048];  // x when d_model * element size <= 32 KB
   float ured[2 * kP3Ch];  // dot product of each unit (row) of the item
-  unsigned bstar;
+  unsigned lo, bstar;
 };
 struct P4Smem {
   float red[kFW][kDownCols];
@@ -379,7 +386,10 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
   pick_bin_all<2048>([&](int b) { return sm.h[b]; }, k, sm.wt, &sm.misc[2]);
   const unsigned bstar = sm.misc[2];
   unsigned kk = sm.misc[3];
-  if (tid == 0) xstore_u(&a.sync[kSyncBin], bstar + 1u);
+  if (tid == 0) {
+    xstore_u(&a.sync[kSyncBin], bstar + 1u);
+    xstore_u(a.pred, bstar + 1u);  // the next call's guess of the cut bin
+  }
   unsigned T;
 
   // 2. candidates at b*.
@@ -605,18 +615,27 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int i, int lane) {
 template <bool BF16>
 __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const int c0 = item * kP3Ch;
+  // What to compute first.  Threshold: |s~| >= tau_s, once the item's Stage 1
+  // tile is done.  Top-k: every channel whose digit 1 is at least one bin
+  // below the b* of the layer's previous call (a guess of the cut, which moves
+  // little from token to token), also as soon as the tile is done, so Stage 2
+  // overlaps the rest of Stage 1 and the select; once b* is out, whatever the
+  // guess missed (digit 1 >= b*).  With no guess yet: digit 1 >= b*, after b*.
+  // Only the timing depends on the guess, never the result.
   if (threadIdx.x == 0) {
-    if (a.ts_mode) {
+    unsigned lo = 0u;
+    const unsigned pb = a.ts_mode ? 0u : xload_u(a.pred);
+    if (a.ts_mode || pb >= 2u) {
       wait_geq(&a.tflag[(c0 / kTile) * kSyncStride], 1u, &a.sync[kSyncErr]);
-      sm.bstar = 0u;
+      lo = pb >= 2u ? pb - 2u : 0u;
     } else {
       wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
-      sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
+      lo = xload_u(&a.sync[kSyncBin]) - 1u;
     }
+    sm.lo = lo;
     stamp_wait(a);
   }
   __syncthreads();
-  const unsigned bstar = sm.bstar;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = a.d_ff;
@@ -624,51 +643,65 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const bool valid = lane < kP3Ch && j < n;
   const unsigned key = __float_as_uint(xload(&a.sabs[min(j, n - 1)]));
   const unsigned d1 = key >> 20;
-  // top-k: selected whatever T is / decided later by T and J;
-  // threshold: kept iff |s~| >= tau_s, nothing left to decide
-  const uint64_t dm = a.ts_mode ? __ballot(valid && __uint_as_float(key) >= a.tau_s)
-                                : __ballot(valid && d1 > bstar);
-  const uint64_t bm = a.ts_mode ? 0ull : __ballot(valid && d1 == bstar);
-  // s of both sets: the bin-b* channels are computed before T is known
-  // (about twice the kept ones, a few percent of the step's bytes) so that
-  // nothing here waits for the select.
-  const uint64_t cm = dm | bm;
-  const int nc = (int)__popcll(cm);
   // x to LDS when it fits (every item reads it, so it is L2-resident)
   const uint32_t rowb = (uint32_t)a.d_model * (BF16 ? 2u : 4u);
   const u4 *xs = nullptr;
   if (rowb <= sizeof(sm.x)) {
     for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) sm.x[i] = ((const u4 *)a.x)[i];
-    __syncthreads();
     xs = sm.x;
   }
-  // Work units are rows: unit 2m is the up row, unit 2m + 1 the gate row of
-  // the m-th computed channel.  Wave w takes units w, w + 8, ..., two at a
+  // Two passes: the first set, then (top-k) what b* adds to it.  Each
+  // computes s of the channels of the wave-uniform mask cm, stored by
+  // channel.  Work units are rows: unit 2m is the up row, unit 2m + 1 the gate
+  // row of the m-th channel of cm.  Wave w takes units w, w + 8, ..., two at a
   // time, so every wave streams about the same number of bytes.
-  const int nu = 2 * nc;
-  auto unit_base = [&](int u) {
-    const int ch = c0 + nth_bit(cm, u >> 1, lane);
-    return ((uint32_t)ch * 2u + (uint32_t)(u & 1)) * rowb;
-  };
-  for (int u0 = wv; u0 < nu; u0 += 2 * kFW) {
-    const int u1 = u0 + kFW;
-    float r0, r1;
-    if (u1 < nu) {
-      p3_rows<BF16, 2>(a, xs, unit_base(u0), unit_base(u1), lane, r0, r1);
-      if (lane == 0) {
-        sm.ured[u0] = r0;
-        sm.ured[u1] = r1;
+  uint64_t cm = a.ts_mode ? __ballot(valid && __uint_as_float(key) >= a.tau_s)
+                          : __ballot(valid && d1 >= sm.lo);
+  uint64_t dm = cm, bm = 0ull;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      if (a.ts_mode) break;
+      // top-k: selected whatever T is (digit 1 > b*) / decided later by T
+      // and J (digit 1 = b*, computed before T is known so nothing here
+      // waits for the select)
+      if (threadIdx.x == 0) {
+        wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
+        sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
       }
-    } else {
-      p3_rows<BF16, 1>(a, xs, unit_base(u0), 0u, lane, r0, r1);
-      if (lane == 0) sm.ured[u0] = r0;
+      __syncthreads();
+      const unsigned bstar = sm.bstar;
+      const uint64_t done = cm;
+      dm = __ballot(valid && d1 > bstar);
+      bm = __ballot(valid && d1 == bstar);
+      cm = (dm | bm) & ~done;
+      if (!cm) break;
     }
-  }
-  __syncthreads();
-  if (wv == 0 && ((cm >> lane) & 1ull)) {
-    const unsigned m = __builtin_amdgcn_mbcnt_hi((unsigned)(cm >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo((unsigned)cm, 0u));
-    xstore(&a.sdense[c0 + lane], sm.ured[2 * m] * gate_act(sm.ured[2 * m + 1], a.act));
+    __syncthreads();  // x staged; ured free
+    const int nu = 2 * (int)__popcll(cm);
+    auto unit_base = [&](int u) {
+      const int ch = c0 + nth_bit(cm, u >> 1, lane);
+      return ((uint32_t)ch * 2u + (uint32_t)(u & 1)) * rowb;
+    };
+    for (int u0 = wv; u0 < nu; u0 += 2 * kFW) {
+      const int u1 = u0 + kFW;
+      float r0, r1;
+      if (u1 < nu) {
+        p3_rows<BF16, 2>(a, xs, unit_base(u0), unit_base(u1), lane, r0, r1);
+        if (lane == 0) {
+          sm.ured[u0] = r0;
+          sm.ured[u1] = r1;
+        }
+      } else {
+        p3_rows<BF16, 1>(a, xs, unit_base(u0), 0u, lane, r0, r1);
+        if (lane == 0) sm.ured[u0] = r0;
+      }
+    }
+    __syncthreads();
+    if (wv == 0 && ((cm >> lane) & 1ull)) {
+      const unsigned m = __builtin_amdgcn_mbcnt_hi((unsigned)(cm >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((unsigned)cm, 0u));
+      xstore(&a.sdense[c0 + lane], sm.ured[2 * m] * gate_act(sm.ured[2 * m + 1], a.act));
+    }
   }
   if (threadIdx.x == 0) {
     xstore_u(&a.gmask[4 * item], (unsigned)dm);
@@ -1058,6 +1091,7 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.tflag = b.sync + fused_tflag_word(p);
   a.ghist = b.sync + fused_hist_word(p);
   a.gmask = a.ghist + 2048;
+  a.pred = b.pred;
   a.n_p1 = p.ntile * p.nchunk;
   a.n_p2 = ts_mode ? 0 : 1;
   a.n_p3 = fused_n_p3(p);

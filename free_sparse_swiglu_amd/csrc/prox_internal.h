@@ -30,6 +30,8 @@ struct Bufs {
   // proxy_buf
   uint8_t *pq;     // [ntile][d_model][256] bytes: (code + 8) nibbles, up | gate
   float *psc;      // [ntile][ngroups][2][256] float32 scales
+  unsigned *pred;  // [1] layer state kept across calls: b* of the last batch-1
+                   //     top-k call + 1 (0: none), a guess of the next cut
   // workspace_buf
   float *part;     // [ntile][nchunk][batch][512]   Stage 1 partial sums
   unsigned *tile_cnt;  // [ntile]                  Stage 1 arrival counters
@@ -64,7 +66,7 @@ struct Plan {
 
 struct Layout {
   size_t weights, proxy, workspace;
-  size_t o_wd, o_psc;
+  size_t o_wd, o_psc, o_pred;
   size_t o_part, o_tile_cnt, o_sabs, o_sel, o_selw, o_ssp, o_uni, o_nuni, o_umask,
       o_ypart, o_col_cnt, o_sync, o_xbuf, o_ybuf;
 };

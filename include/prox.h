@@ -78,7 +78,9 @@ typedef struct prox_layer prox_layer;
 
 /* Bytes the caller must allocate (device memory, 256-byte aligned) for:
  *   weights_bytes   relaid exact weights (up/gate channel-major, down row-major)
- *   proxy_bytes     packed INT4 proxy codes and their float32 scales
+ *   proxy_bytes     packed INT4 proxy codes and their float32 scales, plus
+ *                   one word of layer state that batch-1 top-k calls update
+ *                   (a guess of the next cut, used for scheduling only)
  *   workspace_bytes per-call scratch: partial sums, counters, masks, s values
  * Pure host function.  PROX_EINVAL on a null pointer or an invalid shape,
  * PROX_EUNSUPPORTED on a shape outside the limits above.                    */

@@ -400,6 +400,29 @@ def test_fused_path_repeated_launches_are_identical():
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["ragged", "8b"])
+def test_fused_cut_guess_changes_no_bits(name):
+    """A layer keeps the last call's b* as a guess of the next cut, only to
+    start Stage 2 early.  Alternating k moves the cut far from the guess in
+    both directions (guess above the cut: a second pass; below: extra
+    channels computed); every call must give the bits of the same call on a
+    freshly prepared layer (no guess)."""
+    cfg = RAGGED if name == "ragged" else synth.CONFIGS["8b"]
+    gen = "cpu" if name == "ragged" else DEV
+    case = get_case(cfg, gen)
+    W = synth.make_layer(cfg, 0, gen)
+    Wd = [w.to(DEV) for w in W]
+    X = synth.make_inputs(cfg, 6, "guess", 0, gen).to(DEV)
+    ks = [synth.k_for(cfg.d_ff, sp) for sp in (0.7, 0.3, 0.9, 0.5, 0.7, 0.7)]
+    for t, k in enumerate(ks):
+        y = prox.prox_ffn_forward(case.L, X[t], case.tau, k)
+        fresh = prox.prox_prepare_layer(*Wd, cfg.group, 1)
+        y0 = prox.prox_ffn_forward(fresh, X[t], case.tau, k)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), f"call {t}, k={k}"
+        del fresh
+
+
 # ---------------------------------------------------------------------------
 # Stage 2 threshold mask (|s~| >= tau_s) instead of top-k
 # ---------------------------------------------------------------------------
