@@ -52,7 +52,7 @@ enum : int {
   kSyncTicket = 0 * kSyncStride,  // next ticket
   kSyncTiles = 1 * kSyncStride,   // P1 tiles finished
   kSyncSelect = 2 * kSyncStride,  // T and J published (0/1); T at +1, J at +2
-  kSyncExit = 3 * kSyncStride,    // work-groups that left the item loop
+  kSyncExit = 3 * kSyncStride,    // (unused)
   kSyncErr = 4 * kSyncStride,     // sticky error bits (1: a wait timed out, 2: select fallback used)
   kSyncBin = 5 * kSyncStride,     // b* + 1 once published (0 before)
   kSyncP3 = 6 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
@@ -945,13 +945,10 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     }
   }
   // The last work-group out clears the ticket, flags and histogram for the
-  // next launch.
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_flag = __hip_atomic_fetch_add(&a.sync[kSyncExit], 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
-  __syncthreads();
-  if (s_flag) {
+  // next launch.  Every work-group leaves on exactly one ticket >= total from
+  // the counter, so the counter itself says who is last: the one that drew
+  // ticket total + grid - 1 (no second atomic on the way out).
+  if ((unsigned)s_ticket == (unsigned)total + gridDim.x - 1u) {
     constexpr int kCtl = kSyncP3 / kSyncStride;  // control words before the P3 flags
     // control words, P3 flags and tile flags: consecutive lines
     for (int i = threadIdx.x; i < kCtl + a.n_p3 + a.ntile; i += kFT)
