@@ -536,7 +536,20 @@ prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
   hipStream_t s = (hipStream_t)stream;
   for (int l = 0; l < n_layers; ++l) {
     const prox_layer *L = layers[l];
-    hipError_t e = prox::launch_rmsnorm(L->plan, resid, batch, eps, L->bufs.xbuf, s);
+    hipError_t e;
+    if (batch == 1 && k > 0 && L->plan.use_fused && prox::fused_norm_supported(L->plan)) {
+      // one launch per layer: the persistent kernel forms x = RMSNorm(r)
+      // itself, then adds y to r
+      prox::FusedNorm nm;
+      nm.r = resid;
+      nm.eps = eps;
+      nm.xout = L->bufs.xbuf;
+      e = prox::launch_fused(L->plan, L->bufs, L->bufs.xbuf, thresholds[l], k, L->bufs.ybuf,
+                             resid, s, nullptr, false, 0.0f, nm);
+      if (e != hipSuccess) return hip_fail(e, "fused kernel");
+      continue;
+    }
+    e = prox::launch_rmsnorm(L->plan, resid, batch, eps, L->bufs.xbuf, s);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel");
     prox_status st = (k < 0) ? run_dense(L, L->bufs.xbuf, batch, L->bufs.ybuf, resid, s)
                              : run_forward(L, L->bufs.xbuf, batch, thresholds[l], k,
@@ -568,10 +581,18 @@ prox_status prox_stack_forward_ts(const prox_layer *const *layers, int n_layers,
   hipStream_t s = (hipStream_t)stream;
   for (int l = 0; l < n_layers; ++l) {
     const prox_layer *L = layers[l];
-    hipError_t e = prox::launch_rmsnorm(L->plan, resid, 1, eps, L->bufs.xbuf, s);
-    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel");
+    hipError_t e;
+    prox::FusedNorm nm;
+    if (prox::fused_norm_supported(L->plan)) {
+      nm.r = resid;  // x = RMSNorm(r) formed inside the one launch
+      nm.eps = eps;
+      nm.xout = L->bufs.xbuf;
+    } else if ((e = prox::launch_rmsnorm(L->plan, resid, 1, eps, L->bufs.xbuf, s)) !=
+               hipSuccess) {
+      return hip_fail(e, "rmsnorm kernel");
+    }
     e = prox::launch_fused(L->plan, L->bufs, L->bufs.xbuf, thresholds_x[l], 0, L->bufs.ybuf, resid,
-                           s, nullptr, true, thresholds_s[l]);
+                           s, nullptr, true, thresholds_s[l], nm);
     if (e != hipSuccess) return hip_fail(e, "fused kernel");
   }
   return PROX_OK;

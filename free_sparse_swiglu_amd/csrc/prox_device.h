@@ -130,6 +130,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// 1 / sqrt(mean(r^2) + eps) over d_model elements, computed by all NT threads
+// of a work-group in one fixed order (thread t adds r[t]^2, r[t + NT]^2, ...
+// with fmaf, a fixed wave reduction, then the NT / 64 wave sums in order), so
+// every kernel that normalizes the same r with the same NT gets the same bits.
+// part: NT / 64 floats of LDS.
+template <int NT>
+__device__ __forceinline__ float block_inv_rms(const float *r, int d_model, float eps,
+                                               float *part) {
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < d_model; i += NT) ss = fmaf(r[i], r[i], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int q = 0; q < NT / 64; ++q) tot += part[q];
+  __syncthreads();  // part is free again
+  return 1.0f / sqrtf(tot / (float)d_model + eps);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Gate activation: SiLU (act 0, SwiGLU) or the tanh form of GELU (act 1,

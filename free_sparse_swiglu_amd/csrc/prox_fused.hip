@@ -93,12 +93,20 @@ struct FusedArgs {
   unsigned *gmask;  // [n_p3][4] per P3 item: 64-bit masks of the channels above bin b*
                     // and of those in it (low word first)
   unsigned *pred;   // per layer, kept across calls: b* of the last top-k call + 1 (0: none)
+  const float *rnorm;  // when set: x = RMSNorm(rnorm) (float32 residual), formed here
+  float eps;
+  void *xout;          // ... and written here by the tile-0 Stage 1 items
   int ts_mode;      // 1: Stage 2 mask |s~| >= tau_s instead of top-k (no P2)
   int act;          // gate activation (gate_act)
   float tau_s;
   int n_p1, n_p2, n_p3, n_p4;
   unsigned long long *trace;  // optional per-ticket timeline (nullptr: off)
 };
+
+// Wave partial sums of the RMSNorm reduction (block_inv_rms); a work-group of
+// kRmsThreads, like the standalone RMSNorm kernel, gives the same bits.
+static_assert(kFT == kRmsThreads, "RMSNorm reduction order");
+__shared__ float g_rms_part[kFW];
 
 // Timeline stamp of the current item: when its wait for earlier items ended
 // (thread 0 only; 100 MHz s_memrealtime clock).
@@ -156,7 +164,7 @@ struct P4Smem {
 // (see there): one wave per 64-row slice, survivors by ballot, nibble pairs
 // decoded under the bf16 exponent byte for bf16 layers.
 // ---------------------------------------------------------------------------
-template <bool BF16>
+template <bool BF16, bool NORM>
 __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
   constexpr int U = 16;
   const int chunk = item % a.nchunk, t = item / a.nchunk;
@@ -167,6 +175,8 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  float inv = 1.0f;
+  if constexpr (NORM) inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_rms_part);
 
   if (sl < nsl) {
     // the slice's scales first, so that their latency hides behind the rest
@@ -175,7 +185,16 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
         (const float4 *)(a.psc + ((size_t)t * a.ngroups + g) * 512 + (size_t)lane * 8);
     const float4 s0 = sp[0], s1 = sp[1];
     float xl;
-    const uint64_t un = slice_mask<BF16>(a.x, (size_t)sl * 64, a.tau, xl);
+    uint64_t un;
+    if constexpr (NORM) {
+      // x_i = RMSNorm(r)_i in the layer dtype, as launch_rmsnorm stores it
+      const int row = sl * 64 + lane;
+      xl = round_elem<BF16>(a.rnorm[row] * inv);
+      un = __ballot(fabsf(xl) >= a.tau);
+      if (t == 0 && a.xout) st_elem<BF16>(a.xout, row, xl);
+    } else {
+      un = slice_mask<BF16>(a.x, (size_t)sl * 64, a.tau, xl);
+    }
     const float xm = ((un >> lane) & 1ull) ? xl : 0.0f;
     const float xsum = wave_sum(xm);
     const int cnt = (int)__popcll(un);
@@ -612,7 +631,7 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int i, int lane) {
   return (int)__builtin_ctzll(hit);
 }
 
-template <bool BF16>
+template <bool BF16, bool NORM>
 __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const int c0 = item * kP3Ch;
   // What to compute first.  Threshold: |s~| >= tau_s, once the item's Stage 1
@@ -647,7 +666,26 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const uint32_t rowb = (uint32_t)a.d_model * (BF16 ? 2u : 4u);
   const u4 *xs = nullptr;
   if (rowb <= sizeof(sm.x)) {
-    for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) sm.x[i] = ((const u4 *)a.x)[i];
+    if constexpr (NORM) {
+      // x = RMSNorm(r) in the layer dtype, 16 bytes per step
+      const float inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_rms_part);
+      constexpr int EPS16 = BF16 ? 8 : 4;
+      for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) {
+        const float *r = a.rnorm + (size_t)i * EPS16;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (BF16)
+            w[q] = (uint32_t)f32_to_bf16(r[2 * q] * inv) |
+                   ((uint32_t)f32_to_bf16(r[2 * q + 1] * inv) << 16);
+          else
+            w[q] = __float_as_uint(r[q] * inv);
+        }
+        sm.x[i] = u4{w[0], w[1], w[2], w[3]};
+      }
+    } else {
+      for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) sm.x[i] = ((const u4 *)a.x)[i];
+    }
     xs = sm.x;
   }
   // Two passes: the first set, then (top-k) what b* adds to it.  Each
@@ -889,7 +927,9 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
 // ---------------------------------------------------------------------------
 // The persistent kernel.
 // ---------------------------------------------------------------------------
-template <bool BF16>
+// NORM: x = RMSNorm(a.rnorm) is formed inside (a separate instance, so the
+// plain forward keeps its register budget).
+template <bool BF16, bool NORM>
 __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) void ffn_fused_kernel(
     FusedArgs a) {
   __shared__ union {
@@ -925,13 +965,13 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     int r = t;
     if (r < a.n_p1) {
       phase = 1;
-      p1_item<BF16>(a, r, sm.p1, &s_flag);
+      p1_item<BF16, NORM>(a, r, sm.p1, &s_flag);
     } else if ((r -= a.n_p1) < a.n_p2) {
       phase = 2;
       p2_select(a, sm.p2);
     } else if ((r -= a.n_p2) < a.n_p3) {
       phase = 3;
-      p3_item<BF16>(a, r, sm.p3);
+      p3_item<BF16, NORM>(a, r, sm.p3);
     } else {
       phase = 4;
       p4_item<BF16>(a, r - a.n_p3, sm.p4, &s_flag);
@@ -1006,9 +1046,9 @@ __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, 
 // ---------------------------------------------------------------------------
 // Launcher
 // ---------------------------------------------------------------------------
-template <bool BF16>
+template <bool BF16, bool NORM>
 static hipError_t fused_go(FusedArgs &a, hipStream_t s) {
-  auto fn = ffn_fused_kernel<BF16>;
+  auto fn = ffn_fused_kernel<BF16, NORM>;
   static int cap = 0;
   if (!cap) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -1052,10 +1092,18 @@ int fused_items(const Plan &p, bool ts_mode) {
 
 int fused_p3_items(const Plan &p) { return fused_n_p3(p); }
 
+bool fused_norm_supported(const Plan &p) {
+  return (size_t)p.d_model * p.esz <= sizeof(P3Smem::x);
+}
+
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
                         float *resid, hipStream_t s, unsigned long long *trace, bool ts_mode,
-                        float tau_s) {
+                        float tau_s, FusedNorm norm) {
+  if (norm.r && !fused_norm_supported(p)) return hipErrorInvalidValue;
   FusedArgs a{};
+  a.rnorm = norm.r;
+  a.eps = norm.eps;
+  a.xout = norm.xout;
   a.trace = trace;
   a.ts_mode = ts_mode ? 1 : 0;
   a.act = p.act;
@@ -1093,7 +1141,8 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.n_p2 = ts_mode ? 0 : 1;
   a.n_p3 = fused_n_p3(p);
   a.n_p4 = p.ncol * a.nrange;
-  return p.bf16 ? fused_go<true>(a, s) : fused_go<false>(a, s);
+  if (norm.r) return p.bf16 ? fused_go<true, true>(a, s) : fused_go<false, true>(a, s);
+  return p.bf16 ? fused_go<true, false>(a, s) : fused_go<false, false>(a, s);
 }
 
 hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,

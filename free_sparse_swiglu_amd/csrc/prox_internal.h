@@ -21,6 +21,9 @@ constexpr int kMaxDff = 32768;
 constexpr int kMaxDmodel = 16384;
 // LDS a work-group may hold (gfx950: 160 KiB per compute unit).
 constexpr size_t kMaxLds = 160 * 1024;
+// Threads of a work-group that normalizes one residual row (RMSNorm); the
+// persistent kernel normalizes with the same count, hence the same bits.
+constexpr int kRmsThreads = 512;
 
 // Device buffers of one layer (all owned by the caller).
 struct Bufs {
@@ -105,9 +108,19 @@ int fused_ypart_rows(const Plan &p);  // partial-y rows the fused kernel needs
 // trace: optional [fused_items][4] u64 timeline (start, wait end, end,
 // block | phase << 32).  ts_mode: Stage 2 mask |s~| >= tau_s instead of top-k
 // (k is then unused).
+// norm: when norm.r is set, x is not read; the kernel forms x = RMSNorm(r)
+// itself (batch 1, x of at most 32 KiB, bit-identical to launch_rmsnorm) and
+// writes it to norm.xout.
+struct FusedNorm {
+  const float *r = nullptr;
+  float eps = 0.0f;
+  void *xout = nullptr;
+};
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
                         float *resid, hipStream_t s, unsigned long long *trace = nullptr,
-                        bool ts_mode = false, float tau_s = 0.0f);
+                        bool ts_mode = false, float tau_s = 0.0f, FusedNorm norm = FusedNorm());
+// Can launch_fused normalize x itself for this layer?
+bool fused_norm_supported(const Plan &p);
 int fused_items(const Plan &p, bool ts_mode);
 int fused_p3_items(const Plan &p);
 

@@ -889,20 +889,13 @@ __global__ __launch_bounds__(1024) void compact_debug_kernel(const void *x,
 // Stack glue: x = cast(r / sqrt(mean(r^2) + eps)), unit gain.
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *resid,
-                                                      int d_model, float eps,
-                                                      void *x) {
-  __shared__ float ws[4];
+__global__ __launch_bounds__(kRmsThreads) void rmsnorm_kernel(const float *resid, int d_model,
+                                                             float eps, void *x) {
+  __shared__ float part[kRmsThreads / 64];
   const int b = blockIdx.x;
   const float *r = resid + (size_t)b * d_model;
-  float ss = 0.0f;
-  for (int i = threadIdx.x; i < d_model; i += 256) ss = fmaf(r[i], r[i], ss);
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = ((ws[0] + ws[1]) + ws[2]) + ws[3];
-  const float inv = 1.0f / sqrtf(tot / (float)d_model + eps);
-  for (int i = threadIdx.x; i < d_model; i += 256)
+  const float inv = block_inv_rms<kRmsThreads>(r, d_model, eps, part);
+  for (int i = threadIdx.x; i < d_model; i += kRmsThreads)
     st_elem<BF16>(x, (size_t)b * d_model + i, r[i] * inv);
 }
 
@@ -1239,9 +1232,9 @@ hipError_t launch_compact_debug(const Plan &p, const void *x, int batch,
 hipError_t launch_rmsnorm(const Plan &p, const float *resid, int batch,
                           float eps, void *x, hipStream_t s) {
   if (p.bf16)
-    rmsnorm_kernel<true><<<batch, 256, 0, s>>>(resid, p.d_model, eps, x);
+    rmsnorm_kernel<true><<<batch, kRmsThreads, 0, s>>>(resid, p.d_model, eps, x);
   else
-    rmsnorm_kernel<false><<<batch, 256, 0, s>>>(resid, p.d_model, eps, x);
+    rmsnorm_kernel<false><<<batch, kRmsThreads, 0, s>>>(resid, p.d_model, eps, x);
   return hipGetLastError();
 }
 

@@ -328,6 +328,49 @@ def test_stack_parity(k_frac):
         assert rel_err(r.cpu().numpy(), r_ref) <= 2e-2
 
 
+@pytest.mark.parametrize("mode", ["topk", "threshold"])
+def test_stack_fused_norm_matches_separate_launches(mode):
+    """For one token the stack runs one launch per layer: the persistent
+    kernel forms x = RMSNorm(r) itself.  Layer by layer, the residual must
+    carry the same bits as the separate RMSNorm kernel + forward + add."""
+    cfg = synth.Config("stacksmall", 1024, 2816, 128, "bf16", "student_t", 0.5, 32, (0.7,))
+    nl = 3
+    layers, taus, tss = [], [], []
+    ws = None
+    for l in range(nl):
+        W = synth.make_layer(cfg, l, "cpu")
+        L = prox.prox_prepare_layer(*[w.to(DEV) for w in W], cfg.group, 1, workspace=ws)
+        ws = L.workspace
+        layers.append(L)
+        taus.append(synth.layer_tau(cfg, l, "cpu") * 0.5)
+    k = synth.k_for(cfg.d_ff, 0.7)
+    R0 = synth.make_inputs(cfg, 2, "stacknorm", 0, "cpu").float().to(DEV)
+    if mode == "threshold":
+        # tau_s per layer: the 0.7 quantile of |s~| on the first token's inputs
+        r = R0[0].clone()
+        for l in range(nl):
+            x = prox.prox_rmsnorm(layers[l], r)
+            out = prox.prox_ffn_forward_debug(layers[l], x[None], taus[l], k)
+            tss.append(float(torch.quantile(out["s_abs"][0].float(), 0.7)))
+            r += out["y"][0].float()
+    for t in range(R0.shape[0]):
+        ra = R0[t].clone()
+        if mode == "topk":
+            prox.prox_stack_forward(layers, taus, k, ra)
+        else:
+            prox.prox_stack_forward_ts(layers, taus, tss, ra)
+        rb = R0[t].clone()
+        for l in range(nl):
+            x = prox.prox_rmsnorm(layers[l], rb)
+            if mode == "topk":
+                y = prox.prox_ffn_forward(layers[l], x, taus[l], k)
+            else:
+                y = prox.prox_ffn_forward_ts(layers[l], x, taus[l], tss[l])
+            rb += y.float()
+        torch.cuda.synchronize()
+        assert torch.equal(ra, rb), f"token {t}: max diff {float((ra - rb).abs().max())}"
+
+
 # ---------------------------------------------------------------------------
 # Full-size shapes (8B, 14B, 70B), in the launch configuration bench.py times
 # ---------------------------------------------------------------------------
