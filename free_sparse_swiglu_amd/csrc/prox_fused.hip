@@ -829,25 +829,26 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
   // finish.
   if (nr > 0) load_batch(0);
   if (tid < 64) {
-    // lanes 0..QPR-1: the range's P3 items; the others: the select (T, J),
-    // which the threshold mode does not have
     const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
-    const unsigned *f = (lane < QPR || a.ts_mode)
-                            ? &a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride]
-                            : &a.sync[kSyncSelect];
-    wave_wait_flags(f, &a.sync[kSyncErr]);
+    wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride], &a.sync[kSyncErr]);
     if (lane == 0) stamp_wait(a);
   }
   __syncthreads();
-  // 3. s of each listed channel, 0 for a bin-b* channel below the cut.
+  // 3. s of each listed channel (final once the range's P3 items are done,
+  // the bin-b* ones included), loaded while the select may still run; then
+  // 0 for a bin-b* channel below the cut.
   {
+    const float sj = tid < nr ? xload(&a.sdense[sm.rs[tid]]) : 0.0f;
+    if (!a.ts_mode) {
+      if (tid == 0) wait_geq(&a.sync[kSyncSelect], 1u, &a.sync[kSyncErr]);
+      __syncthreads();
+    }
     const unsigned T = a.ts_mode ? 0u : xload_u(&a.sync[kSyncSelect + 1]);
     const int J = a.ts_mode ? n : (int)xload_u(&a.sync[kSyncSelect + 2]);
     if (tid < nr) {
       const int ch = sm.rs[tid];
       const unsigned key = sm.rk[tid];
-      const float s = xload(&a.sdense[ch]);
-      sm.sv[tid] = (key > T || (key == T && ch <= J)) ? s : 0.0f;
+      sm.sv[tid] = (key > T || (key == T && ch <= J)) ? sj : 0.0f;
     }
   }
   __syncthreads();
