@@ -146,10 +146,12 @@ struct ProxyArgs {
   int act;  // gate activation (gate_act)
 };
 
+// 5..8 tokens: 8 rows per stage, so that the accumulators of all tokens and
+// two stages of codes fit 128 VGPRs and two work-groups share a CU.
 template <int NB, bool BF16>
-__global__ __launch_bounds__(512) void proxy_kernel(ProxyArgs a) {
+__global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a) {
   constexpr int NW = 8;             // waves (64-row slices) per work-group
-  constexpr int U = 16;             // rows per pipeline stage
+  constexpr int U = NB > 4 ? 8 : 16;  // rows per pipeline stage
   constexpr int LL = 64 + 3 * U;    // list length incl. padding for prefetch
   __shared__ float red[NW][512];
   __shared__ __attribute__((aligned(16))) int rl[NW][LL];       // surviving rows
