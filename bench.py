@@ -559,8 +559,8 @@ def main():
     # read by the library when a layer is prepared
     os.environ["PROX_BATCH_GEMV"] = args.batch_gemv
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
-              "supported (the multi-GPU split is a design note, not a measured path)",
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the library "
+              "runs one layer on one GPU; splitting a layer over GPUs is not implemented)",
               file=sys.stderr)
         sys.exit(2)
     import torch
