@@ -564,63 +564,52 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
 // elements), dot2 with x, s = u * SiLU(g), stored by channel.  The kept
 // channels are dealt to the 8 waves in ascending order.
 // ---------------------------------------------------------------------------
-// CH 16-byte steps of ROWS rows (byte offsets base0, base1 in the up/gate
-// weights) in flight, then their dot products with x (from LDS when xs is
-// given, else from global memory).
-template <bool BF16, int CH, int ROWS>
+// CH 16-byte steps of one row (byte offset base in the up/gate weights) in
+// flight, then their dot products with x (from LDS when xs is given, else
+// from global memory).
+template <bool BF16, int CH>
 __device__ __forceinline__ void p3_pass(const FusedArgs &a, const u4 *xs, __amdgpu_buffer_rsrc_t rs,
-                                        uint32_t base0, uint32_t base1, int m0, int lane,
-                                        float &acc0, float &acc1) {
-  u4 w0[CH], w1[CH];
+                                        uint32_t base, int m0, int lane, float &acc) {
+  u4 w[CH];
 #pragma unroll
   for (int m = 0; m < CH; ++m) {
     const uint32_t off = (uint32_t)((m0 + m) * 64 + lane) * 16u;
-    w0[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, base0, kNT);
-    if (ROWS == 2) w1[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, base1, kNT);
+    w[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, base, kNT);
   }
   if (xs) {
 #pragma unroll
-    for (int m = 0; m < CH; ++m) {
-      const u4 xr = xs[(m0 + m) * 64 + lane];
-      acc0 = dot16<BF16>(w0[m], xr, acc0);
-      if (ROWS == 2) acc1 = dot16<BF16>(w1[m], xr, acc1);
-    }
+    for (int m = 0; m < CH; ++m) acc = dot16<BF16>(w[m], xs[(m0 + m) * 64 + lane], acc);
   } else {
     u4 xr[CH];
 #pragma unroll
     for (int m = 0; m < CH; ++m) xr[m] = ((const u4 *)a.x)[(m0 + m) * 64 + lane];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < CH; ++m) {
-      acc0 = dot16<BF16>(w0[m], xr[m], acc0);
-      if (ROWS == 2) acc1 = dot16<BF16>(w1[m], xr[m], acc1);
-    }
+    for (int m = 0; m < CH; ++m) acc = dot16<BF16>(w[m], xr[m], acc);
   }
 }
 
-// Dot products of x with one or two whole rows of the up/gate weights.  One
-// 16-byte step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a
-// multiple of 1024, so the steps tile the row exactly.  With x in LDS a pass
-// holds 8 steps of two rows (16 KB per wave in flight); with x in registers 4.
-template <bool BF16, int ROWS>
-__device__ __forceinline__ void p3_rows(const FusedArgs &a, const u4 *xs, uint32_t base0,
-                                        uint32_t base1, int lane, float &r0, float &r1) {
+// Dot product of x with one whole row of the up/gate weights.  One 16-byte
+// step covers 64 lanes x 16 bytes of a row; d_model * ESZ is a multiple of
+// 1024, so the steps tile the row exactly.  A pass keeps 4 steps (4 KB per
+// wave) in flight: P3 runs while Stage 1, the select and P4 wait on chains
+// of dependent memory round trips, and every byte P3 keeps in flight
+// lengthens those round trips without adding bandwidth (HBM is already
+// saturated).  Measured at 8B: 2 rows x 8 KB per wave 46.0 us, 1 row x 8 KB
+// 45.0 us, 1 row x 4 KB 44.3 us, 1 row x 2 KB 45.6 us.
+template <bool BF16>
+__device__ __forceinline__ float p3_row(const FusedArgs &a, const u4 *xs, uint32_t base, int lane) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
   const int nstep = (int)(((uint32_t)a.d_model * (BF16 ? 2u : 4u)) >> 10);
-  float acc0 = 0.0f, acc1 = 0.0f;
+  float acc = 0.0f;
   int m0 = 0;
-  if (xs)
-    for (; m0 + 8 <= nstep; m0 += 8)
-      p3_pass<BF16, 8, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
-  for (; m0 + 4 <= nstep; m0 += 4)
-    p3_pass<BF16, 4, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
+  for (; m0 + 4 <= nstep; m0 += 4) p3_pass<BF16, 4>(a, xs, rs, base, m0, lane, acc);
   if (m0 + 2 <= nstep) {
-    p3_pass<BF16, 2, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
+    p3_pass<BF16, 2>(a, xs, rs, base, m0, lane, acc);
     m0 += 2;
   }
-  if (m0 < nstep) p3_pass<BF16, 1, ROWS>(a, xs, rs, base0, base1, m0, lane, acc0, acc1);
-  r0 = wave_sum(acc0);
-  r1 = ROWS == 2 ? wave_sum(acc1) : 0.0f;
+  if (m0 < nstep) p3_pass<BF16, 1>(a, xs, rs, base, m0, lane, acc);
+  return wave_sum(acc);
 }
 
 // The i-th set bit (0-based) of a wave-uniform mask, found by all lanes.
@@ -691,7 +680,7 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   // Two passes: the first set, then (top-k) what b* adds to it.  Each
   // computes s of the channels of the wave-uniform mask cm, stored by
   // channel.  Work units are rows: unit 2m is the up row, unit 2m + 1 the gate
-  // row of the m-th channel of cm.  Wave w takes units w, w + 8, ..., two at a
+  // row of the m-th channel of cm.  Wave w takes units w, w + 8, ..., one at a
   // time, so every wave streams about the same number of bytes.
   uint64_t cm = a.ts_mode ? __ballot(valid && __uint_as_float(key) >= a.tau_s)
                           : __ballot(valid && d1 >= sm.lo);
@@ -720,19 +709,9 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
       const int ch = c0 + nth_bit(cm, u >> 1, lane);
       return ((uint32_t)ch * 2u + (uint32_t)(u & 1)) * rowb;
     };
-    for (int u0 = wv; u0 < nu; u0 += 2 * kFW) {
-      const int u1 = u0 + kFW;
-      float r0, r1;
-      if (u1 < nu) {
-        p3_rows<BF16, 2>(a, xs, unit_base(u0), unit_base(u1), lane, r0, r1);
-        if (lane == 0) {
-          sm.ured[u0] = r0;
-          sm.ured[u1] = r1;
-        }
-      } else {
-        p3_rows<BF16, 1>(a, xs, unit_base(u0), 0u, lane, r0, r1);
-        if (lane == 0) sm.ured[u0] = r0;
-      }
+    for (int u = wv; u < nu; u += kFW) {
+      const float r = p3_row<BF16>(a, xs, unit_base(u), lane);
+      if (lane == 0) sm.ured[u] = r;
     }
     __syncthreads();
     if (wv == 0 && ((cm >> lane) & 1ull)) {
@@ -762,7 +741,9 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
-  constexpr int U = BF16 ? 20 : 8;  // rows per wave per batch
+  // rows per wave per batch: 10 rows x 512 B; 20 measured 0.5 us slower at 8B
+  // (more bytes in flight behind which the dependent round trips queue)
+  constexpr int U = BF16 ? 10 : 8;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int QPR = kP4Ch / kP3Ch;  // P3 items per range
   static_assert(QPR < 64, "one wave polls the range's P3 flags and the select flag");
