@@ -295,6 +295,7 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
     xstore(&part[e], v);
   }
   if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, s_flag)) return;
+  __builtin_amdgcn_s_setprio(3);  // the tile epilogue gates the select and P3: issue first
 
   // Tile epilogue: |s~| = |u~ * SiLU(g~)| of the tile's 256 channels, and the
   // tile's counts of digit 1 (bits 30..20 of |s~|) added to the global
@@ -327,6 +328,7 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
     xstore_u(&a.tflag[t * kSyncStride], 1u);
     __hip_atomic_fetch_add(&a.sync[kSyncTiles], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -379,6 +381,9 @@ __device__ __forceinline__ void pick_bin_all(H hist, unsigned kk, unsigned *wt, 
 }
 
 __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
+  // The select is on the critical path and shares its CU with P3 waves that
+  // mostly wait on memory: its waves issue first.
+  __builtin_amdgcn_s_setprio(3);
   if (threadIdx.x == 0) {
     wait_geq(&a.sync[kSyncTiles], (unsigned)a.ntile, &a.sync[kSyncErr]);
     stamp_wait(a);
@@ -556,6 +561,7 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) xstore_u(&a.sync[kSyncSelect], 1u);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // ---------------------------------------------------------------------------
