@@ -18,8 +18,8 @@
 //       bin b* (about twice as many as will be kept), so nothing waits for T.
 //       Once the layer has run a top-k call, an item does not wait for b*
 //       either: as soon as its Stage 1 tile is done it computes every channel
-//       from one bin below the previous call's b* up (a guess of the cut kept
-//       per layer), then, when b* is out, any channel of digit 1 >= b* that
+//       from the previous call's b* up (a guess of the cut kept per layer),
+//       then, when b* is out, any channel of digit 1 >= b* that
 //       the guess missed.  The guess moves work earlier; it never changes
 //       which channels are kept or any value;
 //   P4  Stage 2 down projection, one item per (512 channels, 256 columns):
@@ -630,18 +630,19 @@ template <bool BF16, bool NORM>
 __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const int c0 = item * kP3Ch;
   // What to compute first.  Threshold: |s~| >= tau_s, once the item's Stage 1
-  // tile is done.  Top-k: every channel whose digit 1 is at least one bin
-  // below the b* of the layer's previous call (a guess of the cut, which moves
-  // little from token to token), also as soon as the tile is done, so Stage 2
-  // overlaps the rest of Stage 1 and the select; once b* is out, whatever the
-  // guess missed (digit 1 >= b*).  With no guess yet: digit 1 >= b*, after b*.
-  // Only the timing depends on the guess, never the result.
+  // tile is done.  Top-k: every channel whose digit 1 is at least the b* of
+  // the layer's previous call (a guess of the cut, which moves little from
+  // token to token), also as soon as the tile is done, so Stage 2 overlaps the
+  // rest of Stage 1 and the select; once b* is out, whatever the guess missed
+  // (digit 1 >= b*).  With no guess yet: digit 1 >= b*, after b*.  Only the
+  // timing depends on the guess, never the result.  (Starting one bin lower,
+  // to catch more of a falling cut, measured 0.3 us slower at 8B.)
   if (threadIdx.x == 0) {
     unsigned lo = 0u;
     const unsigned pb = a.ts_mode ? 0u : xload_u(a.pred);
     if (a.ts_mode || pb >= 2u) {
       wait_geq(&a.tflag[(c0 / kTile) * kSyncStride], 1u, &a.sync[kSyncErr]);
-      lo = pb >= 2u ? pb - 2u : 0u;
+      lo = pb >= 2u ? pb - 1u : 0u;
     } else {
       wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
       lo = xload_u(&a.sync[kSyncBin]) - 1u;
