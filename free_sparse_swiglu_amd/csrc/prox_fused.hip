@@ -51,7 +51,8 @@ namespace prox {
 enum : int {
   kSyncTicket = 0 * kSyncStride,  // next ticket
   kSyncTiles = 1 * kSyncStride,   // P1 tiles finished
-  kSyncSelect = 2 * kSyncStride,  // T and J published (0/1); T at +1, J at +2
+  kSyncSelect = 2 * kSyncStride,  // one 64-bit word: T (low), J + 1 (high; 0 until published);
+                                  // T, J again at +2, +3 (kept after the launch)
   kSyncExit = 3 * kSyncStride,    // (unused)
   kSyncErr = 4 * kSyncStride,     // sticky error bits (1: a wait timed out, 2: select fallback used)
   kSyncBin = 5 * kSyncStride,     // b* + 1 once published (0 before)
@@ -102,6 +103,28 @@ struct FusedArgs {
   int n_p1, n_p2, n_p3, n_p4;
   unsigned long long *trace;  // optional per-ticket timeline (nullptr: off)
 };
+
+// The select's result: T and J + 1 as one agent-coherent 64-bit word (J + 1
+// is never 0, so a nonzero high half means published).
+__device__ __forceinline__ void xstore_tj(unsigned *w, unsigned T, int J) {
+  const unsigned long long v = (unsigned long long)T | ((unsigned long long)(unsigned)(J + 1) << 32);
+  __hip_atomic_store((unsigned long long *)w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Bounded wait for it (like wait_geq): *T, *J receive the values.
+__device__ __forceinline__ void wait_tj(const unsigned *w, unsigned *err, unsigned *T, unsigned *J) {
+  unsigned n = 0;
+  unsigned long long v;
+  while (((v = __hip_atomic_load((const unsigned long long *)w, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT)) >> 32) == 0ull) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++n > (1u << 22)) {
+      atomicOr(err, 1u);
+      break;
+    }
+  }
+  *T = (unsigned)v;
+  *J = (unsigned)(v >> 32) - 1u;
+}
 
 // Wave partial sums of the RMSNorm reduction (block_inv_rms); a work-group of
 // kRmsThreads, like the standalone RMSNorm kernel, gives the same bits.
@@ -157,6 +180,7 @@ struct P4Smem {
   float sv[kP4Ch];     // their s (0 when below the cut)
   unsigned wcnt[kFW];
   unsigned bstar;
+  unsigned tj[2];      // T and J of the select
 };
 
 // ---------------------------------------------------------------------------
@@ -553,14 +577,16 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
       const uint64_t hit = __ballot(((me >> lane) & 1ull) && rank + 1u == r1);
       J = (who && hit) ? (g << 6) + (int)__builtin_ctzll(hit) : n - 1;
     }
+    // T and J go out in one 64-bit store, which is also the flag: a waiter
+    // gets both with the load that sees it, and nothing here waits for an
+    // earlier store to land first.
     if (lane == 0) {
-      xstore_u(&a.sync[kSyncSelect + 1], T);
-      xstore_u(&a.sync[kSyncSelect + 2], (unsigned)J);
+      // a copy that outlives the launch's reset, for the list kernel
+      xstore_u(&a.sync[kSyncSelect + 2], T);
+      xstore_u(&a.sync[kSyncSelect + 3], (unsigned)J);
+      xstore_tj(&a.sync[kSyncSelect], T, J);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) xstore_u(&a.sync[kSyncSelect], 1u);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -828,11 +854,11 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
   {
     const float sj = tid < nr ? xload(&a.sdense[sm.rs[tid]]) : 0.0f;
     if (!a.ts_mode) {
-      if (tid == 0) wait_geq(&a.sync[kSyncSelect], 1u, &a.sync[kSyncErr]);
+      if (tid == 0) wait_tj(&a.sync[kSyncSelect], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1]);
       __syncthreads();
     }
-    const unsigned T = a.ts_mode ? 0u : xload_u(&a.sync[kSyncSelect + 1]);
-    const int J = a.ts_mode ? n : (int)xload_u(&a.sync[kSyncSelect + 2]);
+    const unsigned T = a.ts_mode ? 0u : sm.tj[0];
+    const int J = a.ts_mode ? n : (int)sm.tj[1];
     if (tid < nr) {
       const int ch = sm.rs[tid];
       const unsigned key = sm.rk[tid];
@@ -982,6 +1008,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     // control words, P3 flags and tile flags: consecutive lines
     for (int i = threadIdx.x; i < kCtl + a.n_p3 + a.ntile; i += kFT)
       if (i * kSyncStride != kSyncErr) xstore_u(&a.sync[i * kSyncStride], 0u);
+    if (threadIdx.x == 0) xstore_u(&a.sync[kSyncSelect + 1], 0u);
     for (int i = threadIdx.x; i < 2048; i += kFT) xstore_u(&a.ghist[i], 0u);
   }
 }
@@ -997,8 +1024,8 @@ __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, 
   __shared__ unsigned base;
   if (threadIdx.x == 0) base = 0u;
   __syncthreads();
-  const unsigned T = tj[1];
-  const int J = (int)tj[2];
+  const unsigned T = tj[2];
+  const int J = (int)tj[3];
   for (int q0 = 0; q0 < n_p3; q0 += kFT) {
     const int q = q0 + (int)threadIdx.x;
     uint64_t m = 0ull;
