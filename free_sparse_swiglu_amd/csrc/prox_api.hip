@@ -131,6 +131,7 @@ Layout make_layout(const Plan &p) {
   const size_t yrows = std::max((size_t)p.nrc * B, (size_t)fused_ypart_rows(p));
   L.o_ypart = o;     o = align256(o + yrows * p.d_model * sizeof(float));
   L.o_col_cnt = o;   o = align256(o + (size_t)p.ncol * sizeof(unsigned));
+  L.o_ucnt = o;      o = align256(o + sizeof(unsigned));
   L.o_sync = o;      o = align256(o + fused_sync_words(p) * sizeof(unsigned));
   L.o_xbuf = o;      o = align256(o + B * p.d_model * p.esz);
   L.o_ybuf = o;      o = align256(o + B * p.d_model * p.esz);
@@ -185,12 +186,7 @@ prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau
   if ((e = prox::launch_topk(p, b, batch, k, batch == 1 || lists, s)) != hipSuccess)
     return hip_fail(e, "top-k kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
-  const int mode = batch == 1 ? 0 : 1;
-  if (mode == 1) {
-    if ((e = prox::launch_union(p, b, batch, k, s)) != hipSuccess)
-      return hip_fail(e, "mask union kernel");
-    if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
-  }
+  const int mode = batch == 1 ? 0 : 1;  // several tokens: the top-k launch also built the union
   if ((e = prox::launch_upgate(p, b, x, batch, mode, k, s)) != hipSuccess)
     return hip_fail(e, "stage 2 up/gate kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
@@ -296,6 +292,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.umask = (uint8_t *)(ws + lay.o_umask);
   b.ypart = (float *)(ws + lay.o_ypart);
   b.col_cnt = (unsigned *)(ws + lay.o_col_cnt);
+  b.ucnt = (unsigned *)(ws + lay.o_ucnt);
   b.sync = (unsigned *)(ws + lay.o_sync);
   b.xbuf = ws + lay.o_xbuf;
   b.ybuf = ws + lay.o_ybuf;
@@ -605,8 +602,8 @@ prox_status prox_ffn_forward_profiled(const prox_layer *layer, const void *x, in
   g_err.clear();
   prox_status st = check_forward_args(layer, x, batch, threshold, k, y);
   if (st != PROX_OK) return st;
-  if (!events || n_events < 6 || !n_recorded)
-    return fail(PROX_EINVAL, "events (at least 6) and n_recorded are required");
+  if (!events || n_events < 5 || !n_recorded)
+    return fail(PROX_EINVAL, "events (at least 5) and n_recorded are required");
   EventLog lg{events, n_events, 0};
   st = run_forward(layer, x, batch, threshold, k, y, nullptr, (hipStream_t)stream, &lg);
   *n_recorded = lg.n;

@@ -48,6 +48,7 @@ struct Bufs {
   uint8_t *umask;  // [d_ff]                        token bits per union entry
   float *ypart;    // [nrc][batch][d_model]         Stage 2 down partial sums
   unsigned *col_cnt;  // [ncol]                    Stage 2 arrival counters
+  unsigned *ucnt;  // [1]                           top-k work-groups done (several tokens)
   unsigned *sync;  // fused kernel: tickets, flags, histogram, masks (fused_sync_words)
   void *xbuf;      // [batch][d_model] dtype         stack: normalized input
   void *ybuf;      // [batch][d_model] dtype         stack: layer output
@@ -71,7 +72,7 @@ struct Layout {
   size_t weights, proxy, workspace;
   size_t o_wd, o_psc, o_pred;
   size_t o_part, o_tile_cnt, o_sabs, o_sel, o_selw, o_ssp, o_uni, o_nuni, o_umask,
-      o_ypart, o_col_cnt, o_sync, o_xbuf, o_ybuf;
+      o_ypart, o_col_cnt, o_ucnt, o_sync, o_xbuf, o_ybuf;
 };
 
 Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act);
@@ -88,8 +89,6 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
                         float tau, hipStream_t s);
 hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
                        hipStream_t s);
-hipError_t launch_union(const Plan &p, const Bufs &b, int batch, int k,
-                        hipStream_t s);
 // mode: 0 = one token over sel, 1 = batch over the union, 2 = dense
 hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
                          int mode, int n, hipStream_t s);

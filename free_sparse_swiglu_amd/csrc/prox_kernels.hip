@@ -381,14 +381,49 @@ __device__ __forceinline__ void pick_bin(const unsigned *hist, unsigned kk,
   }
 }
 
+// Union of the per-token mask words (several tokens): U ascending, plus for
+// each entry the bit set of tokens whose mask holds it.  All 1024 threads of
+// one work-group; thread w owns mask word w (channels 32 w .. 32 w + 31, d_ff
+// <= 32768), reads that word of every token, and writes its union entries at
+// its exclusive prefix of the word popcounts.
+__device__ __forceinline__ void mask_union(const unsigned *selw, int d_ff, int nb, int *uni,
+                                           int *nuni, uint8_t *umask, unsigned *wsum) {
+  const int w = threadIdx.x;
+  const int words = (d_ff + 31) >> 5;
+  unsigned tw[kMaxBatch], u = 0u;
+#pragma unroll
+  for (int b = 0; b < kMaxBatch; ++b) {
+    tw[b] = (b < nb && w < words) ? xload_u(&selw[(size_t)b * words + w]) : 0u;
+    u |= tw[b];
+  }
+  unsigned total;
+  unsigned pos = block_excl_scan<16>((unsigned)__popc(u), wsum, total);
+  while (u) {
+    const int bit = __builtin_ctz(u);
+    u &= u - 1u;
+    unsigned m = 0u;
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) m |= ((tw[b] >> bit) & 1u) << b;
+    uni[pos] = w * 32 + bit;
+    umask[pos] = (uint8_t)m;
+    ++pos;
+  }
+  if (w == 0) *nuni = (int)total;
+}
+
+// With several tokens (ucnt set) the last work-group to finish also builds
+// the union of the masks, so top-k and union are one launch.
 template <int PER>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff, int k,
-                                                    int *sel, unsigned *selw) {
+                                                    int *sel, unsigned *selw, unsigned *ucnt,
+                                                    int *uni, int *nuni, uint8_t *umask) {
   __shared__ unsigned h1[2048];
   __shared__ unsigned h2[2048];
   __shared__ unsigned h3[512];
   __shared__ unsigned cnt[PER * 16];
   __shared__ unsigned s_bin, s_kk;
+  __shared__ unsigned wsum[16];
+  __shared__ int s_last;
   const int b = blockIdx.x;
   if (k <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -445,97 +480,66 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
       const int j = e * 1024 + tid;
       const uint64_t km = __ballot(j < d_ff && key[e] >= T);
       const int wi = e * 32 + w * 2;
-      if (lane == 0 && wi < words) outw[wi] = (unsigned)km;
-      if (lane == 1 && wi + 1 < words) outw[wi + 1] = (unsigned)(km >> 32);
+      if (lane == 0 && wi < words) xstore_u(&outw[wi], (unsigned)km);
+      if (lane == 1 && wi + 1 < words) xstore_u(&outw[wi + 1], (unsigned)(km >> 32));
     }
-    return;
-  }
+  } else {
 
-  // Compaction.  Pass A: per (slot, wave) counts of keys > T and == T.
-  uint64_t mgt[PER], meq[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const bool ok = e * 1024 + tid < d_ff;
-    mgt[e] = __ballot(ok && key[e] > T);
-    meq[e] = __ballot(ok && key[e] == T);
-    if (lane == 0) cnt[e * 16 + w] = ((unsigned)__popcll(meq[e]) << 16) | (unsigned)__popcll(mgt[e]);
+    // Compaction.  Pass A: per (slot, wave) counts of keys > T and == T.
+    uint64_t mgt[PER], meq[PER];
+  #pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const bool ok = e * 1024 + tid < d_ff;
+      mgt[e] = __ballot(ok && key[e] > T);
+      meq[e] = __ballot(ok && key[e] == T);
+      if (lane == 0) cnt[e * 16 + w] = ((unsigned)__popcll(meq[e]) << 16) | (unsigned)__popcll(mgt[e]);
+    }
+    __syncthreads();
+    // Wave 0: exclusive scan of the PER*16 counts in (slot, wave) order.
+    if (w == 0) {
+      constexpr int CPL = (PER * 16 + 63) / 64;
+      unsigned c[CPL], sum = 0;
+  #pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int q = lane * CPL + i;
+        c[i] = q < PER * 16 ? cnt[q] : 0u;
+        sum += c[i];
+      }
+      unsigned run = wave_incl_scan(sum) - sum;
+  #pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int q = lane * CPL + i;
+        if (q < PER * 16) cnt[q] = run;
+        run += c[i];
+      }
+    }
+    __syncthreads();
+    // Pass B: positions.  Before this key: gt_b keys > T and eq_b keys == T;
+    // it is kept if > T, or == T with eq_b < kk; its position is gt_b + min(eq_b, kk).
+    const uint64_t below = (1ull << lane) - 1ull;
+  #pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = e * 1024 + tid;
+      const unsigned base = cnt[e * 16 + w];
+      const unsigned gt_b = (base & 0xffffu) + (unsigned)__popcll(mgt[e] & below);
+      const unsigned eq_b = (base >> 16) + (unsigned)__popcll(meq[e] & below);
+      const bool kept = j < d_ff && (key[e] > T || (key[e] == T && eq_b < kk));
+      if (kept && out) out[key[e] > T ? gt_b + min(eq_b, kk) : gt_b + eq_b] = j;
+      // The same mask as bit words: this wave's 64 channels are words
+      // 32 e + 2 w and 32 e + 2 w + 1.
+      if (outw) {
+        const uint64_t km = __ballot(kept);
+        const int wi = e * 32 + w * 2;
+        if (lane == 0 && wi < words) xstore_u(&outw[wi], (unsigned)km);
+        if (lane == 1 && wi + 1 < words) xstore_u(&outw[wi + 1], (unsigned)(km >> 32));
+      }
+    }
   }
-  __syncthreads();
-  // Wave 0: exclusive scan of the PER*16 counts in (slot, wave) order.
-  if (w == 0) {
-    constexpr int CPL = (PER * 16 + 63) / 64;
-    unsigned c[CPL], sum = 0;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int q = lane * CPL + i;
-      c[i] = q < PER * 16 ? cnt[q] : 0u;
-      sum += c[i];
-    }
-    unsigned run = wave_incl_scan(sum) - sum;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int q = lane * CPL + i;
-      if (q < PER * 16) cnt[q] = run;
-      run += c[i];
-    }
-  }
-  __syncthreads();
-  // Pass B: positions.  Before this key: gt_b keys > T and eq_b keys == T;
-  // it is kept if > T, or == T with eq_b < kk; its position is gt_b + min(eq_b, kk).
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int j = e * 1024 + tid;
-    const unsigned base = cnt[e * 16 + w];
-    const unsigned gt_b = (base & 0xffffu) + (unsigned)__popcll(mgt[e] & below);
-    const unsigned eq_b = (base >> 16) + (unsigned)__popcll(meq[e] & below);
-    const bool kept = j < d_ff && (key[e] > T || (key[e] == T && eq_b < kk));
-    if (kept && out) out[key[e] > T ? gt_b + min(eq_b, kk) : gt_b + eq_b] = j;
-    // The same mask as bit words: this wave's 64 channels are words
-    // 32 e + 2 w and 32 e + 2 w + 1.
-    if (outw) {
-      const uint64_t km = __ballot(kept);
-      const int wi = e * 32 + w * 2;
-      if (lane == 0 && wi < words) outw[wi] = (unsigned)km;
-      if (lane == 1 && wi + 1 < words) outw[wi + 1] = (unsigned)(km >> 32);
-    }
+  if (ucnt) {
+    if (!arrive_last(ucnt, gridDim.x, &s_last)) return;
+    mask_union(selw, d_ff, (int)gridDim.x, uni, nuni, umask, wsum);
   }
 }
-
-// ---------------------------------------------------------------------------
-// Union of the per-token masks (batch path): U ascending, plus for each entry
-// the bit set of tokens whose mask holds it.  One 1024-thread work-group;
-// thread w owns mask word w (channels 32 w .. 32 w + 31, d_ff <= 32768), reads
-// that word of every token, and writes its union entries at its exclusive
-// prefix of the word popcounts.
-// ---------------------------------------------------------------------------
-template <int NB>
-__global__ __launch_bounds__(1024) void union_kernel(const unsigned *selw, int d_ff, int *uni,
-                                                     int *nuni, uint8_t *umask) {
-  __shared__ unsigned wsum[16];
-  const int w = threadIdx.x;
-  const int words = (d_ff + 31) >> 5;
-  unsigned tw[NB], u = 0u;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    tw[b] = w < words ? selw[(size_t)b * words + w] : 0u;
-    u |= tw[b];
-  }
-  unsigned total;
-  unsigned pos = block_excl_scan<16>((unsigned)__popc(u), wsum, total);
-  while (u) {
-    const int bit = __builtin_ctz(u);
-    u &= u - 1u;
-    unsigned m = 0u;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) m |= ((tw[b] >> bit) & 1u) << b;
-    uni[pos] = w * 32 + bit;
-    umask[pos] = (uint8_t)m;
-    ++pos;
-  }
-  if (w == 0) *nuni = (int)total;
-}
-
 // ---------------------------------------------------------------------------
 // K-e  Stage 2a: exact gathered up/gate GEMV fused with SiLU and the product
 //      (Sec. 4.1, Stage 2 equations: u_sp, h_sp, s_sp over the full x)
@@ -954,7 +958,8 @@ hipError_t launch_prepare(const Plan &p, const Bufs &b, const void *w_up,
   if (e != hipSuccess) return e;
   e = hipMemsetAsync(b.tile_cnt, 0, sizeof(unsigned) * p.ntile, s);
   if (e != hipSuccess) return e;
-  return hipMemsetAsync(b.col_cnt, 0, sizeof(unsigned) * p.ncol, s);
+  if ((e = hipMemsetAsync(b.col_cnt, 0, sizeof(unsigned) * p.ncol, s)) != hipSuccess) return e;
+  return hipMemsetAsync(b.ucnt, 0, sizeof(unsigned), s);
 }
 
 hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
@@ -981,10 +986,12 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
 template <int PER>
 static void topk_launch(const Plan &p, const Bufs &b, int batch, int k, bool lists,
                         hipStream_t s) {
-  // one token: the list only (it drives Stage 2); several: the mask words
-  // drive the union, the lists only when asked for
+  // one token: the list only (it drives Stage 2); several: the mask words and
+  // their union (built by the last work-group), the lists only when asked for
+  const bool several = batch > 1;
   topk_kernel<PER><<<batch, 1024, 0, s>>>(b.sabs, p.d_ff, k, lists ? b.sel : nullptr,
-                                          batch > 1 ? b.selw : nullptr);
+                                          several ? b.selw : nullptr, several ? b.ucnt : nullptr,
+                                          b.uni, b.nuni, b.umask);
 }
 
 hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
@@ -999,12 +1006,6 @@ hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool list
   return hipGetLastError();
 }
 
-hipError_t launch_union(const Plan &p, const Bufs &b, int batch, int k, hipStream_t s) {
-  (void)k;
-  if (p.d_ff > 32 * 1024) return hipErrorInvalidValue;
-  PROX_DISPATCH_NB(batch, (union_kernel<NB><<<1, 1024, 0, s>>>(b.selw, p.d_ff, b.uni, b.nuni, b.umask)));
-  return hipGetLastError();
-}
 
 // MFMA form of the batched up/gate step (bf16, 2 <= NB <= 8 tokens): one
 // wave per tile of 16 list positions.  v_mfma_f32_16x16x32_bf16 computes

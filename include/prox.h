@@ -213,8 +213,9 @@ prox_status prox_rmsnorm(const prox_layer *layer, const float *resid, int batch,
  * for measurement.  `events` holds n_events caller-created hipEvent_t; one is
  * recorded on `stream` before the first kernel and one after each kernel, so
  * consecutive pairs bracket the kernels in launch order:
- *   sparse: Stage 1 proxy, top-k, [mask union if batch > 1], Stage 2 up/gate,
- *           Stage 2 down                        (at least 6 events needed)
+ *   sparse: Stage 1 proxy, top-k (which also forms the union of the masks
+ *           when batch > 1), Stage 2 up/gate, Stage 2 down
+ *                                               (at least 5 events needed)
  *   dense:  up/gate, down                        (at least 3 events needed)
  * *n_recorded receives the number of events recorded.  Same results as the
  * plain calls; no host synchronization.                                      */
