@@ -62,7 +62,8 @@ static_assert(kSyncErr == kFusedErrWord, "error word index");
 
 constexpr int kFW = 8;             // waves per work-group
 constexpr int kFT = kFW * 64;      // threads per work-group
-constexpr int kWaveCand = 256;     // top-k candidates per wave held in LDS (fast path)
+constexpr int kWaveCand = 192;     // top-k candidates per wave held in LDS (fast path)
+constexpr int kPreSlots = 28;      // key slots the select can hold in LDS: d_ff <= 28 * 512
 constexpr int kMaxPer = 64;        // key slots per thread: d_ff <= 64 * 512
 constexpr int kGroups = kMaxPer * kFW;  // groups of 64 channels: d_ff <= 512 * 64
 constexpr int kKC = 32;            // key slots loaded per round of a select pass
@@ -126,17 +127,6 @@ __device__ __forceinline__ void wait_tj(const unsigned *w, unsigned *err, unsign
   *J = (unsigned)(v >> 32) - 1u;
 }
 
-// Wave partial sums of the RMSNorm reduction (block_inv_rms); a work-group of
-// kRmsThreads, like the standalone RMSNorm kernel, gives the same bits.
-static_assert(kFT == kRmsThreads, "RMSNorm reduction order");
-__shared__ float g_rms_part[kFW];
-
-// Timeline stamp of the current item: when its wait for earlier items ended
-// (thread 0 only; 100 MHz s_memrealtime clock).
-__shared__ unsigned long long g_twait;
-__device__ __forceinline__ void stamp_wait(const FusedArgs &a) {
-  if (a.trace) g_twait = __builtin_amdgcn_s_memrealtime();
-}
 
 // Bounded wait of a whole wave until every lane's flag is >= 1 (lanes with
 // nothing to wait for pass their own satisfied flag).
@@ -159,14 +149,17 @@ struct P1Smem {
   __attribute__((aligned(16))) int rl[kFW][64 + 48];
   __attribute__((aligned(16))) float xc[kFW][64 + 48];
 };
+template <bool SEL>
 struct P2Smem {
+  // the small arrays first (LDS offsets below 64 KiB fit the instructions)
+  unsigned ccnt[kFW];
+  unsigned wt[16];
+  unsigned misc[8];
   unsigned h[2048];
   unsigned ck[kFW * kWaveCand];  // candidate keys (per-wave lists)
   int ci[kFW * kWaveCand];       // candidate channels
   unsigned ceq[kGroups];         // per group of 64 channels: keys equal to T
-  unsigned ccnt[kFW];
-  unsigned wt[16];
-  unsigned misc[8];
+  unsigned keys[SEL ? kPreSlots * kFT : 1];  // |s~| bits of channel j at j (top-k instances)
 };
 struct P3Smem {
   u4 x[2048];  // x when d_model * element size <= 32 KB
@@ -183,13 +176,43 @@ struct P4Smem {
   unsigned tj[2];      // T and J of the select
 };
 
+// All of the kernel's LDS as one object, the small words first: LDS
+// instructions encode offsets below 64 KiB, and a word placed past the
+// 80 KB union would need an address register wherever it is used.
+template <bool SEL>
+struct FusedShared {
+  // wave partial sums of the RMSNorm reduction (block_inv_rms); a work-group
+  // of kRmsThreads, like the standalone RMSNorm kernel, gives the same bits
+  float rms_part[kFW];
+  // timeline stamp of the current item: when its wait for earlier items
+  // ended (thread 0 only; 100 MHz s_memrealtime clock)
+  unsigned long long twait;
+  int ticket, flag;
+  union {
+    P1Smem p1;
+    P2Smem<SEL> p2;
+    P3Smem p3;
+    P4Smem p4;
+  } u;
+};
+static_assert(kFT == kRmsThreads, "RMSNorm reduction order");
+// SEL: the instance runs the top-k select (the threshold-mask instances
+// leave it out and keep the key array out of LDS).
+template <bool SEL>
+__shared__ FusedShared<SEL> g_fs;
+
+template <bool SEL>
+__device__ __forceinline__ void stamp_wait(const FusedArgs &a) {
+  if (a.trace) g_fs<SEL>.twait = __builtin_amdgcn_s_memrealtime();
+}
+
 // ---------------------------------------------------------------------------
 // P1: Stage 1 for one (tile, chunk) item.  Same arithmetic as proxy_kernel
 // (see there): one wave per 64-row slice, survivors by ballot, nibble pairs
 // decoded under the bf16 exponent byte for bf16 layers.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool NORM>
-__device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
+template <bool BF16, bool NORM, bool SEL>
+__device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
   constexpr int U = 16;
   const int chunk = item % a.nchunk, t = item / a.nchunk;
   const int lane = threadIdx.x & 63;
@@ -200,7 +223,7 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
   float inv = 1.0f;
-  if constexpr (NORM) inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_rms_part);
+  if constexpr (NORM) inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
 
   if (sl < nsl) {
     // the slice's scales first, so that their latency hides behind the rest
@@ -362,10 +385,13 @@ __device__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
 // digit 2 = bits 19..9, digit 3 = bits 8..0.  Channel j is read by thread
 // j % 512 in slot j / 512 and belongs to group j / 64 (one wave, one slot).
 // Fast path:
+//   0. while Stage 1 runs, the keys of every finished tile are copied
+//      straight into LDS (d_ff <= kPreSlots * 512; larger layers copy them
+//      after the histogram, kPreSlots slots at a time);
 //   1. the global digit-1 histogram (built by the P1 tile epilogues) gives
 //      the bin b* of the k-th largest key; b* is published for P3;
-//   2. one pass over the keys gathers those with digit 1 = b* (typically a
-//      few hundred) in per-wave LDS lists;
+//   2. one pass over the keys in LDS gathers those with digit 1 = b*
+//      (typically a few hundred) in per-wave LDS lists;
 //   3. two radix steps over the gathered keys give the k-th key T and the
 //      number kk of keys equal to T that are kept;
 //   4. the tie cutoff J: the channel of the kk-th key equal to T in index
@@ -404,19 +430,74 @@ __device__ __forceinline__ void pick_bin_all(H hist, unsigned kk, unsigned *wt, 
   __syncthreads();
 }
 
-__device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
+template <bool SEL>
+__device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
   // The select is on the critical path and shares its CU with P3 waves that
   // mostly wait on memory: its waves issue first.
   __builtin_amdgcn_s_setprio(3);
-  if (threadIdx.x == 0) {
-    wait_geq(&a.sync[kSyncTiles], (unsigned)a.ntile, &a.sync[kSyncErr]);
-    stamp_wait(a);
-  }
-  __syncthreads();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = a.d_ff;
   const int per = (n + kFT - 1) / kFT;
   const unsigned k = (unsigned)a.k;
+  // Keys in flight before the last tile is done: when every key fits the
+  // LDS array (per <= kPreSlots) and every tile flag one lane (ntile <= 64),
+  // each wave polls all tile flags at once and, slot by slot, copies the keys
+  // of its slots whose tiles are done straight into LDS.  The keys of the
+  // last tile then travel with the histogram instead of after b*.  Slot m of
+  // wave w holds channels m * 512 + 64 w + lane, all in tile 2 m + w / 4
+  // (the slots past d_ff read 0).
+  const bool pre = per <= kPreSlots && a.ntile <= 64;
+  if (pre) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.sabs, (uint32_t)n * 4u);
+    const uint32_t koff = (uint32_t)tid * 4u;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const unsigned *fl = &a.tflag[min(lane, a.ntile - 1) * kSyncStride];
+    uint64_t done = 0ull;  // tiles seen done (bit t), wave-uniform
+    unsigned spins = 0;
+#pragma unroll 1
+    for (int m = 0; m < per; ++m) {
+      const int tm = min(2 * m + (wu >> 2), a.ntile - 1);
+      // Poll only while this slot's tile is not known to be done (a poll
+      // waits for this wave's earlier copies too).
+      while (!((done >> tm) & 1ull) && spins <= (1u << 22)) {
+        const uint64_t b = __ballot(xload_u(fl) >= 1u);
+        // scalar (no VGPR to wait on); readfirstlane returns int: widen unsigned
+        done = ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+               (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+        if (!((done >> tm) & 1ull)) {
+          __builtin_amdgcn_s_sleep(1);
+          spins = __builtin_amdgcn_readfirstlane(spins + 1u);
+        }
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void *)&sm.keys[m * kFT + wu * 64], 4, koff,
+          (uint32_t)(m * kFT) * 4u, 0, kSelBits);
+    }
+    // Then the digit-1 histogram, complete once every tile is done: each
+    // wave polls on until it has seen all of them and copies its share of
+    // the bins (four blocks of 64) into LDS, without waiting for the others.
+    const uint64_t all = a.ntile == 64 ? ~0ull : (1ull << a.ntile) - 1ull;
+    while ((done & all) != all && spins <= (1u << 22)) {
+      const uint64_t b = __ballot(xload_u(fl) >= 1u);
+      done = ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+             (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+      if ((done & all) != all) {
+        __builtin_amdgcn_s_sleep(1);
+        spins = __builtin_amdgcn_readfirstlane(spins + 1u);
+      }
+    }
+    if (spins > (1u << 22) && lane == 0) atomicOr(&a.sync[kSyncErr], 1u);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.ghist, 2048u * 4u);
+#pragma unroll
+    for (int q = 0; q < 2048 / kFT; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rh, (__attribute__((address_space(3))) void *)&sm.h[q * kFT + wu * 64], 4, koff,
+          (uint32_t)(q * kFT) * 4u, 0, kSelBits);
+  } else if (threadIdx.x == 0) {
+    wait_geq(&a.sync[kSyncTiles], (unsigned)a.ntile, &a.sync[kSyncErr]);
+  }
+  if (threadIdx.x == 0) stamp_wait<SEL>(a);
+  __syncthreads();
   // Keys of slots [e0, e0 + kKC): unconditional loads (indices clamped into
   // range) so that they all stay in flight; callers mask j >= n themselves.
   auto load_keys = [&](int e0, unsigned (&kc)[kKC]) {
@@ -426,8 +507,10 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
       kc[m] = __float_as_uint(xload(&a.sabs[j]));
     }
   };
-  for (int i = tid; i < 2048; i += kFT) sm.h[i] = xload_u(&a.ghist[i]);
+  if (!pre)
+    for (int i = tid; i < 2048; i += kFT) sm.h[i] = xload_u(&a.ghist[i]);
   for (int i = tid; i < kGroups; i += kFT) sm.ceq[i] = 0u;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // what went straight into LDS, too
   __syncthreads();
 
   // 1. the digit-1 bin of the k-th key, published at once.
@@ -440,26 +523,46 @@ __device__ void p2_select(const FusedArgs &a, P2Smem &sm) {
   }
   unsigned T;
 
-  // 2. candidates at b*.
+  // 2. candidates at b*, from the keys in LDS (kPreSlots slots per round;
+  // one round, already copied, on the early path).
   unsigned cbase = 0u;
-  for (int e0 = 0; e0 < per; e0 += kKC) {
-    unsigned kc[kKC];
-    load_keys(e0, kc);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  for (int e0 = 0; e0 < per; e0 += kPreSlots) {
+    if (!pre) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.sabs, (uint32_t)n * 4u);
+#pragma unroll 1
+      for (int m = 0; m < min(kPreSlots, per - e0); ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void *)&sm.keys[m * kFT + wu * 64], 4,
+            (uint32_t)tid * 4u, (uint32_t)((e0 + m) * kFT) * 4u, 0, kSelBits);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    // Each thread marks its candidate slots in a bit mask (all LDS reads in
+    // flight at once, no branches); one wave scan places them.
+    static_assert(kPreSlots <= 32, "one mask bit per slot");
+    unsigned msk = 0u;
 #pragma unroll
-    for (int m = 0; m < kKC; ++m) {
-      const int e = e0 + m;
-      if (e < per) {
-        const int j = e * kFT + tid;
-        const bool c = j < n && (kc[m] >> 20) == bstar;
-        const uint64_t mc = __ballot(c);
-        const unsigned pos = cbase + __builtin_amdgcn_mbcnt_hi(
-                                         (unsigned)(mc >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mc, 0u));
-        if (c && pos < (unsigned)kWaveCand) {
-          sm.ck[w * kWaveCand + pos] = kc[m];
-          sm.ci[w * kWaveCand + pos] = j;
-        }
-        cbase += (unsigned)__popcll(mc);
+    for (int m0 = 0; m0 < kPreSlots; m0 += kPreSlots / 2) {
+      unsigned kv[kPreSlots / 2];
+#pragma unroll
+      for (int m = 0; m < kPreSlots / 2; ++m) kv[m] = sm.keys[(m0 + m) * kFT + tid];
+#pragma unroll
+      for (int m = 0; m < kPreSlots / 2; ++m)
+        msk |= (unsigned)((e0 + m0 + m < per) & ((e0 + m0 + m) * kFT + tid < n) &
+                          ((kv[m] >> 20) == bstar)) << (m0 + m);
+    }
+    const unsigned cnt = (unsigned)__popc(msk);
+    const unsigned incl = wave_incl_scan_dpp(cnt);
+    unsigned pos = cbase + incl - cnt;
+    cbase += (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+    while (msk) {
+      const int m = __builtin_ctz(msk);
+      msk &= msk - 1u;
+      if (pos < (unsigned)kWaveCand) {
+        sm.ck[w * kWaveCand + pos] = sm.keys[m * kFT + tid];
+        sm.ci[w * kWaveCand + pos] = (e0 + m) * kFT + tid;
       }
+      ++pos;
     }
   }
   if (lane == 0) sm.ccnt[w] = cbase;
@@ -652,8 +755,8 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int i, int lane) {
   return (int)__builtin_ctzll(hit);
 }
 
-template <bool BF16, bool NORM>
-__device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
+template <bool BF16, bool NORM, bool SEL>
+__device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const int c0 = item * kP3Ch;
   // What to compute first.  Threshold: |s~| >= tau_s, once the item's Stage 1
   // tile is done.  Top-k: every channel whose digit 1 is at least the b* of
@@ -674,7 +777,7 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
       lo = xload_u(&a.sync[kSyncBin]) - 1u;
     }
     sm.lo = lo;
-    stamp_wait(a);
+    stamp_wait<SEL>(a);
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -690,7 +793,7 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   if (rowb <= sizeof(sm.x)) {
     if constexpr (NORM) {
       // x = RMSNorm(r) in the layer dtype, 16 bytes per step
-      const float inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_rms_part);
+      const float inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
       constexpr int EPS16 = BF16 ? 8 : 4;
       for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) {
         const float *r = a.rnorm + (size_t)i * EPS16;
@@ -772,8 +875,8 @@ __device__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
 // may be kept (digit 1 >= b*) start loading before the range's P3 items and
 // the select are done; a bin-b* channel below the cut gets s = 0.
 // ---------------------------------------------------------------------------
-template <bool BF16>
-__device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
+template <bool BF16, bool SEL>
+__device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
   // rows per wave per batch: 10 rows x 512 B; 20 measured 0.5 us slower at 8B
   // (more bytes in flight behind which the dependent round trips queue)
   constexpr int U = BF16 ? 10 : 8;
@@ -845,7 +948,7 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
   if (tid < 64) {
     const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
     wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride], &a.sync[kSyncErr]);
-    if (lane == 0) stamp_wait(a);
+    if (lane == 0) stamp_wait<SEL>(a);
   }
   __syncthreads();
   // 3. s of each listed channel (final once the range's P3 items are done,
@@ -943,17 +1046,14 @@ __device__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
 // The persistent kernel.
 // ---------------------------------------------------------------------------
 // NORM: x = RMSNorm(a.rnorm) is formed inside (a separate instance, so the
-// plain forward keeps its register budget).
-template <bool BF16, bool NORM>
+// plain forward keeps its register budget).  SEL: top-k (with the select
+// item) rather than the threshold mask.
+template <bool BF16, bool NORM, bool SEL>
 __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) void ffn_fused_kernel(
     FusedArgs a) {
-  __shared__ union {
-    P1Smem p1;
-    P2Smem p2;
-    P3Smem p3;
-    P4Smem p4;
-  } sm;
-  __shared__ int s_ticket, s_flag;
+  auto &sm = g_fs<SEL>.u;
+  int &s_ticket = g_fs<SEL>.ticket;
+  int &s_flag = g_fs<SEL>.flag;
   const int total = a.n_p1 + a.n_p2 + a.n_p3 + a.n_p4;
   // The first min(grid, n_p1) tickets are the work-groups' own indices (all
   // work-groups of the grid are resident at once, see the launcher), which
@@ -974,27 +1074,27 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     unsigned long long t0 = 0;
     if (a.trace && threadIdx.x == 0) {
       t0 = __builtin_amdgcn_s_memrealtime();
-      g_twait = t0;
+      g_fs<SEL>.twait = t0;
     }
     int phase;
     int r = t;
     if (r < a.n_p1) {
       phase = 1;
-      p1_item<BF16, NORM>(a, r, sm.p1, &s_flag);
+      p1_item<BF16, NORM, SEL>(a, r, sm.p1, &s_flag);
     } else if ((r -= a.n_p1) < a.n_p2) {
       phase = 2;
-      p2_select(a, sm.p2);
+      if constexpr (SEL) p2_select<SEL>(a, sm.p2);
     } else if ((r -= a.n_p2) < a.n_p3) {
       phase = 3;
-      p3_item<BF16, NORM>(a, r, sm.p3);
+      p3_item<BF16, NORM, SEL>(a, r, sm.p3);
     } else {
       phase = 4;
-      p4_item<BF16>(a, r - a.n_p3, sm.p4, &s_flag);
+      p4_item<BF16, SEL>(a, r - a.n_p3, sm.p4, &s_flag);
     }
     if (a.trace && threadIdx.x == 0) {
       unsigned long long *e = a.trace + 4 * (size_t)t;
       e[0] = t0;
-      e[1] = g_twait;
+      e[1] = g_fs<SEL>.twait;
       e[2] = __builtin_amdgcn_s_memrealtime();
       e[3] = (unsigned long long)blockIdx.x | ((unsigned long long)phase << 32);
     }
@@ -1062,9 +1162,9 @@ __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, 
 // ---------------------------------------------------------------------------
 // Launcher
 // ---------------------------------------------------------------------------
-template <bool BF16, bool NORM>
+template <bool BF16, bool NORM, bool SEL>
 static hipError_t fused_go(FusedArgs &a, hipStream_t s) {
-  auto fn = ffn_fused_kernel<BF16, NORM>;
+  auto fn = ffn_fused_kernel<BF16, NORM, SEL>;
   static int cap = 0;
   if (!cap) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -1157,8 +1257,12 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.n_p2 = ts_mode ? 0 : 1;
   a.n_p3 = fused_n_p3(p);
   a.n_p4 = p.ncol * a.nrange;
-  if (norm.r) return p.bf16 ? fused_go<true, true>(a, s) : fused_go<false, true>(a, s);
-  return p.bf16 ? fused_go<true, false>(a, s) : fused_go<false, false>(a, s);
+  if (!ts_mode) {
+    if (norm.r) return p.bf16 ? fused_go<true, true, true>(a, s) : fused_go<false, true, true>(a, s);
+    return p.bf16 ? fused_go<true, false, true>(a, s) : fused_go<false, false, true>(a, s);
+  }
+  if (norm.r) return p.bf16 ? fused_go<true, true, false>(a, s) : fused_go<false, true, false>(a, s);
+  return p.bf16 ? fused_go<true, false, false>(a, s) : fused_go<false, false, false>(a, s);
 }
 
 hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,
