@@ -166,14 +166,22 @@ struct P3Smem {
   float ured[2 * kP3Ch];  // dot product of each unit (row) of the item
   unsigned lo, bstar;
 };
+// P4 rows (bf16, 512 bytes each) taken straight into LDS ahead of the wait,
+// beyond the first batch held in registers: in the top-k instances as many
+// as their LDS (sized by the select's keys) holds anyway; the threshold-mask
+// instances grow theirs for 80 (measured: worth the larger LDS).
+template <bool SEL>
+constexpr int kP4LdsRows = SEL ? 128 : 80;
+template <bool SEL>
 struct P4Smem {
+  unsigned wcnt[kFW];
+  unsigned bstar;
+  unsigned tj[2];      // T and J of the select
   float red[kFW][kDownCols];
   int rs[kP4Ch];       // listed channels
   unsigned rk[kP4Ch];  // their keys
   float sv[kP4Ch];     // their s (0 when below the cut)
-  unsigned wcnt[kFW];
-  unsigned bstar;
-  unsigned tj[2];      // T and J of the select
+  u2 rows[kP4LdsRows<SEL>][64];
 };
 
 // All of the kernel's LDS as one object, the small words first: LDS
@@ -192,7 +200,7 @@ struct FusedShared {
     P1Smem p1;
     P2Smem<SEL> p2;
     P3Smem p3;
-    P4Smem p4;
+    P4Smem<SEL> p4;
   } u;
 };
 static_assert(kFT == kRmsThreads, "RMSNorm reduction order");
@@ -876,7 +884,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
 // the select are done; a bin-b* channel below the cut gets s = 0.
 // ---------------------------------------------------------------------------
 template <bool BF16, bool SEL>
-__device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem &sm, int *s_flag) {
+__device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL> &sm, int *s_flag) {
   // rows per wave per batch: 10 rows x 512 B; 20 measured 0.5 us slower at 8B
   // (more bytes in flight behind which the dependent round trips queue)
   constexpr int U = BF16 ? 10 : 8;
@@ -943,8 +951,23 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem &sm
     }
   };
   // 2. the first rows stream in while the range's P3 items and the select
-  // finish.
+  // finish: one batch into registers, the next ND rows straight into LDS.
+  constexpr int ND = BF16 ? kP4LdsRows<SEL> : 0;  // multiple of kFW (or 0)
+  constexpr int NB0 = kFW * U;  // rows of a register batch
+  static_assert(ND % kFW == 0, "LDS rows per wave");
   if (nr > 0) load_batch(0);
+  if constexpr (ND > 0) {
+    const int dend = min(nr, NB0 + ND);
+    for (int rr = NB0 + wv; rr < dend; rr += kFW) {
+      const uint32_t rowoff =
+          (uint32_t)__builtin_amdgcn_readfirstlane(sm.rs[rr]) * (uint32_t)(kDownCols * ESZ);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)&sm.rows[rr - NB0][h * 32], 4,
+            (uint32_t)lane * 4u, rowoff + (uint32_t)h * 256u, 0, kNT);
+    }
+  }
   if (tid < 64) {
     const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
     wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride], &a.sync[kSyncErr]);
@@ -970,7 +993,9 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem &sm
   }
   __syncthreads();
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int b0 = 0; b0 < nr; b0 += kFW * U) {
+  // each wave adds its rows (wv, wv + 8, ...) in ascending order: the first
+  // register batch, the LDS rows, then further register batches
+  for (int b0 = 0; b0 < nr; b0 += (b0 == 0 ? NB0 + ND : NB0)) {
     if (b0 > 0) load_batch(b0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -990,6 +1015,20 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem &sm
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[c] = fmaf(sv, wf[c], acc[c]);
+    }
+    if constexpr (ND > 0) {
+      if (b0 == 0 && nr > NB0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the LDS rows have landed
+#pragma unroll 4
+        for (int rr = NB0 + wv; rr < min(nr, NB0 + ND); rr += kFW) {
+          const u2 w = sm.rows[rr - NB0][lane];
+          const float sv = sm.sv[rr];
+          acc[0] = fmaf(sv, bf16_to_f32(w.x & 0xffffu), acc[0]);
+          acc[1] = fmaf(sv, bf16_to_f32(w.x >> 16), acc[1]);
+          acc[2] = fmaf(sv, bf16_to_f32(w.y & 0xffffu), acc[2]);
+          acc[3] = fmaf(sv, bf16_to_f32(w.y >> 16), acc[3]);
+        }
+      }
     }
   }
   *(float4 *)&sm.red[wv][lane * 4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
