@@ -38,7 +38,8 @@
 // for nothing, so the schedule cannot deadlock.  Every wait is bounded.  Data
 // passed between work-groups goes through agent-coherent accesses
 // (xstore/xload, sc1 buffer loads); the last work-group to leave resets the
-// ticket, the flags and the histogram for the next launch.
+// ticket and the flags for the next launch (the select clears the
+// histogram as soon as it has read it).
 #include <type_traits>
 
 #include "prox_device.h"
@@ -519,6 +520,9 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
     for (int i = tid; i < 2048; i += kFT) sm.h[i] = xload_u(&a.ghist[i]);
   for (int i = tid; i < kGroups; i += kFT) sm.ceq[i] = 0u;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // what went straight into LDS, too
+  // The histogram is in LDS and nothing else reads it: clear it for the next
+  // launch here rather than at the exit.
+  for (int i = tid; i < 2048; i += kFT) xstore_u(&a.ghist[i], 0u);
   __syncthreads();
 
   // 1. the digit-1 bin of the k-th key, published at once.
@@ -1138,8 +1142,8 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       e[3] = (unsigned long long)blockIdx.x | ((unsigned long long)phase << 32);
     }
   }
-  // The last work-group out clears the ticket, flags and histogram for the
-  // next launch.  Every work-group leaves on exactly one ticket >= total from
+  // The last work-group out clears the ticket and the flags for the next
+  // launch (the select clears the histogram once it has read it).  Every work-group leaves on exactly one ticket >= total from
   // the counter, so the counter itself says who is last: the one that drew
   // ticket total + grid - 1 (no second atomic on the way out).
   if ((unsigned)s_ticket == (unsigned)total + gridDim.x - 1u) {
@@ -1148,7 +1152,6 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     for (int i = threadIdx.x; i < kCtl + a.n_p3 + a.ntile; i += kFT)
       if (i * kSyncStride != kSyncErr) xstore_u(&a.sync[i * kSyncStride], 0u);
     if (threadIdx.x == 0) xstore_u(&a.sync[kSyncSelect + 1], 0u);
-    for (int i = threadIdx.x; i < 2048; i += kFT) xstore_u(&a.ghist[i], 0u);
   }
 }
 
