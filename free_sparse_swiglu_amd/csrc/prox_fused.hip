@@ -232,8 +232,12 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
   float inv = 1.0f;
-  if constexpr (NORM) inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
-
+  float rv = 0.0f;  // NORM: r of this thread's row of the chunk, chunk * 512 + tid
+  if constexpr (NORM) {
+    // loaded with the RMS pass's loads, not after it
+    rv = a.rnorm[min(chunk * kFT + (int)threadIdx.x, a.d_model - 1)];
+    inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
+  }
   if (sl < nsl) {
     // the slice's scales first, so that their latency hides behind the rest
     const int g = (sl * 64) / a.G;
@@ -244,8 +248,8 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
     uint64_t un;
     if constexpr (NORM) {
       // x_i = RMSNorm(r)_i in the layer dtype, as launch_rmsnorm stores it
-      const int row = sl * 64 + lane;
-      xl = round_elem<BF16>(a.rnorm[row] * inv);
+      const int row = sl * 64 + lane;  // = chunk * 512 + tid
+      xl = round_elem<BF16>(rv * inv);
       un = __ballot(fabsf(xl) >= a.tau);
       if (t == 0 && a.xout) st_elem<BF16>(a.xout, row, xl);
     } else {
@@ -770,6 +774,33 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int i, int lane) {
 template <bool BF16, bool NORM, bool SEL>
 __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
   const int c0 = item * kP3Ch;
+  // x to LDS when it fits (every item reads it, so it is L2-resident), before
+  // the wait: it does not depend on Stage 1.
+  const uint32_t rowb = (uint32_t)a.d_model * (BF16 ? 2u : 4u);
+  const u4 *xs = nullptr;
+  if (rowb <= sizeof(sm.x)) {
+    if constexpr (NORM) {
+      // x = RMSNorm(r) in the layer dtype, 16 bytes per step
+      const float inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
+      constexpr int EPS16 = BF16 ? 8 : 4;
+      for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) {
+        const float *r = a.rnorm + (size_t)i * EPS16;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (BF16)
+            w[q] = (uint32_t)f32_to_bf16(r[2 * q] * inv) |
+                   ((uint32_t)f32_to_bf16(r[2 * q + 1] * inv) << 16);
+          else
+            w[q] = __float_as_uint(r[q] * inv);
+        }
+        sm.x[i] = u4{w[0], w[1], w[2], w[3]};
+      }
+    } else {
+      for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) sm.x[i] = ((const u4 *)a.x)[i];
+    }
+    xs = sm.x;
+  }
   // What to compute first.  Threshold: |s~| >= tau_s, once the item's Stage 1
   // tile is done.  Top-k: every channel whose digit 1 is at least the b* of
   // the layer's previous call (a guess of the cut, which moves little from
@@ -799,32 +830,6 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
   const bool valid = lane < kP3Ch && j < n;
   const unsigned key = __float_as_uint(xload(&a.sabs[min(j, n - 1)]));
   const unsigned d1 = key >> 20;
-  // x to LDS when it fits (every item reads it, so it is L2-resident)
-  const uint32_t rowb = (uint32_t)a.d_model * (BF16 ? 2u : 4u);
-  const u4 *xs = nullptr;
-  if (rowb <= sizeof(sm.x)) {
-    if constexpr (NORM) {
-      // x = RMSNorm(r) in the layer dtype, 16 bytes per step
-      const float inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
-      constexpr int EPS16 = BF16 ? 8 : 4;
-      for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) {
-        const float *r = a.rnorm + (size_t)i * EPS16;
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (BF16)
-            w[q] = (uint32_t)f32_to_bf16(r[2 * q] * inv) |
-                   ((uint32_t)f32_to_bf16(r[2 * q + 1] * inv) << 16);
-          else
-            w[q] = __float_as_uint(r[q] * inv);
-        }
-        sm.x[i] = u4{w[0], w[1], w[2], w[3]};
-      }
-    } else {
-      for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) sm.x[i] = ((const u4 *)a.x)[i];
-    }
-    xs = sm.x;
-  }
   // Two passes: the first set, then (top-k) what b* adds to it.  Each
   // computes s of the channels of the wave-uniform mask cm, stored by
   // channel.  Work units are rows: unit 2m is the up row, unit 2m + 1 the gate
