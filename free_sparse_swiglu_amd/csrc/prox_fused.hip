@@ -54,7 +54,7 @@ enum : int {
   kSyncTiles = 1 * kSyncStride,   // P1 tiles finished
   kSyncSelect = 2 * kSyncStride,  // one 64-bit word: T (low), J + 1 (high; 0 until published);
                                   // T, J again at +2, +3 (kept after the launch)
-  kSyncExit = 3 * kSyncStride,    // (unused)
+  kSyncInv = 3 * kSyncStride,     // in-kernel RMSNorm: bits of 1/rms(r) once known (0 before)
   kSyncErr = 4 * kSyncStride,     // sticky error bits (1: a wait timed out, 2: select fallback used)
   kSyncBin = 5 * kSyncStride,     // b* + 1 once published (0 before)
   kSyncP3 = 6 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
@@ -237,6 +237,8 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
     // loaded with the RMS pass's loads, not after it
     rv = a.rnorm[min(chunk * kFT + (int)threadIdx.x, a.d_model - 1)];
     inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
+    // for the Stage 2 items, which scale r by it without reducing again
+    if (item == 0 && threadIdx.x == 0) xstore_u(&a.sync[kSyncInv], __float_as_uint(inv));
   }
   if (sl < nsl) {
     // the slice's scales first, so that their latency hides behind the rest
@@ -780,11 +782,27 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
   const u4 *xs = nullptr;
   if (rowb <= sizeof(sm.x)) {
     if constexpr (NORM) {
-      // x = RMSNorm(r) in the layer dtype, 16 bytes per step
-      const float inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
+      // x = RMSNorm(r) in the layer dtype, 16 bytes per step, with the
+      // 1/rms(r) that the first Stage 1 item published (the same bits as a
+      // reduction here; 1/rms > 0, so 0 means not yet).  The threshold-mask
+      // instances load the residual of each thread's first step together
+      // with that word (in the top-k instances those registers spill).
       constexpr int EPS16 = BF16 ? 8 : 4;
-      for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) {
-        const float *r = a.rnorm + (size_t)i * EPS16;
+      const int nst = (int)(rowb >> 4);
+      float r0[EPS16];
+      if constexpr (!SEL) {
+        const int i0 = min((int)threadIdx.x, nst - 1);
+#pragma unroll
+        for (int q = 0; q < EPS16; ++q) r0[q] = a.rnorm[(size_t)i0 * EPS16 + q];
+      }
+      unsigned ib = xload_u(&a.sync[kSyncInv]);
+      if (__syncthreads_or(ib == 0u)) {
+        if (threadIdx.x == 0) wait_geq(&a.sync[kSyncInv], 1u, &a.sync[kSyncErr]);
+        __syncthreads();
+        ib = xload_u(&a.sync[kSyncInv]);
+      }
+      const float inv = __uint_as_float(ib);
+      auto put = [&](int i, const float *r) {
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -795,7 +813,13 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
             w[q] = __float_as_uint(r[q] * inv);
         }
         sm.x[i] = u4{w[0], w[1], w[2], w[3]};
+      };
+      int i1 = threadIdx.x;
+      if constexpr (!SEL) {
+        if (i1 < nst) put(i1, r0);
+        i1 += kFT;
       }
+      for (int i = i1; i < nst; i += kFT) put(i, a.rnorm + (size_t)i * EPS16);
     } else {
       for (int i = threadIdx.x; i < (int)(rowb >> 4); i += kFT) sm.x[i] = ((const u4 *)a.x)[i];
     }
