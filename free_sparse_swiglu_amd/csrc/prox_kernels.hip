@@ -350,30 +350,34 @@ __global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a)
 // output position of a kept channel is (kept in earlier slots) + (kept in
 // earlier waves of its slot) + (kept in lower lanes), from ballots and one
 // scan of the per-(slot, wave) counts, so the list comes out ascending.
-// Each digit's bin is picked by wave 0 alone (one barrier per digit).
+// Each digit's bin is picked by the whole work-group (pick_bin).
 
-// Wave 0 scans hist[0, NBINS) from the top and finds the bin holding the
-// kk-th largest key; writes it and the remaining rank to *s_bin / *s_kk.
-template <int NBINS>
-__device__ __forceinline__ void pick_bin(const unsigned *hist, unsigned kk,
-                                         unsigned *s_bin, unsigned *s_kk) {
-  constexpr int BPL = NBINS / 64;  // bins per lane, lane l owns the l-th block from the top
-  const int lane = threadIdx.x & 63;
-  const int hi = NBINS - 1 - lane * BPL;  // lane's highest bin
-  unsigned c[BPL];
+// All 1024 threads find the bin holding the kk-th largest key: thread t
+// owns bins [NBINS - (t + 1) * BPT, NBINS - t * BPT) (from the top; threads
+// past the bins own none), reads them from consecutive LDS words and a block
+// scan gives the keys above its bins.  hist(b) returns the count of bin b.
+// Writes the bin and the remaining rank to *s_bin / *s_kk (2 barriers
+// inside; the caller's barrier publishes them).
+template <int NBINS, typename H>
+__device__ __forceinline__ void pick_bin(H hist, unsigned kk, unsigned *wsum, unsigned *s_bin,
+                                         unsigned *s_kk) {
+  constexpr int BPT = NBINS >= 1024 ? NBINS / 1024 : 1;
+  const int t = threadIdx.x;
+  unsigned c[BPT];
   unsigned sum = 0;
 #pragma unroll
-  for (int i = 0; i < BPL; ++i) {
-    c[i] = hist[hi - i];
+  for (int i = 0; i < BPT; ++i) {
+    const int r = t * BPT + i;  // rank of the bin from the top
+    c[i] = r < NBINS ? hist(NBINS - 1 - r) : 0u;
     sum += c[i];
   }
-  const unsigned incl = wave_incl_scan(sum);
-  unsigned above = incl - sum;  // keys in higher bins than this lane's block
-  if (above < kk && incl >= kk) {
+  unsigned tot;
+  unsigned above = block_excl_scan<16>(sum, wsum, tot);
+  if (above < kk && above + sum >= kk) {
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) {
+    for (int i = 0; i < BPT; ++i) {
       if (above < kk && above + c[i] >= kk) {
-        *s_bin = (unsigned)(hi - i);
+        *s_bin = (unsigned)(NBINS - 1 - (t * BPT + i));
         *s_kk = kk - above;
       }
       above += c[i];
@@ -384,10 +388,12 @@ __device__ __forceinline__ void pick_bin(const unsigned *hist, unsigned kk,
 // Union of the per-token mask words (several tokens): U ascending, plus for
 // each entry the bit set of tokens whose mask holds it.  All 1024 threads of
 // one work-group; thread w owns mask word w (channels 32 w .. 32 w + 31, d_ff
-// <= 32768), reads that word of every token, and writes its union entries at
-// its exclusive prefix of the word popcounts.
+// <= 32768), reads that word of every token and places its union entries at
+// its exclusive prefix of the word popcounts, in LDS; the work-group then
+// writes the list out in order, consecutive threads on consecutive entries.
 __device__ __forceinline__ void mask_union(const unsigned *selw, int d_ff, int nb, int *uni,
-                                           int *nuni, uint8_t *umask, unsigned *wsum) {
+                                           int *nuni, uint8_t *umask, unsigned *wsum,
+                                           uint16_t *su, uint8_t *sb) {
   const int w = threadIdx.x;
   const int words = (d_ff + 31) >> 5;
   unsigned tw[kMaxBatch], u = 0u;
@@ -404,9 +410,14 @@ __device__ __forceinline__ void mask_union(const unsigned *selw, int d_ff, int n
     unsigned m = 0u;
 #pragma unroll
     for (int b = 0; b < kMaxBatch; ++b) m |= ((tw[b] >> bit) & 1u) << b;
-    uni[pos] = w * 32 + bit;
-    umask[pos] = (uint8_t)m;
+    su[pos] = (uint16_t)(w * 32 + bit);
+    sb[pos] = (uint8_t)m;
     ++pos;
+  }
+  __syncthreads();
+  for (int p = w; p < (int)total; p += 1024) {
+    uni[p] = (int)su[p];
+    umask[p] = sb[p];
   }
   if (w == 0) *nuni = (int)total;
 }
@@ -417,13 +428,18 @@ template <int PER>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff, int k,
                                                     int *sel, unsigned *selw, unsigned *ucnt,
                                                     int *uni, int *nuni, uint8_t *umask) {
-  __shared__ unsigned h1[2048];
+  // digit 1 in 4 copies (waves w and w + 4 share one), so that keys of the
+  // few crowded bins queue on 4 addresses instead of 1
+  __shared__ unsigned h1[4][2048];
   __shared__ unsigned h2[2048];
   __shared__ unsigned h3[512];
   __shared__ unsigned cnt[PER * 16];
   __shared__ unsigned s_bin, s_kk;
   __shared__ unsigned wsum[16];
   __shared__ int s_last;
+  // the union list before it goes out (last work-group, several tokens)
+  __shared__ uint16_t su[kMaxDff];
+  __shared__ uint8_t sb[kMaxDff];
   const int b = blockIdx.x;
   if (k <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -437,7 +453,11 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
     const int j = e * 1024 + tid;
     key[e] = (j < d_ff) ? __float_as_uint(z[j]) : 0u;
   }
-  h1[tid] = 0u; h1[tid + 1024] = 0u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    h1[c][tid] = 0u;
+    h1[c][tid + 1024] = 0u;
+  }
   h2[tid] = 0u; h2[tid + 1024] = 0u;
   if (tid < 512) h3[tid] = 0u;
   __syncthreads();
@@ -445,9 +465,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   // Digit 1: bits 30..20.
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    if (e * 1024 + tid < d_ff) atomicAdd(&h1[key[e] >> 20], 1u);
+    if (e * 1024 + tid < d_ff) atomicAdd(&h1[w & 3][key[e] >> 20], 1u);
   __syncthreads();
-  if (w == 0) pick_bin<2048>(h1, (unsigned)k, &s_bin, &s_kk);
+  pick_bin<2048>([&](int i) { return h1[0][i] + h1[1][i] + h1[2][i] + h1[3][i]; }, (unsigned)k,
+                 wsum, &s_bin, &s_kk);
   __syncthreads();
   const unsigned b1 = s_bin;
   unsigned kk = s_kk;
@@ -457,7 +478,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   for (int e = 0; e < PER; ++e)
     if (e * 1024 + tid < d_ff && (key[e] >> 20) == b1) atomicAdd(&h2[(key[e] >> 9) & 2047u], 1u);
   __syncthreads();
-  if (w == 0) pick_bin<2048>(h2, kk, &s_bin, &s_kk);
+  pick_bin<2048>([&](int i) { return h2[i]; }, kk, wsum, &s_bin, &s_kk);
   __syncthreads();
   const unsigned p2 = (b1 << 11) | s_bin;
   kk = s_kk;
@@ -467,7 +488,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   for (int e = 0; e < PER; ++e)
     if (e * 1024 + tid < d_ff && (key[e] >> 9) == p2) atomicAdd(&h3[key[e] & 511u], 1u);
   __syncthreads();
-  if (w == 0) pick_bin<512>(h3, kk, &s_bin, &s_kk);
+  pick_bin<512>([&](int i) { return h3[i]; }, kk, wsum, &s_bin, &s_kk);
   __syncthreads();
   const unsigned T = (p2 << 9) | s_bin;
   kk = s_kk;  // keys equal to T that are kept (the lowest-index ones)
@@ -537,7 +558,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   }
   if (ucnt) {
     if (!arrive_last(ucnt, gridDim.x, &s_last)) return;
-    mask_union(selw, d_ff, (int)gridDim.x, uni, nuni, umask, wsum);
+    mask_union(selw, d_ff, (int)gridDim.x, uni, nuni, umask, wsum, su, sb);
   }
 }
 // ---------------------------------------------------------------------------
