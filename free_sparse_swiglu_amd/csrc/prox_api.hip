@@ -105,6 +105,9 @@ Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act) {
   p.use_fused = fused_supported(p) && !(path && strcmp(path, "multi") == 0);
   const char *bg = getenv("PROX_BATCH_GEMV");
   p.batch_mfma = bg && strcmp(bg, "mfma") == 0;
+  const char *bp = getenv("PROX_BATCH_PROXY");
+  p.proxy_mfma = bf16 && max_batch >= 2 && G % 32 == 0 && d_model % 32 == 0 &&
+                 !(bp && strcmp(bp, "valu") == 0);
   return p;
 }
 
@@ -117,7 +120,8 @@ Layout make_layout(const Plan &p) {
   const size_t pq = (size_t)p.ntile * p.d_model * kTileBytes;
   L.o_psc = align256(pq);
   L.o_pred = align256(L.o_psc + (size_t)p.ntile * p.ngroups * 512 * sizeof(float));
-  L.proxy = L.o_pred + 256;
+  L.o_pq2 = L.o_pred + 256;
+  L.proxy = L.o_pq2 + (p.proxy_mfma ? align256(pq) : 0);
   size_t o = 0;
   L.o_part = o;      o = align256(o + (size_t)p.ntile * p.nchunk * B * 512 * sizeof(float));
   L.o_tile_cnt = o;  o = align256(o + (size_t)p.ntile * sizeof(unsigned));
@@ -281,6 +285,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.pq = (uint8_t *)pb;
   b.psc = (float *)(pb + lay.o_psc);
   b.pred = (unsigned *)(pb + lay.o_pred);
+  b.pq2 = L->plan.proxy_mfma ? (unsigned *)(pb + lay.o_pq2) : nullptr;
   b.part = (float *)(ws + lay.o_part);
   b.tile_cnt = (unsigned *)(ws + lay.o_tile_cnt);
   b.sabs = (float *)(ws + lay.o_sabs);

@@ -32,6 +32,8 @@ struct Bufs {
   void *wd;        // [d_model/256][d_ff][256] dtype: W_down in 256-column chunks
   // proxy_buf
   uint8_t *pq;     // [ntile][d_model][256] bytes: (code + 8) nibbles, up | gate
+  unsigned *pq2;   // [ntile][d_model/8][512] words: the same codes, 8 rows of one
+                   //     proxy column per word (proxy_mfma layers only)
   float *psc;      // [ntile][ngroups][2][256] float32 scales
   unsigned *pred;  // [1] layer state kept across calls: b* of the last batch-1
                    //     top-k call + 1 (0: none), a guess of the next cut
@@ -66,11 +68,12 @@ struct Plan {
   int use_fused;    // batch-1 forwards run the persistent fused kernel
   int act;          // gate activation: 0 SiLU, 1 GELU (tanh form)
   int batch_mfma;   // bf16 batches of 2..8 tokens: up/gate on MFMA (default: VALU dot2)
+  int proxy_mfma;   // bf16 batches of 2..8 tokens: Stage 1 on MFMA over pq2
 };
 
 struct Layout {
   size_t weights, proxy, workspace;
-  size_t o_wd, o_psc, o_pred;
+  size_t o_wd, o_psc, o_pred, o_pq2;
   size_t o_part, o_tile_cnt, o_sabs, o_sel, o_selw, o_ssp, o_uni, o_nuni, o_umask,
       o_ypart, o_col_cnt, o_ucnt, o_sync, o_xbuf, o_ybuf;
 };

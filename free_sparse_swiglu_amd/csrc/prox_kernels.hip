@@ -134,8 +134,12 @@ __global__ __launch_bounds__(256) void export_proxy_kernel(
 //   float32 layers: byte -> float conversion and one FMA per code.
 // The last work-group to finish a tile adds the partials of all chunks in a
 // fixed order and writes |s~| = |u~ * SiLU(g~)| for the tile's columns.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 struct ProxyArgs {
   const uint8_t *pq;
+  const unsigned *pq2;  // codes in 8-row words (matrix-core form), or null
   const float *psc;
   const void *x;
   float tau;
@@ -328,6 +332,163 @@ __global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a)
   if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, &s_last)) return;
 
   // Tile epilogue: u~, g~ for 256 columns per token, then |s~|.
+  const float *tp = a.part + (size_t)t * a.nchunk * NB * 512;
+  for (int e = threadIdx.x; e < NB * 256; e += 512) {
+    const int b = e >> 8, col = e & 255;
+    const float u = xsum_strided(&tp[(size_t)b * 512 + col], a.nchunk, (size_t)NB * 512);
+    const float gg = xsum_strided(&tp[(size_t)b * 512 + 256 + col], a.nchunk, (size_t)NB * 512);
+    const int j = t * kTile + col;
+    if (j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(u * gate_act(gg, a.act));
+  }
+}
+
+// Stage 1 on the matrix cores for 2..8 tokens (bf16 layers, G and d_model
+// multiples of 32), same work split and partials as proxy_kernel: one
+// work-group per (512-row chunk, tile), wave w on proxy columns 64 w ..
+// 64 w + 63 of the tile (up 0..255, gate 256..511).  The codes come from
+// pq2, where one word holds 8 consecutive rows of one proxy column (byte q:
+// row 2q low nibble, row 2q + 1 high nibble), so a lane's 16-byte load is
+// the K-run of 8 rows for 4 columns: the A operand of 4 MFMAs at once.
+// v_mfma_f32_16x16x32_bf16, per 32-row step s and r = 0..3:
+//   A: lane l holds column c0 + 4 (l%16) + r, rows 32 s + 8 (l/16) .. +7, as
+//      bf16 128 + nib (the nibble under the exponent byte 0x43, exact);
+//   B: lane l holds token l%16 (tokens past NB repeat the last one; their
+//      results are dropped), the same rows of x masked by its own
+//      threshold, from LDS;
+//   D: element i of lane l = column c0 + 16 (l/16) + 4 i + r, token l%16.
+// sum_i x_i (128 + nib_i) = sum_i x_i q_i + 136 sum_i x_i, so at the end of
+// each G-row group the step sums of x take out the offset and the column's
+// group scale is applied: acc += S (D - 136 sum x).  The whole matrix is
+// read whatever the input mask: at 2 or more tokens the union of the masks
+// leaves few 8-row blocks empty.
+__global__ __launch_bounds__(512) void retile_pq2_kernel(const uint8_t *pq, unsigned *pq2,
+                                                         int d_model) {
+  const int rb = blockIdx.x, t = blockIdx.y, pc = threadIdx.x;
+  const uint8_t *src = pq + ((size_t)t * d_model + (size_t)rb * 8) * kTileBytes + (pc >> 1);
+  const int sh = (pc & 1) * 4;
+  unsigned w = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w |= (unsigned)((src[(size_t)e * kTileBytes] >> sh) & 0xfu) << (4 * e);
+  pq2[((size_t)t * (d_model / 8) + rb) * 512 + pc] = w;
+}
+
+template <int NB>
+__global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
+  constexpr int KS = 16;  // 32-row steps per 512-row chunk
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NB][512];  // masked x (bf16 bits)
+  __shared__ float xk[NB][KS];                                    // its sum over each step
+  __shared__ float ss[KS][512];  // group scales of the chunk's groups (at most one per step)
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int chunk = blockIdx.x, t = blockIdx.y;
+  const int r0 = chunk * 512;
+  const int nks = min(KS, (a.d_model - r0) / 32);
+  const int c0 = wv * 64;
+  const int grp0 = r0 / a.G;
+  const int ngc = (r0 + 32 * nks - 1) / a.G - grp0 + 1;  // groups the chunk touches (<= KS)
+
+  // Masked x of the chunk's rows per token and the group scales go out
+  // first; the codes (the whole chunk for this wave's columns, 16 bytes per
+  // lane per step) right behind them, so that the staging below waits only
+  // for its own loads and each step only for its codes.
+  const int i0 = threadIdx.x, row = r0 + i0;
+  float xv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) xv[b] = row < a.d_model ? ld_elem<true>(a.x, (size_t)b * a.d_model + row) : 0.0f;
+  float sv[KS];
+#pragma unroll
+  for (int q = 0; q < KS; ++q)
+    sv[q] = q < ngc ? a.psc[((size_t)t * a.ngroups + grp0 + q) * 512 + i0] : 0.0f;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(a.pq2 + (size_t)t * (a.d_model / 8) * 512, (uint32_t)a.d_model * kTileBytes);
+  u4 w[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const uint32_t off = ((uint32_t)(chunk * 64 + 4 * s + g) * 512u + (uint32_t)(c0 + 4 * m)) * 4u;
+    w[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);  // past d_model: 0, unused
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float v = fabsf(xv[b]) >= a.tau ? xv[b] : 0.0f;
+    xs[b][i0] = (uint16_t)(__float_as_uint(v) >> 16);
+    // sum over the 32 rows of this half-wave
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((lane & 31) == 0) xk[b][i0 >> 5] = v;
+  }
+#pragma unroll
+  for (int q = 0; q < KS; ++q)
+    if (q < ngc) ss[q][i0] = sv[q];
+  // LDS written; the codes may still be in flight (a plain barrier, no wait
+  // on memory loads)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  const int tok = min(m, NB - 1);
+  f32x4_t acc[4], d[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    d[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  uint32_t nib_mask;
+  asm volatile("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(nib_mask));
+  float xg = 0.0f;  // sum of this lane's token's masked x over the current group
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s < nks) {
+      bf16x8_t B;
+      __builtin_memcpy(&B, &xs[tok][32 * s + 8 * g], 16);
+      const uint32_t wd[4] = {w[s].x, w[s].y, w[s].z, w[s].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = wd[r] & nib_mask, hi = (wd[r] >> 4) & nib_mask;
+        uint32_t q[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          q[qq] = __builtin_amdgcn_perm(hi, lo, (uint32_t)qq | 0x0c00u | ((uint32_t)(4 + qq) << 16) |
+                                                    0x0c000000u) |
+                  0x43004300u;
+        bf16x8_t A;
+        __builtin_memcpy(&A, q, 16);
+        d[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, d[r], 0, 0, 0);
+      }
+      xg += xk[tok][s];
+      const int row_end = r0 + 32 * (s + 1);
+      if (s == nks - 1 || row_end % a.G == 0) {
+        const int gi = (row_end - 1) / a.G - grp0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[r][i] += ss[gi][c0 + 16 * g + 4 * i + r] * (d[r][i] - 136.0f * xg);
+            d[r][i] = 0.0f;
+          }
+        xg = 0.0f;
+      }
+    }
+  }
+  // This chunk's partials: lane l holds columns c0 + 16 (l/16) .. +15 of
+  // token l%16; through LDS (the scales' space) so that the stores are whole
+  // rows.
+  __syncthreads();  // every wave is done with the scales
+  float (*red)[512] = ss;
+  static_assert(NB <= KS, "partials fit the scale array");
+  if (m < NB) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(float4 *)&red[m][c0 + 16 * g + 4 * i] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+  }
+  __syncthreads();
+  {
+    float *part = a.part + ((size_t)t * a.nchunk + chunk) * NB * 512;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xstore(&part[b * 512 + i0], red[b][i0]);
+  }
+  if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, &s_last)) return;
+
+  // Tile epilogue, as in proxy_kernel: u~, g~ per token, then |s~|.
   const float *tp = a.part + (size_t)t * a.nchunk * NB * 512;
   for (int e = threadIdx.x; e < NB * 256; e += 512) {
     const int b = e >> 8, col = e & 255;
@@ -977,6 +1138,10 @@ hipError_t launch_prepare(const Plan &p, const Bufs &b, const void *w_up,
                                               p.d_ff, p.G, p.ngroups);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.proxy_mfma && b.pq2) {
+    retile_pq2_kernel<<<dim3(p.d_model / 8, p.ntile), 512, 0, s>>>(b.pq, b.pq2, p.d_model);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   e = hipMemsetAsync(b.tile_cnt, 0, sizeof(unsigned) * p.ntile, s);
   if (e != hipSuccess) return e;
   if ((e = hipMemsetAsync(b.col_cnt, 0, sizeof(unsigned) * p.ncol, s)) != hipSuccess) return e;
@@ -993,10 +1158,16 @@ hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
 
 hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
                         float tau, hipStream_t s) {
-  ProxyArgs a{b.pq, b.psc, x, tau, p.d_model, p.d_ff, p.G, p.ngroups,
+  ProxyArgs a{b.pq, b.pq2, b.psc, x, tau, p.d_model, p.d_ff, p.G, p.ngroups,
               p.nchunk, b.part, b.tile_cnt, b.sabs, p.act};
   dim3 g(p.nchunk, p.ntile);
-  if (p.bf16) {
+  // From 3 tokens on the matrix cores: at 2 the VALU kernel is faster (it
+  // reads only the rows the union of the input masks keeps, about 3/4 of
+  // them; measured at the 70B shape 54 against 62 us, and 81 against 69 us
+  // at 4 tokens).  Same grid: ceil(d_model / 512) work-groups per tile.
+  if (p.proxy_mfma && b.pq2 && batch >= 3) {
+    PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB><<<g, 512, 0, s>>>(a)));
+  } else if (p.bf16) {
     PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true><<<g, 512, 0, s>>>(a)));
   } else {
     PROX_DISPATCH_NB(batch, (proxy_kernel<NB, false><<<g, 512, 0, s>>>(a)));
@@ -1039,8 +1210,6 @@ hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool list
 // in flight; x comes from L2.  Each load instruction reads 64 bytes from each
 // of 16 rows, against 1 KB of one row in the VALU form, and measured slower
 // than the VALU form at 2, 4 and 8 tokens, so it runs only on request.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int NB, int MODE>
 __global__ __launch_bounds__(256) void upgate_mfma_kernel(UpGateArgs a) {
