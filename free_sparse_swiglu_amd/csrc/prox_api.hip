@@ -106,7 +106,7 @@ Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act) {
   const char *bg = getenv("PROX_BATCH_GEMV");
   p.batch_mfma = bg && strcmp(bg, "mfma") == 0;
   const char *bp = getenv("PROX_BATCH_PROXY");
-  p.proxy_mfma = bf16 && max_batch >= 2 && G % 32 == 0 && d_model % 32 == 0 &&
+  p.proxy_mfma = bf16 && max_batch >= 2 && G % 64 == 0 && d_model % 32 == 0 &&
                  !(bp && strcmp(bp, "valu") == 0);
   return p;
 }

@@ -342,10 +342,11 @@ __global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a)
   }
 }
 
-// Stage 1 on the matrix cores for 2..8 tokens (bf16 layers, G and d_model
-// multiples of 32), same work split and partials as proxy_kernel: one
-// work-group per (512-row chunk, tile), wave w on proxy columns 64 w ..
-// 64 w + 63 of the tile (up 0..255, gate 256..511).  The codes come from
+// Stage 1 on the matrix cores for 3..8 tokens (bf16 layers, G a multiple of
+// 64, d_model of 32), the partials and tile epilogue of proxy_kernel: one
+// work-group per (chunk of kMfmaRows rows, tile), wave w on proxy columns
+// 64 w .. 64 w + 63 of the tile (up 0..255, gate 256..511), with 16 steps
+// of codes in flight throughout.  The codes come from
 // pq2, where one word holds 8 consecutive rows of one proxy column (byte q:
 // row 2q low nibble, row 2q + 1 high nibble), so a lane's 16-byte load is
 // the K-run of 8 rows for 4 columns: the A operand of 4 MFMAs at once.
@@ -372,54 +373,72 @@ __global__ __launch_bounds__(512) void retile_pq2_kernel(const uint8_t *pq, unsi
   pq2[((size_t)t * (d_model / 8) + rb) * 512 + pc] = w;
 }
 
+// Rows per work-group of the matrix-core Stage 1 (its own chunking; partials
+// and the tile counter use kMfmaRows-row chunks).
+constexpr int kMfmaRows = 1024;
+
 template <int NB>
 __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
-  constexpr int KS = 16;  // 32-row steps per 512-row chunk
-  __shared__ __attribute__((aligned(16))) uint16_t xs[NB][512];  // masked x (bf16 bits)
-  __shared__ float xk[NB][KS];                                    // its sum over each step
-  __shared__ float ss[KS][512];  // group scales of the chunk's groups (at most one per step)
+  constexpr int KS = 32;  // 32-row steps per chunk of kMfmaRows rows
+  constexpr int WIN = 16;  // steps of codes in flight per wave
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NB][kMfmaRows];  // masked x (bf16 bits)
+  __shared__ float xk[NB][KS];                                         // its sum over each step
+  __shared__ float ss[kMfmaRows / 64][512];  // group scales of the chunk's groups (G >= 64)
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int chunk = blockIdx.x, t = blockIdx.y;
-  const int r0 = chunk * 512;
+  const int r0 = chunk * kMfmaRows;
   const int nks = min(KS, (a.d_model - r0) / 32);
   const int c0 = wv * 64;
   const int grp0 = r0 / a.G;
-  const int ngc = (r0 + 32 * nks - 1) / a.G - grp0 + 1;  // groups the chunk touches (<= KS)
+  const int ngc = (r0 + 32 * nks - 1) / a.G - grp0 + 1;  // groups the chunk touches
 
   // Masked x of the chunk's rows per token and the group scales go out
-  // first; the codes (the whole chunk for this wave's columns, 16 bytes per
-  // lane per step) right behind them, so that the staging below waits only
-  // for its own loads and each step only for its codes.
-  const int i0 = threadIdx.x, row = r0 + i0;
-  float xv[NB];
+  // first; the first WIN steps of codes (16 bytes per lane per step) right
+  // behind them, so that the staging below waits only for its own loads.
+  // Each later step's codes are requested as a step is consumed.
+  const int i0 = threadIdx.x;
+  float xv[2][NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) xv[b] = row < a.d_model ? ld_elem<true>(a.x, (size_t)b * a.d_model + row) : 0.0f;
-  float sv[KS];
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int q = 0; q < KS; ++q)
-    sv[q] = q < ngc ? a.psc[((size_t)t * a.ngroups + grp0 + q) * 512 + i0] : 0.0f;
+    for (int b = 0; b < NB; ++b) {
+      // clamped loads, no branch: every load in flight at once
+      const int row = r0 + i0 + 512 * h;
+      const float v = ld_elem<true>(a.x, (size_t)b * a.d_model + min(row, a.d_model - 1));
+      xv[h][b] = row < a.d_model ? v : 0.0f;
+    }
+  constexpr int NGC = kMfmaRows / 64;
+  float sv[NGC];
+#pragma unroll
+  for (int q = 0; q < NGC; ++q)
+    sv[q] = a.psc[((size_t)t * a.ngroups + grp0 + min(q, ngc - 1)) * 512 + i0];
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.pq2 + (size_t)t * (a.d_model / 8) * 512, (uint32_t)a.d_model * kTileBytes);
-  u4 w[KS];
+  auto code_off = [&](int s) {
+    return ((uint32_t)(r0 / 8 + 4 * s + g) * 512u + (uint32_t)(c0 + 4 * m)) * 4u;
+  };
+  u4 w[WIN];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const uint32_t off = ((uint32_t)(chunk * 64 + 4 * s + g) * 512u + (uint32_t)(c0 + 4 * m)) * 4u;
-    w[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);  // past d_model: 0, unused
-  }
+  for (int s = 0; s < WIN; ++s)  // past d_model: 0, unused
+    w[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, code_off(s), 0, kNT);
+  // (kept ahead of the staging: the scheduler would sink them below it)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float v = fabsf(xv[b]) >= a.tau ? xv[b] : 0.0f;
-    xs[b][i0] = (uint16_t)(__float_as_uint(v) >> 16);
-    // sum over the 32 rows of this half-wave
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    if ((lane & 31) == 0) xk[b][i0 >> 5] = v;
-  }
+    for (int b = 0; b < NB; ++b) {
+      float v = fabsf(xv[h][b]) >= a.tau ? xv[h][b] : 0.0f;
+      xs[b][i0 + 512 * h] = (uint16_t)(__float_as_uint(v) >> 16);
+      // sum over the 32 rows of this half-wave
 #pragma unroll
-  for (int q = 0; q < KS; ++q)
+      for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+      if ((lane & 31) == 0) xk[b][(i0 + 512 * h) >> 5] = v;
+    }
+#pragma unroll
+  for (int q = 0; q < NGC; ++q)
     if (q < ngc) ss[q][i0] = sv[q];
   // LDS written; the codes may still be in flight (a plain barrier, no wait
   // on memory loads)
@@ -437,10 +456,11 @@ __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
   float xg = 0.0f;  // sum of this lane's token's masked x over the current group
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
+    const uint32_t wd[4] = {w[s % WIN].x, w[s % WIN].y, w[s % WIN].z, w[s % WIN].w};
+    if (s + WIN < KS) w[s % WIN] = __builtin_amdgcn_raw_buffer_load_b128(rs, code_off(s + WIN), 0, kNT);
     if (s < nks) {
       bf16x8_t B;
       __builtin_memcpy(&B, &xs[tok][32 * s + 8 * g], 16);
-      const uint32_t wd[4] = {w[s].x, w[s].y, w[s].z, w[s].w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t lo = wd[r] & nib_mask, hi = (wd[r] >> 4) & nib_mask;
@@ -1164,9 +1184,11 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
   // From 3 tokens on the matrix cores: at 2 the VALU kernel is faster (it
   // reads only the rows the union of the input masks keeps, about 3/4 of
   // them; measured at the 70B shape 54 against 62 us, and 81 against 69 us
-  // at 4 tokens).  Same grid: ceil(d_model / 512) work-groups per tile.
+  // at 4 tokens).  Its own grid: ceil(d_model / kMfmaRows) work-groups per tile.
   if (p.proxy_mfma && b.pq2 && batch >= 3) {
-    PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB><<<g, 512, 0, s>>>(a)));
+    a.nchunk = (p.d_model + kMfmaRows - 1) / kMfmaRows;
+    const dim3 gm(a.nchunk, p.ntile);
+    PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB><<<gm, 512, 0, s>>>(a)));
   } else if (p.bf16) {
     PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true><<<g, 512, 0, s>>>(a)));
   } else {

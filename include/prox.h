@@ -81,7 +81,7 @@ typedef struct prox_layer prox_layer;
  *   proxy_bytes     packed INT4 proxy codes and their float32 scales, plus
  *                   one word of layer state that batch-1 top-k calls update
  *                   (a guess of the next cut, used for scheduling only); bf16
- *                   layers with max_batch >= 2 (G and d_model multiples of 32)
+ *                   layers with max_batch >= 2 (G a multiple of 64, d_model of 32)
  *                   hold the codes a second time, 8 rows of one column per
  *                   word, for the matrix-core Stage 1 of several tokens
  *   workspace_bytes per-call scratch: partial sums, counters, masks, s values
