@@ -1183,7 +1183,7 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
   dim3 g(p.nchunk, p.ntile);
   // From 3 tokens on the matrix cores: at 2 the VALU kernel is faster (it
   // reads only the rows the union of the input masks keeps, about 3/4 of
-  // them; measured at the 70B shape 54 against 62 us, and 81 against 69 us
+  // them; measured at the 70B shape 54 against 59 us, and 81 against 63 us
   // at 4 tokens).  Its own grid: ceil(d_model / kMfmaRows) work-groups per tile.
   if (p.proxy_mfma && b.pq2 && batch >= 3) {
     a.nchunk = (p.d_model + kMfmaRows - 1) / kMfmaRows;

@@ -279,6 +279,30 @@ def test_batch_mfma_form_parity(B, monkeypatch):
     assert rel_err(yv.float().cpu().numpy(), out["y"].float().cpu().numpy()) <= _tol(RAGGED)
 
 
+@pytest.mark.parametrize("B", [3, 8])
+def test_batch_stage1_mfma_matches_valu(B, monkeypatch):
+    """Stage 1 of 3..8 tokens runs on the matrix cores over the 8-row code
+    words written at prepare time: its |s~| against the oracle (through the
+    mask and output checks) and against the VALU Stage 1 of a layer prepared
+    with PROX_BATCH_PROXY=valu (same codes, other summation order)."""
+    monkeypatch.setenv("PROX_BATCH_PROXY", "valu")
+    valu = Case(RAGGED, 0, "cpu", 8)
+    monkeypatch.delenv("PROX_BATCH_PROXY")
+    mf = get_case(RAGGED, max_batch=8)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    X = mf.inputs(B, "stage1mfma")
+    xd = X.to(DEV)
+    out_m = prox.prox_ffn_forward_debug(mf.L, xd, mf.tau, k)
+    out_v = prox.prox_ffn_forward_debug(valu.L, xd, valu.tau, k)
+    torch.cuda.synchronize()
+    for t in range(B):
+        _check_token(mf, xd[t], X[t].float().numpy(), mf.tau, k, out_m, t=t)
+        sm = out_m["s_abs"][t].cpu().numpy().astype(np.float64)
+        sv = out_v["s_abs"][t].cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(sm))
+        assert rel_err(sm, sv) <= 1e-5, f"token {t}: {rel_err(sm, sv):.3e}"
+
+
 def test_batch_split_tie():
     """A zero token has |s~| = 0 everywhere: its mask is the k lowest
     channels (ties to the lower index), the product path (mask words only)
