@@ -331,14 +331,42 @@ __global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a)
 
   if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, &s_last)) return;
 
-  // Tile epilogue: u~, g~ for 256 columns per token, then |s~|.
+  // Tile epilogue: u~, g~ per token, then |s~|, the chunk partials added in
+  // chunk order, every partial of this thread's (token, column) pairs
+  // requested at once, 8 chunks per round.
   const float *tp = a.part + (size_t)t * a.nchunk * NB * 512;
-  for (int e = threadIdx.x; e < NB * 256; e += 512) {
+  constexpr int PP = (NB * 256 + 511) / 512;  // pairs per thread
+  float su[PP], sg[PP];
+#pragma unroll
+  for (int p = 0; p < PP; ++p) su[p] = sg[p] = 0.0f;
+  for (int cb = 0; cb < a.nchunk; cb += 8) {
+    float vu[PP][8], vg[PP][8];
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+      const int e = min((int)threadIdx.x + 512 * p, NB * 256 - 1);
+      const int b = e >> 8, col = e & 255;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float *q = tp + ((size_t)min(cb + c, a.nchunk - 1) * NB + b) * 512 + col;
+        vu[p][c] = xload(q);
+        vg[p][c] = xload(q + 256);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PP; ++p)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (cb + c < a.nchunk) {
+          su[p] += vu[p][c];
+          sg[p] += vg[p][c];
+        }
+  }
+#pragma unroll
+  for (int p = 0; p < PP; ++p) {
+    const int e = (int)threadIdx.x + 512 * p;
     const int b = e >> 8, col = e & 255;
-    const float u = xsum_strided(&tp[(size_t)b * 512 + col], a.nchunk, (size_t)NB * 512);
-    const float gg = xsum_strided(&tp[(size_t)b * 512 + 256 + col], a.nchunk, (size_t)NB * 512);
     const int j = t * kTile + col;
-    if (j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(u * gate_act(gg, a.act));
+    if (e < NB * 256 && j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(su[p] * gate_act(sg[p], a.act));
   }
 }
 
@@ -508,14 +536,42 @@ __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
   }
   if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, &s_last)) return;
 
-  // Tile epilogue, as in proxy_kernel: u~, g~ per token, then |s~|.
+  // Tile epilogue: u~, g~ per token, then |s~|, the chunk partials added in
+  // chunk order (as proxy_kernel does), every partial of this thread's
+  // (token, column) pairs requested at once, 8 chunks per round.
   const float *tp = a.part + (size_t)t * a.nchunk * NB * 512;
-  for (int e = threadIdx.x; e < NB * 256; e += 512) {
+  constexpr int PP = (NB * 256 + 511) / 512;  // pairs per thread
+  float su[PP], sg[PP];
+#pragma unroll
+  for (int p = 0; p < PP; ++p) su[p] = sg[p] = 0.0f;
+  for (int cb = 0; cb < a.nchunk; cb += 8) {
+    float vu[PP][8], vg[PP][8];
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+      const int e = min((int)threadIdx.x + 512 * p, NB * 256 - 1);
+      const int b = e >> 8, col = e & 255;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float *q = tp + ((size_t)min(cb + c, a.nchunk - 1) * NB + b) * 512 + col;
+        vu[p][c] = xload(q);
+        vg[p][c] = xload(q + 256);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PP; ++p)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (cb + c < a.nchunk) {
+          su[p] += vu[p][c];
+          sg[p] += vg[p][c];
+        }
+  }
+#pragma unroll
+  for (int p = 0; p < PP; ++p) {
+    const int e = (int)threadIdx.x + 512 * p;
     const int b = e >> 8, col = e & 255;
-    const float u = xsum_strided(&tp[(size_t)b * 512 + col], a.nchunk, (size_t)NB * 512);
-    const float gg = xsum_strided(&tp[(size_t)b * 512 + 256 + col], a.nchunk, (size_t)NB * 512);
     const int j = t * kTile + col;
-    if (j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(u * gate_act(gg, a.act));
+    if (e < NB * 256 && j < a.d_ff) a.sabs[(size_t)b * a.d_ff + j] = fabsf(su[p] * gate_act(sg[p], a.act));
   }
 }
 
