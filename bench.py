@@ -78,32 +78,26 @@ def algorithmic_bytes(cfg, n1, groups_touched, k, batch=1, union=None):
                 total=stage1 + upgate + down + io)
 
 
-def build_ring(cfg, ring, max_batch=1, path=None, activation=0):
-    """Prepare `ring` seeded layers sharing one workspace.  path="multi"
-    prepares them for the multi-kernel path (one kernel per phase);
-    activation 1 makes them GeGLU layers."""
+def build_ring(cfg, ring, max_batch=1, path=0, activation=0, batch_upgate=0):
+    """Prepare `ring` seeded layers sharing one workspace.  path=1
+    (PROX_PATH_MULTI) prepares them for the multi-kernel path (one kernel per
+    phase); activation 1 makes them GeGLU layers; batch_upgate is the
+    prox_form of the batched up/gate step."""
     import torch
 
     from free_sparse_swiglu_amd import prox, synth
     layers, taus = [], []
     ws = None
-    old = os.environ.get("PROX_PATH")
-    if path:
-        os.environ["PROX_PATH"] = path
     for l in range(ring):
         W = synth.make_layer(cfg, l, "cuda")
         L = prox.prox_prepare_layer(*W, cfg.group, max_batch, workspace=ws,
-                                    activation=activation)
+                                    activation=activation, path=path,
+                                    batch_upgate=batch_upgate)
         ws = L.workspace
         torch.cuda.synchronize()
         del W
         layers.append(L)
         taus.append(synth.layer_tau(cfg, l, "cuda"))
-    if path:
-        if old is None:
-            os.environ.pop("PROX_PATH", None)
-        else:
-            os.environ["PROX_PATH"] = old
     return layers, taus
 
 
@@ -246,7 +240,7 @@ def bench_single_layer(args, name):
 
     # The same step on the multi-kernel path (one kernel per phase), for the
     # per-phase breakdown.
-    mlayers, _ = build_ring(cfg, R, path="multi")
+    mlayers, _ = build_ring(cfg, R, path=prox.PROX_PATH_MULTI)
 
     def mstep(i):
         l = i % R
@@ -367,7 +361,8 @@ def bench_batch(args):
     from free_sparse_swiglu_amd import prox, synth
     cfg = synth.CONFIGS["70b"]
     k = synth.k_for(cfg.d_ff, args.sparsity)
-    layers, taus = build_ring(cfg, args.ring, max_batch=8)
+    form = prox.PROX_FORM_MFMA if args.batch_gemv == "mfma" else prox.PROX_FORM_AUTO
+    layers, taus = build_ring(cfg, args.ring, max_batch=8, batch_upgate=form)
     R = len(layers)
     out = {}
     for B in cfg.batches:
@@ -531,6 +526,57 @@ def bench_alpha(args):
                 shapes=out)
 
 
+def bench_timeline(args):
+    """Per-phase timeline of the persistent kernel at the 8B shape (k at the
+    requested sparsity): each traced call records, per work item, its start,
+    the end of its wait for earlier items and its end (100 MHz GPU clock).
+    Reported per phase, in microseconds from the call's first item start:
+    the median over calls of the first start, the median start, the last end
+    and the median wait."""
+    import numpy as np
+    import torch
+
+    from free_sparse_swiglu_amd import prox, synth
+    cfg = synth.CONFIGS["8b"]
+    k = synth.k_for(cfg.d_ff, args.sparsity)
+    layers, taus = build_ring(cfg, min(args.ring, 4))
+    R = len(layers)
+    X = [synth.make_inputs(cfg, 8, "bench", l, "cuda") for l in range(R)]
+    y = torch.empty(cfg.d_model, dtype=X[0].dtype, device="cuda")
+    for i in range(args.warmup):
+        prox.prox_ffn_forward(layers[i % R], X[i % R][i % 8], taus[i % R], k, y)
+    names = {1: "stage1", 2: "select", 3: "upgate", 4: "down"}
+    per = {n: dict(first_start=[], med_start=[], last_end=[], med_wait=[], med_dur=[])
+           for n in names.values()}
+    spans = []
+    ncalls = max(4, min(args.steps, 40))
+    for i in range(ncalls):
+        l = i % R
+        _, tr, counts = prox.prox_ffn_forward_traced(layers[l], X[l][i % 8], taus[l], k, y)
+        torch.cuda.synchronize()
+        t = tr.cpu().numpy()
+        t0 = t[:, 0].min()
+        spans.append((t[:, 2].max() - t0) / 100.0)
+        ph = (t[:, 3] >> 32)
+        for code, nm in names.items():
+            m = ph == code
+            if not m.any():
+                continue
+            st = (t[m, 0] - t0) / 100.0
+            we = (t[m, 1] - t0) / 100.0
+            en = (t[m, 2] - t0) / 100.0
+            per[nm]["first_start"].append(st.min())
+            per[nm]["med_start"].append(np.median(st))
+            per[nm]["last_end"].append(en.max())
+            per[nm]["med_wait"].append(np.median(we - st))
+            per[nm]["med_dur"].append(np.median(en - st))
+    out = {nm: {key: round(float(np.median(v)), 2) for key, v in d.items() if v}
+           for nm, d in per.items()}
+    return dict(metric="per-phase timeline of the persistent kernel, 8B-shaped, batch 1",
+                unit="us", n_gpus=1, calls=ncalls, k=k, counts=counts,
+                item_span_us=round(float(np.median(spans)), 2), phases=out)
+
+
 def bench_copy(args):
     import torch
     n = 1 << 30
@@ -548,7 +594,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="8b",
-                    choices=["8b", "14b", "70b", "stack8b", "alpha", "copy"])
+                    choices=["8b", "14b", "70b", "stack8b", "alpha", "copy", "timeline"])
     ap.add_argument("--sparsity", type=float, default=0.7)
     ap.add_argument("--ring", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -556,8 +602,6 @@ def main():
     ap.add_argument("--batch-gemv", choices=["valu", "mfma"], default="valu",
                     help="form of the batched up/gate step the layers are prepared with")
     args = ap.parse_args()
-    # read by the library when a layer is prepared
-    os.environ["PROX_BATCH_GEMV"] = args.batch_gemv
     if args.gpus != 1:
         print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the library "
               "runs one layer on one GPU; splitting a layer over GPUs is not implemented)",
@@ -575,6 +619,8 @@ def main():
         res = bench_stack(args)
     elif args.workload == "alpha":
         res = bench_alpha(args)
+    elif args.workload == "timeline":
+        res = bench_timeline(args)
     else:
         res = bench_copy(args)
     print(json.dumps(res), flush=True)

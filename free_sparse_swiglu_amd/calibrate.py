@@ -29,24 +29,29 @@ import torch
 from . import costmodel, prox, synth
 
 
+def calibrate_layer(L, r, quantile: float, k: int, eps: float = 1e-5, return_input=False):
+    """One step of the sequential calibration (top-k Stage 2 mask): tau_x of
+    layer L is the `quantile` of the pooled |x| of the calibration tokens'
+    inputs x = cast(RMSNorm(r)); then the tokens pass the layer with it
+    (r += y, in place).  r: float32 [N][d_model] residual-stream tokens."""
+    N = r.shape[0]
+    mb = L.shape.max_batch
+    x = torch.empty(r.shape, dtype=L.dtype, device=r.device)
+    for c in range(0, N, mb):
+        prox.prox_rmsnorm(L, r[c:c + mb], eps, x[c:c + mb])
+    tau = synth.calibrate_tau(x, quantile)
+    for c in range(0, N, mb):
+        prox.prox_stack_forward([L], [tau], k, r[c:c + mb], eps)
+    return (tau, x) if return_input else tau
+
+
 def sequential_thresholds(layers, calib_resid, quantile: float, k: int, eps: float = 1e-5):
     """Thresholds tau_x for each layer of a stack.
 
     calib_resid: float32 [N][d_model] residual-stream calibration tokens (not
     modified).  Returns a list of floats, one per layer."""
     r = calib_resid.detach().clone().contiguous()
-    N = r.shape[0]
-    mb = min(layer.shape.max_batch for layer in layers)
-    taus = []
-    for L in layers:
-        x = torch.empty(r.shape, dtype=L.dtype, device=r.device)
-        for c in range(0, N, mb):
-            prox.prox_rmsnorm(L, r[c:c + mb], eps, x[c:c + mb])
-        tau = synth.calibrate_tau(x, quantile)
-        taus.append(tau)
-        for c in range(0, N, mb):
-            prox.prox_stack_forward([L], [tau], k, r[c:c + mb], eps)
-    return taus
+    return [calibrate_layer(L, r, quantile, k, eps) for L in layers]
 
 
 def _abs_proxy_state(L, x_row, tau_x, s_abs, y):
@@ -57,33 +62,40 @@ def _abs_proxy_state(L, x_row, tau_x, s_abs, y):
         ctypes.byref(dbg), prox._stream()))
 
 
+def calibrate_layer_ts(L, r, s1: float, s2: float, eps: float = 1e-5, return_input=False):
+    """One step of Algorithm 1 (App. A.7) with both thresholds: x_l =
+    cast(RMSNorm(r)) of every token; tau_x,l = the s1 quantile of the pooled
+    |x_l|; |s~_l| of every token under that input mask (INT4 proxy); tau_s,l =
+    the s2 quantile of the pooled |s~_l|; then every token passes layer l with
+    both thresholds (r += y, in place).  Returns (tau_x, tau_s)."""
+    N = r.shape[0]
+    mb = L.shape.max_batch
+    x = torch.empty(r.shape, dtype=L.dtype, device=r.device)
+    for c in range(0, N, mb):
+        prox.prox_rmsnorm(L, r[c:c + mb], eps, x[c:c + mb])
+    tx = synth.calibrate_tau(x, s1)
+    S = torch.empty(N, L.d_ff, dtype=torch.float32, device=r.device)
+    y = torch.empty(1, L.d_model, dtype=L.dtype, device=r.device)
+    for t in range(N):
+        _abs_proxy_state(L, x[t:t + 1], tx, S[t], y)
+    ts = synth.calibrate_tau(S, s2)
+    for t in range(N):
+        prox.prox_stack_forward_ts([L], [tx], [ts], r[t], eps)
+    return (tx, ts, x) if return_input else (tx, ts)
+
+
 def sequential_thresholds_ts(layers, calib_resid, s1: float, s2: float, eps: float = 1e-5,
                              return_inputs: bool = False):
-    """Algorithm 1 of App. A.7 with both thresholds.
+    """Algorithm 1 of App. A.7 with both thresholds, layer by layer in depth
+    order (calibrate_layer_ts).
 
     calib_resid: float32 [N][d_model] residual-stream calibration tokens (not
-    modified).  For each layer in depth order: x_l = cast(RMSNorm(r)) of every
-    token; tau_x,l = the s1 quantile of the pooled |x_l|; |s~_l| of every token
-    under that input mask (INT4 proxy); tau_s,l = the s2 quantile of the
-    pooled |s~_l|; then every token passes layer l with both thresholds
-    (r += y).  Returns (taus_x, taus_s) or, with return_inputs, also the list
+    modified).  Returns (taus_x, taus_s) or, with return_inputs, also the list
     of per-layer inputs x_l [N][d_model]."""
     r = calib_resid.detach().clone().contiguous()
-    N = r.shape[0]
-    mb = min(layer.shape.max_batch for layer in layers)
     taus_x, taus_s, inputs = [], [], []
     for L in layers:
-        x = torch.empty(r.shape, dtype=L.dtype, device=r.device)
-        for c in range(0, N, mb):
-            prox.prox_rmsnorm(L, r[c:c + mb], eps, x[c:c + mb])
-        tx = synth.calibrate_tau(x, s1)
-        S = torch.empty(N, L.d_ff, dtype=torch.float32, device=r.device)
-        y = torch.empty(1, L.d_model, dtype=L.dtype, device=r.device)
-        for t in range(N):
-            _abs_proxy_state(L, x[t:t + 1], tx, S[t], y)
-        ts = synth.calibrate_tau(S, s2)
-        for t in range(N):
-            prox.prox_stack_forward_ts([L], [tx], [ts], r[t], eps)
+        tx, ts, x = calibrate_layer_ts(L, r, s1, s2, eps, return_input=True)
         taus_x.append(tx)
         taus_s.append(ts)
         if return_inputs:

@@ -54,6 +54,11 @@ prox_status check_shape(const prox_shape *sh) {
     return fail(PROX_EINVAL, "unknown dtype %d", sh->dtype);
   if (sh->activation != PROX_ACT_SILU && sh->activation != PROX_ACT_GELU_TANH)
     return fail(PROX_EINVAL, "unknown activation %d", sh->activation);
+  if (sh->path != PROX_PATH_PERSISTENT && sh->path != PROX_PATH_MULTI)
+    return fail(PROX_EINVAL, "unknown path %d", sh->path);
+  for (int f : {sh->batch_stage1, sh->batch_upgate})
+    if (f != PROX_FORM_AUTO && f != PROX_FORM_VALU && f != PROX_FORM_MFMA)
+      return fail(PROX_EINVAL, "unknown batch form %d", f);
   if (sh->d_model % sh->group_size != 0)
     return fail(PROX_EINVAL, "d_model (%d) is not a multiple of group_size (%d)",
                 sh->d_model, sh->group_size);
@@ -72,6 +77,12 @@ prox_status check_shape(const prox_shape *sh) {
   if (sh->max_batch > prox::kMaxBatch)
     return fail(PROX_EUNSUPPORTED, "max_batch above %d is not supported (got %d)",
                 prox::kMaxBatch, sh->max_batch);
+  if (sh->batch_upgate == PROX_FORM_MFMA && sh->dtype != PROX_BF16)
+    return fail(PROX_EUNSUPPORTED, "the matrix-core up/gate form needs bf16 weights");
+  if (sh->batch_stage1 == PROX_FORM_MFMA &&
+      (sh->dtype != PROX_BF16 || sh->group_size % 64 != 0 || sh->max_batch < 2))
+    return fail(PROX_EUNSUPPORTED,
+                "the matrix-core Stage 1 needs bf16 weights, G a multiple of 64 and max_batch >= 2");
   // Byte offsets inside the weight buffers are 32-bit.
   const size_t esz = sh->dtype == PROX_BF16 ? 2 : 4;
   if ((size_t)sh->d_ff * 2 * sh->d_model * esz >= (1ull << 32))
@@ -79,11 +90,21 @@ prox_status check_shape(const prox_shape *sh) {
   return PROX_OK;
 }
 
+prox::Plan plan_of(const prox_shape *sh) {
+  prox::PlanChoice ch;
+  ch.path = sh->path;
+  ch.batch_stage1 = sh->batch_stage1;
+  ch.batch_upgate = sh->batch_upgate;
+  return prox::make_plan(sh->d_model, sh->d_ff, sh->group_size, sh->dtype == PROX_BF16,
+                         sh->max_batch, sh->activation, ch);
+}
+
 }  // namespace
 
 namespace prox {
 
-Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act) {
+Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act,
+               const PlanChoice &ch) {
   Plan p{};
   p.act = act;
   p.d_model = d_model;
@@ -101,14 +122,28 @@ Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act) {
   if (nrc > 64) nrc = 64;
   p.nrc = nrc;
   p.upgate_cap = 4096;
-  const char *path = getenv("PROX_PATH");
-  p.use_fused = fused_supported(p) && !(path && strcmp(path, "multi") == 0);
-  const char *bg = getenv("PROX_BATCH_GEMV");
-  p.batch_mfma = bg && strcmp(bg, "mfma") == 0;
-  const char *bp = getenv("PROX_BATCH_PROXY");
-  p.proxy_mfma = bf16 && max_batch >= 2 && G % 64 == 0 && d_model % 32 == 0 &&
-                 !(bp && strcmp(bp, "valu") == 0);
+  p.use_fused = fused_supported(p) && ch.path == PROX_PATH_PERSISTENT;
+  p.batch_mfma = ch.batch_upgate == PROX_FORM_MFMA;
+  // Stage 1 on the matrix cores: forced (from 2 tokens), or automatically
+  // from 3 tokens (measured faster there; at 2 the VALU kernel reads only
+  // the rows the union of the input masks keeps).
+  const bool mfma_ok = bf16 && G % 64 == 0 && d_model % 32 == 0;
+  if (ch.batch_stage1 == PROX_FORM_MFMA && mfma_ok && max_batch >= 2)
+    p.proxy_mfma = 2;
+  else if (ch.batch_stage1 == PROX_FORM_AUTO && mfma_ok && max_batch >= 3)
+    p.proxy_mfma = 3;
+  else
+    p.proxy_mfma = 0;
+  p.wait_limit = kDefaultWaitLimit;
   return p;
+}
+
+size_t sync_block_bytes() {
+  size_t o = align256(fused_sync_words() * sizeof(unsigned));
+  o = align256(o + (size_t)(kMaxDff / kTile) * sizeof(unsigned));
+  o = align256(o + (size_t)(kMaxDmodel / kDownCols) * sizeof(unsigned));
+  o = align256(o + sizeof(unsigned));
+  return o;
 }
 
 Layout make_layout(const Plan &p) {
@@ -122,9 +157,15 @@ Layout make_layout(const Plan &p) {
   L.o_pred = align256(L.o_psc + (size_t)p.ntile * p.ngroups * 512 * sizeof(float));
   L.o_pq2 = L.o_pred + 256;
   L.proxy = L.o_pq2 + (p.proxy_mfma ? align256(pq) : 0);
+  // The synchronisation block (fixed size, see sync_block_bytes).
   size_t o = 0;
+  L.o_sync = o;      o = align256(o + fused_sync_words() * sizeof(unsigned));
+  L.o_tile_cnt = o;  o = align256(o + (size_t)(kMaxDff / kTile) * sizeof(unsigned));
+  L.o_col_cnt = o;   o = align256(o + (size_t)(kMaxDmodel / kDownCols) * sizeof(unsigned));
+  L.o_ucnt = o;      o = align256(o + sizeof(unsigned));
+  L.hdr = o;
+  // Per-call scratch.
   L.o_part = o;      o = align256(o + (size_t)p.ntile * p.nchunk * B * 512 * sizeof(float));
-  L.o_tile_cnt = o;  o = align256(o + (size_t)p.ntile * sizeof(unsigned));
   L.o_sabs = o;      o = align256(o + B * p.d_ff * sizeof(float));
   L.o_sel = o;       o = align256(o + B * p.d_ff * sizeof(int));
   L.o_selw = o;      o = align256(o + B * ((p.d_ff + 31) / 32) * sizeof(unsigned));
@@ -134,11 +175,10 @@ Layout make_layout(const Plan &p) {
   L.o_umask = o;     o = align256(o + (size_t)p.d_ff);
   const size_t yrows = std::max((size_t)p.nrc * B, (size_t)fused_ypart_rows(p));
   L.o_ypart = o;     o = align256(o + yrows * p.d_model * sizeof(float));
-  L.o_col_cnt = o;   o = align256(o + (size_t)p.ncol * sizeof(unsigned));
-  L.o_ucnt = o;      o = align256(o + sizeof(unsigned));
-  L.o_sync = o;      o = align256(o + fused_sync_words(p) * sizeof(unsigned));
   L.o_xbuf = o;      o = align256(o + B * p.d_model * p.esz);
   L.o_ybuf = o;      o = align256(o + B * p.d_model * p.esz);
+  L.o_drows = o;     o = align256(o + B * p.d_model * sizeof(int));
+  L.o_dcnt = o;      o = align256(o + B * (p.d_model / 64) * sizeof(int));
   L.workspace = o;
   return L;
 }
@@ -160,10 +200,13 @@ struct EventLog {
   }
 };
 
-// Stage 1, top-k and Stage 2 for `batch` tokens; writes y.
+// Stage 1, top-k and Stage 2 for `batch` tokens; writes y.  lists: the
+// top-k kernel also writes the per-token lists (batch > 1); dbg: the Stage 1
+// kernel writes its survivor lists (b.drows / b.dcnt), and with k = 0 (no
+// kernel on the path) Stage 1 runs alone to give them.
 prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau,
                         int k, void *y, float *resid, hipStream_t s,
-                        EventLog *log = nullptr, bool lists = false) {
+                        EventLog *log = nullptr, bool lists = false, bool dbg = false) {
   const prox::Plan &p = L->plan;
   const prox::Bufs &b = L->bufs;
   EventLog none{nullptr, 0, 0};
@@ -171,18 +214,22 @@ prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau
   hipError_t e;
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   if (k == 0) {
+    if (dbg && (e = prox::launch_proxy(p, b, x, batch, tau, s, true)) != hipSuccess)
+      return hip_fail(e, "stage 1 proxy kernel");
     e = prox::launch_zero_y(p, y, batch, s);
     if (e != hipSuccess) return hip_fail(e, "zero output");
     if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
     return PROX_OK;  // y = 0 adds nothing to the residual
   }
   if (batch == 1 && p.use_fused) {
-    if ((e = prox::launch_fused(p, b, x, tau, k, y, resid, s)) != hipSuccess)
+    prox::FusedOpts o;
+    o.dbg = dbg;
+    if ((e = prox::launch_fused(p, b, x, tau, k, y, resid, s, o)) != hipSuccess)
       return hip_fail(e, "fused kernel");
     if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
     return PROX_OK;
   }
-  if ((e = prox::launch_proxy(p, b, x, batch, tau, s)) != hipSuccess)
+  if ((e = prox::launch_proxy(p, b, x, batch, tau, s, dbg)) != hipSuccess)
     return hip_fail(e, "stage 1 proxy kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
   // Several tokens: Stage 2 runs over the union, built from mask words, so
@@ -239,6 +286,8 @@ extern "C" {
 
 const char *prox_last_error(void) { return g_err.c_str(); }
 
+size_t prox_sync_block_bytes(void) { return prox::sync_block_bytes(); }
+
 prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
                              size_t *proxy_bytes, size_t *workspace_bytes) {
   g_err.clear();
@@ -246,9 +295,7 @@ prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
   if (st != PROX_OK) return st;
   if (!weights_bytes || !proxy_bytes || !workspace_bytes)
     return fail(PROX_EINVAL, "output size pointers must be non-NULL");
-  const prox::Plan p = prox::make_plan(shape->d_model, shape->d_ff, shape->group_size,
-                                       shape->dtype == PROX_BF16, shape->max_batch,
-                                       shape->activation);
+  const prox::Plan p = plan_of(shape);
   const prox::Layout L = prox::make_layout(p);
   *weights_bytes = L.weights;
   *proxy_bytes = L.proxy;
@@ -275,8 +322,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
     return fail(PROX_EINVAL, "source weights must be aligned to their element size");
   prox_layer *L = new (std::nothrow) prox_layer;
   if (!L) return fail(PROX_EINVAL, "out of host memory");
-  L->plan = prox::make_plan(shape->d_model, shape->d_ff, shape->group_size,
-                            shape->dtype == PROX_BF16, shape->max_batch, shape->activation);
+  L->plan = plan_of(shape);
   const prox::Layout lay = prox::make_layout(L->plan);
   char *wb = (char *)weights_buf, *pb = (char *)proxy_buf, *ws = (char *)workspace_buf;
   prox::Bufs &b = L->bufs;
@@ -288,6 +334,8 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.pq2 = L->plan.proxy_mfma ? (unsigned *)(pb + lay.o_pq2) : nullptr;
   b.part = (float *)(ws + lay.o_part);
   b.tile_cnt = (unsigned *)(ws + lay.o_tile_cnt);
+  b.drows = (int *)(ws + lay.o_drows);
+  b.dcnt = (int *)(ws + lay.o_dcnt);
   b.sabs = (float *)(ws + lay.o_sabs);
   b.sel = (int *)(ws + lay.o_sel);
   b.selw = (unsigned *)(ws + lay.o_selw);
@@ -302,9 +350,9 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.xbuf = ws + lay.o_xbuf;
   b.ybuf = ws + lay.o_ybuf;
   hipError_t e = prox::launch_prepare(L->plan, b, w_up, w_gate, w_down, (hipStream_t)stream);
-  if (e == hipSuccess)
-    e = hipMemsetAsync(b.sync, 0, prox::fused_sync_words(L->plan) * sizeof(unsigned),
-                       (hipStream_t)stream);
+  // the synchronisation block (tickets, flags, counters, status) and the
+  // layer's cut guess start at zero
+  if (e == hipSuccess) e = hipMemsetAsync(ws, 0, lay.hdr, (hipStream_t)stream);
   if (e == hipSuccess) e = hipMemsetAsync(b.pred, 0, sizeof(unsigned), (hipStream_t)stream);
   if (e != hipSuccess) {
     delete L;
@@ -348,6 +396,8 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
   prox_status st = check_forward_args(layer, x, batch, threshold, k, y);
   if (st != PROX_OK) return st;
   if (!dbg) return fail(PROX_EINVAL, "dbg is NULL");
+  if ((dbg->n1 != nullptr) != (dbg->idx != nullptr))
+    return fail(PROX_EINVAL, "n1 and idx must be given together");
   hipStream_t s = (hipStream_t)stream;
   const prox::Plan &p = layer->plan;
   const prox::Bufs &b = layer->bufs;
@@ -355,17 +405,16 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
   if (dbg->status &&
       (e = hipMemsetAsync(b.sync + prox::kFusedErrWord, 0, sizeof(unsigned), s)) != hipSuccess)
     return hip_fail(e, "clear status");
-  st = run_forward(layer, x, batch, threshold, k, y, nullptr, s, nullptr, true);
+  const bool surv = dbg->idx != nullptr;
+  st = run_forward(layer, x, batch, threshold, k, y, nullptr, s, nullptr, true, surv);
   if (st != PROX_OK) return st;
   if (dbg->status &&
       (e = hipMemcpyAsync(dbg->status, b.sync + prox::kFusedErrWord, sizeof(unsigned),
                           hipMemcpyDeviceToDevice, s)) != hipSuccess)
     return hip_fail(e, "copy status");
-  if (dbg->n1 || dbg->idx) {
-    if (!dbg->n1 || !dbg->idx) return fail(PROX_EINVAL, "n1 and idx must be given together");
-    e = prox::launch_compact_debug(p, x, batch, threshold, dbg->n1, dbg->idx, s);
-    if (e != hipSuccess) return hip_fail(e, "compaction debug kernel");
-  }
+  // the survivors as the Stage 1 kernel itself decided them
+  if (surv && (e = prox::launch_survivors(p, b, batch, dbg->n1, dbg->idx, s)) != hipSuccess)
+    return hip_fail(e, "survivor list kernel");
   const size_t nf = (size_t)batch * p.d_ff;
   if (k > 0) {
     if (dbg->s_abs &&
@@ -406,6 +455,23 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
   return PROX_OK;
 }
 
+prox_status prox_read_status(const prox_layer *layer, int32_t *status, void *stream) {
+  g_err.clear();
+  if (!layer || !status) return fail(PROX_EINVAL, "layer and status are required");
+  if (!aligned(status, 4)) return fail(PROX_EINVAL, "status must be 4-byte aligned");
+  hipError_t e = prox::launch_read_status(layer->plan, layer->bufs, (int *)status,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "status kernel");
+  return PROX_OK;
+}
+
+prox_status prox_set_wait_limit(prox_layer *layer, uint32_t polls) {
+  g_err.clear();
+  if (!layer) return fail(PROX_EINVAL, "layer is NULL");
+  layer->plan.wait_limit = polls;
+  return PROX_OK;
+}
+
 static prox_status check_ts_args(const prox_layer *layer, const void *x, float threshold_x,
                                  float threshold_s, const void *y) {
   prox_status st = check_forward_args(layer, x, 1, threshold_x, 0, y);
@@ -414,7 +480,7 @@ static prox_status check_ts_args(const prox_layer *layer, const void *x, float t
   if (!layer->plan.use_fused)
     return fail(PROX_EUNSUPPORTED,
                 "the Stage 2 threshold mask runs on the persistent kernel only (layer prepared "
-                "with PROX_PATH=multi)");
+                "with path = PROX_PATH_MULTI)");
   return PROX_OK;
 }
 
@@ -423,8 +489,11 @@ prox_status prox_ffn_forward_ts(const prox_layer *layer, const void *x, float th
   g_err.clear();
   prox_status st = check_ts_args(layer, x, threshold_x, threshold_s, y);
   if (st != PROX_OK) return st;
+  prox::FusedOpts o;
+  o.ts_mode = true;
+  o.tau_s = threshold_s;
   hipError_t e = prox::launch_fused(layer->plan, layer->bufs, x, threshold_x, 0, y, nullptr,
-                                    (hipStream_t)stream, nullptr, true, threshold_s);
+                                    (hipStream_t)stream, o);
   if (e != hipSuccess) return hip_fail(e, "fused kernel");
   return PROX_OK;
 }
@@ -436,6 +505,8 @@ prox_status prox_ffn_forward_ts_debug(const prox_layer *layer, const void *x, fl
   prox_status st = check_ts_args(layer, x, threshold_x, threshold_s, y);
   if (st != PROX_OK) return st;
   if (!dbg) return fail(PROX_EINVAL, "dbg is NULL");
+  if ((dbg->n1 != nullptr) != (dbg->idx != nullptr))
+    return fail(PROX_EINVAL, "n1 and idx must be given together");
   hipStream_t s = (hipStream_t)stream;
   const prox::Plan &p = layer->plan;
   const prox::Bufs &b = layer->bufs;
@@ -443,18 +514,19 @@ prox_status prox_ffn_forward_ts_debug(const prox_layer *layer, const void *x, fl
   if (dbg->status &&
       (e = hipMemsetAsync(b.sync + prox::kFusedErrWord, 0, sizeof(unsigned), s)) != hipSuccess)
     return hip_fail(e, "clear status");
-  if ((e = prox::launch_fused(p, b, x, threshold_x, 0, y, nullptr, s, nullptr, true,
-                              threshold_s)) != hipSuccess)
+  prox::FusedOpts o;
+  o.ts_mode = true;
+  o.tau_s = threshold_s;
+  o.dbg = dbg->idx != nullptr;
+  if ((e = prox::launch_fused(p, b, x, threshold_x, 0, y, nullptr, s, o)) != hipSuccess)
     return hip_fail(e, "fused kernel");
   if (dbg->status &&
       (e = hipMemcpyAsync(dbg->status, b.sync + prox::kFusedErrWord, sizeof(unsigned),
                           hipMemcpyDeviceToDevice, s)) != hipSuccess)
     return hip_fail(e, "copy status");
-  if (dbg->n1 || dbg->idx) {
-    if (!dbg->n1 || !dbg->idx) return fail(PROX_EINVAL, "n1 and idx must be given together");
-    e = prox::launch_compact_debug(p, x, 1, threshold_x, dbg->n1, dbg->idx, s);
-    if (e != hipSuccess) return hip_fail(e, "compaction debug kernel");
-  }
+  // the survivors as the persistent kernel's Stage 1 items decided them
+  if (dbg->idx && (e = prox::launch_survivors(p, b, 1, dbg->n1, dbg->idx, s)) != hipSuccess)
+    return hip_fail(e, "survivor list kernel");
   if (dbg->s_abs && (e = hipMemcpyAsync(dbg->s_abs, b.sabs, (size_t)p.d_ff * 4,
                                         hipMemcpyDeviceToDevice, s)) != hipSuccess)
     return hip_fail(e, "copy |s~|");
@@ -542,12 +614,12 @@ prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
     if (batch == 1 && k > 0 && L->plan.use_fused && prox::fused_norm_supported(L->plan)) {
       // one launch per layer: the persistent kernel forms x = RMSNorm(r)
       // itself, then adds y to r
-      prox::FusedNorm nm;
-      nm.r = resid;
-      nm.eps = eps;
-      nm.xout = L->bufs.xbuf;
+      prox::FusedOpts o;
+      o.norm_r = resid;
+      o.eps = eps;
+      o.xout = L->bufs.xbuf;
       e = prox::launch_fused(L->plan, L->bufs, L->bufs.xbuf, thresholds[l], k, L->bufs.ybuf,
-                             resid, s, nullptr, false, 0.0f, nm);
+                             resid, s, o);
       if (e != hipSuccess) return hip_fail(e, "fused kernel");
       continue;
     }
@@ -576,7 +648,7 @@ prox_status prox_stack_forward_ts(const prox_layer *const *layers, int n_layers,
     if (L->plan.d_model != p0.d_model || L->plan.bf16 != p0.bf16)
       return fail(PROX_EINVAL, "layer %d has a different d_model or dtype", l);
     if (!L->plan.use_fused)
-      return fail(PROX_EUNSUPPORTED, "layer %d was prepared with PROX_PATH=multi", l);
+      return fail(PROX_EUNSUPPORTED, "layer %d was prepared with path = PROX_PATH_MULTI", l);
     if (isnan(thresholds_x[l]) || isnan(thresholds_s[l]))
       return fail(PROX_EINVAL, "threshold of layer %d is NaN", l);
   }
@@ -584,17 +656,19 @@ prox_status prox_stack_forward_ts(const prox_layer *const *layers, int n_layers,
   for (int l = 0; l < n_layers; ++l) {
     const prox_layer *L = layers[l];
     hipError_t e;
-    prox::FusedNorm nm;
+    prox::FusedOpts o;
+    o.ts_mode = true;
+    o.tau_s = thresholds_s[l];
     if (prox::fused_norm_supported(L->plan)) {
-      nm.r = resid;  // x = RMSNorm(r) formed inside the one launch
-      nm.eps = eps;
-      nm.xout = L->bufs.xbuf;
+      o.norm_r = resid;  // x = RMSNorm(r) formed inside the one launch
+      o.eps = eps;
+      o.xout = L->bufs.xbuf;
     } else if ((e = prox::launch_rmsnorm(L->plan, resid, 1, eps, L->bufs.xbuf, s)) !=
                hipSuccess) {
       return hip_fail(e, "rmsnorm kernel");
     }
     e = prox::launch_fused(L->plan, L->bufs, L->bufs.xbuf, thresholds_x[l], 0, L->bufs.ybuf, resid,
-                           s, nullptr, true, thresholds_s[l], nm);
+                           s, o);
     if (e != hipSuccess) return hip_fail(e, "fused kernel");
   }
   return PROX_OK;
@@ -635,8 +709,10 @@ prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x, floa
   if (trace_items < total)
     return fail(PROX_EINVAL, "trace holds %d items, the launch has %d", trace_items, total);
   if (!aligned(trace, 16)) return fail(PROX_EINVAL, "trace must be 16-byte aligned");
+  prox::FusedOpts o;
+  o.trace = trace;
   hipError_t e = prox::launch_fused(p, layer->bufs, x, threshold, k, y, nullptr,
-                                    (hipStream_t)stream, trace);
+                                    (hipStream_t)stream, o);
   if (e != hipSuccess) return hip_fail(e, "fused kernel");
   return PROX_OK;
 }

@@ -219,6 +219,19 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned *wsum,
   return off + inc - v;
 }
 
+// Debug export of the survivors a Stage 1 kernel found in one 64-row slice
+// (its m_x decision, Sec. 4.1): rows[sl * 64 + i] = the i-th surviving row,
+// cnt[sl] = their number.  Called by every lane of the wave with the slice's
+// ballot m.
+__device__ __forceinline__ void export_slice(int *rows, int *cnt, int sl, uint64_t m) {
+  const int lane = threadIdx.x & 63;
+  if ((m >> lane) & 1ull)
+    rows[sl * 64 + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u))] =
+        sl * 64 + lane;
+  if (lane == 0) cnt[sl] = (int)__popcll(m);
+}
+
 // Stage 1 input mask for one 64-row slice (Sec. 4.1, m_x equation): each lane
 // tests its own row, |x_i| >= tau keeps it; the wave gets the 64-bit mask.
 // Shared by the proxy kernel and the compaction debug kernel, so the
@@ -258,14 +271,15 @@ __device__ __forceinline__ unsigned xload_u(const unsigned *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until *p >= target, polling with short sleeps.  Bounded: after about
-// 2^22 polls (seconds) it sets bit 0 of *err and returns, so a kernel always
-// terminates even if a producer never signals.
-__device__ __forceinline__ void wait_geq(const unsigned *p, unsigned target, unsigned *err) {
+// Wait until *p >= target, polling with short sleeps.  Bounded: after
+// `limit` polls (the default, 2^22, is seconds) it sets bit 0 of *err and
+// returns, so a kernel always terminates even if a producer never signals.
+__device__ __forceinline__ void wait_geq(const unsigned *p, unsigned target, unsigned *err,
+                                         unsigned limit) {
   unsigned n = 0;
   while (xload_u(p) < target) {
     __builtin_amdgcn_s_sleep(1);
-    if (++n > (1u << 22)) {
+    if (++n > limit) {
       atomicOr(err, 1u);
       return;
     }

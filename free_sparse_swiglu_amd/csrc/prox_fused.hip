@@ -104,6 +104,8 @@ struct FusedArgs {
   float tau_s;
   int n_p1, n_p2, n_p3, n_p4;
   unsigned long long *trace;  // optional per-ticket timeline (nullptr: off)
+  unsigned wlim;    // polls before a bounded wait gives up
+  int *drows, *dcnt;  // debug: Stage 1 survivors per 64-row slice (nullptr: off)
 };
 
 // The select's result: T and J + 1 as one agent-coherent 64-bit word (J + 1
@@ -113,13 +115,14 @@ __device__ __forceinline__ void xstore_tj(unsigned *w, unsigned T, int J) {
   __hip_atomic_store((unsigned long long *)w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Bounded wait for it (like wait_geq): *T, *J receive the values.
-__device__ __forceinline__ void wait_tj(const unsigned *w, unsigned *err, unsigned *T, unsigned *J) {
+__device__ __forceinline__ void wait_tj(const unsigned *w, unsigned *err, unsigned *T, unsigned *J,
+                                        unsigned limit) {
   unsigned n = 0;
   unsigned long long v;
   while (((v = __hip_atomic_load((const unsigned long long *)w, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT)) >> 32) == 0ull) {
     __builtin_amdgcn_s_sleep(1);
-    if (++n > (1u << 22)) {
+    if (++n > limit) {
       atomicOr(err, 1u);
       break;
     }
@@ -131,11 +134,11 @@ __device__ __forceinline__ void wait_tj(const unsigned *w, unsigned *err, unsign
 
 // Bounded wait of a whole wave until every lane's flag is >= 1 (lanes with
 // nothing to wait for pass their own satisfied flag).
-__device__ __forceinline__ void wave_wait_flags(const unsigned *f, unsigned *err) {
+__device__ __forceinline__ void wave_wait_flags(const unsigned *f, unsigned *err, unsigned limit) {
   unsigned n = 0;
   while (!__all(xload_u(f) >= 1u)) {
     __builtin_amdgcn_s_sleep(1);
-    if (++n > (1u << 22)) {
+    if (++n > limit) {
       if ((threadIdx.x & 63) == 0) atomicOr(err, 1u);
       break;
     }
@@ -257,6 +260,7 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
     } else {
       un = slice_mask<BF16>(a.x, (size_t)sl * 64, a.tau, xl);
     }
+    if (a.drows && t == 0) export_slice(a.drows, a.dcnt, sl, un);
     const float xm = ((un >> lane) & 1ull) ? xl : 0.0f;
     const float xsum = wave_sum(xm);
     const int cnt = (int)__popcll(un);
@@ -474,7 +478,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
       const int tm = min(2 * m + (wu >> 2), a.ntile - 1);
       // Poll only while this slot's tile is not known to be done (a poll
       // waits for this wave's earlier copies too).
-      while (!((done >> tm) & 1ull) && spins <= (1u << 22)) {
+      while (!((done >> tm) & 1ull) && spins <= a.wlim) {
         const uint64_t b = __ballot(xload_u(fl) >= 1u);
         // scalar (no VGPR to wait on); readfirstlane returns int: widen unsigned
         done = ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
@@ -492,7 +496,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
     // wave polls on until it has seen all of them and copies its share of
     // the bins (four blocks of 64) into LDS, without waiting for the others.
     const uint64_t all = a.ntile == 64 ? ~0ull : (1ull << a.ntile) - 1ull;
-    while ((done & all) != all && spins <= (1u << 22)) {
+    while ((done & all) != all && spins <= a.wlim) {
       const uint64_t b = __ballot(xload_u(fl) >= 1u);
       done = ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
              (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
@@ -501,7 +505,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
         spins = __builtin_amdgcn_readfirstlane(spins + 1u);
       }
     }
-    if (spins > (1u << 22) && lane == 0) atomicOr(&a.sync[kSyncErr], 1u);
+    if (spins > a.wlim && lane == 0) atomicOr(&a.sync[kSyncErr], 1u);
     const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.ghist, 2048u * 4u);
 #pragma unroll
     for (int q = 0; q < 2048 / kFT; ++q)
@@ -509,7 +513,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
           rh, (__attribute__((address_space(3))) void *)&sm.h[q * kFT + wu * 64], 4, koff,
           (uint32_t)(q * kFT) * 4u, 0, kSelBits);
   } else if (threadIdx.x == 0) {
-    wait_geq(&a.sync[kSyncTiles], (unsigned)a.ntile, &a.sync[kSyncErr]);
+    wait_geq(&a.sync[kSyncTiles], (unsigned)a.ntile, &a.sync[kSyncErr], a.wlim);
   }
   if (threadIdx.x == 0) stamp_wait<SEL>(a);
   __syncthreads();
@@ -797,7 +801,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
       }
       unsigned ib = xload_u(&a.sync[kSyncInv]);
       if (__syncthreads_or(ib == 0u)) {
-        if (threadIdx.x == 0) wait_geq(&a.sync[kSyncInv], 1u, &a.sync[kSyncErr]);
+        if (threadIdx.x == 0) wait_geq(&a.sync[kSyncInv], 1u, &a.sync[kSyncErr], a.wlim);
         __syncthreads();
         ib = xload_u(&a.sync[kSyncInv]);
       }
@@ -837,10 +841,10 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
     unsigned lo = 0u;
     const unsigned pb = a.ts_mode ? 0u : xload_u(a.pred);
     if (a.ts_mode || pb >= 2u) {
-      wait_geq(&a.tflag[(c0 / kTile) * kSyncStride], 1u, &a.sync[kSyncErr]);
+      wait_geq(&a.tflag[(c0 / kTile) * kSyncStride], 1u, &a.sync[kSyncErr], a.wlim);
       lo = pb >= 2u ? pb - 1u : 0u;
     } else {
-      wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
+      wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr], a.wlim);
       lo = xload_u(&a.sync[kSyncBin]) - 1u;
     }
     sm.lo = lo;
@@ -869,7 +873,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
       // and J (digit 1 = b*, computed before T is known so nothing here
       // waits for the select)
       if (threadIdx.x == 0) {
-        wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
+        wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr], a.wlim);
         sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
       }
       __syncthreads();
@@ -936,10 +940,10 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
     if (tid < 64) {
       constexpr int TPR = kP4Ch / kTile;  // tiles per range
       const int t0 = r * TPR, t1 = min(a.ntile, t0 + TPR) - 1;
-      wave_wait_flags(&a.tflag[min(t0 + lane, t1) * kSyncStride], &a.sync[kSyncErr]);
+      wave_wait_flags(&a.tflag[min(t0 + lane, t1) * kSyncStride], &a.sync[kSyncErr], a.wlim);
     }
   } else if (tid == 0) {
-    wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr]);
+    wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr], a.wlim);
     sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
   }
   __syncthreads();
@@ -1003,7 +1007,7 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   }
   if (tid < 64) {
     const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
-    wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride], &a.sync[kSyncErr]);
+    wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride], &a.sync[kSyncErr], a.wlim);
     if (lane == 0) stamp_wait<SEL>(a);
   }
   __syncthreads();
@@ -1013,7 +1017,7 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   {
     const float sj = tid < nr ? xload(&a.sdense[sm.rs[tid]]) : 0.0f;
     if (!a.ts_mode) {
-      if (tid == 0) wait_tj(&a.sync[kSyncSelect], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1]);
+      if (tid == 0) wait_tj(&a.sync[kSyncSelect], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
       __syncthreads();
     }
     const unsigned T = a.ts_mode ? 0u : sm.tj[0];
@@ -1177,9 +1181,10 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   // ticket total + grid - 1 (no second atomic on the way out).
   if ((unsigned)s_ticket == (unsigned)total + gridDim.x - 1u) {
     constexpr int kCtl = kSyncP3 / kSyncStride;  // control words before the P3 flags
-    // control words, P3 flags and tile flags: consecutive lines
-    for (int i = threadIdx.x; i < kCtl + a.n_p3 + a.ntile; i += kFT)
+    // control words and P3 flags (consecutive lines), then the tile flags
+    for (int i = threadIdx.x; i < kCtl + a.n_p3; i += kFT)
       if (i * kSyncStride != kSyncErr) xstore_u(&a.sync[i * kSyncStride], 0u);
+    for (int i = threadIdx.x; i < a.ntile; i += kFT) xstore_u(&a.tflag[i * kSyncStride], 0u);
     if (threadIdx.x == 0) xstore_u(&a.sync[kSyncSelect + 1], 0u);
   }
 }
@@ -1261,15 +1266,14 @@ bool fused_supported(const Plan &p) {
 static int fused_n_p3(const Plan &p) { return (p.d_ff + kP3Ch - 1) / kP3Ch; }
 
 // Sync block: control words, P3 flags, tile flags (one line each), the
-// digit-1 histogram, the P3 masks.
-static size_t fused_tflag_word(const Plan &p) {
-  return (size_t)kSyncP3 + (size_t)fused_n_p3(p) * kSyncStride;
-}
-static size_t fused_hist_word(const Plan &p) {
-  return fused_tflag_word(p) + (size_t)p.ntile * kSyncStride;
-}
+// digit-1 histogram, the P3 masks, each at a fixed word index sized for the
+// largest supported d_ff (so layers of any shapes can share one block).
+constexpr size_t kMaxP3 = kMaxDff / kP3Ch;
+constexpr size_t kTflagWord = (size_t)kSyncP3 + kMaxP3 * kSyncStride;
+constexpr size_t kHistWord = kTflagWord + (size_t)(kMaxDff / kTile) * kSyncStride;
+constexpr size_t kGmaskWord = kHistWord + 2048;
 
-size_t fused_sync_words(const Plan &p) { return fused_hist_word(p) + 2048 + 4 * fused_n_p3(p); }
+size_t fused_sync_words() { return kGmaskWord + 4 * kMaxP3; }
 
 int fused_ypart_rows(const Plan &p) { return (p.d_ff + kP4Ch - 1) / kP4Ch; }
 
@@ -1284,17 +1288,20 @@ bool fused_norm_supported(const Plan &p) {
 }
 
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
-                        float *resid, hipStream_t s, unsigned long long *trace, bool ts_mode,
-                        float tau_s, FusedNorm norm) {
-  if (norm.r && !fused_norm_supported(p)) return hipErrorInvalidValue;
+                        float *resid, hipStream_t s, const FusedOpts &o) {
+  if (o.norm_r && !fused_norm_supported(p)) return hipErrorInvalidValue;
+  const bool ts_mode = o.ts_mode;
   FusedArgs a{};
-  a.rnorm = norm.r;
-  a.eps = norm.eps;
-  a.xout = norm.xout;
-  a.trace = trace;
+  a.rnorm = o.norm_r;
+  a.eps = o.eps;
+  a.xout = o.xout;
+  a.trace = o.trace;
   a.ts_mode = ts_mode ? 1 : 0;
   a.act = p.act;
-  a.tau_s = tau_s;
+  a.tau_s = o.tau_s;
+  a.wlim = p.wait_limit;
+  a.drows = o.dbg ? b.drows : nullptr;
+  a.dcnt = o.dbg ? b.dcnt : nullptr;
   a.pq = b.pq;
   a.psc = b.psc;
   a.wug = b.wug;
@@ -1320,25 +1327,25 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.ypart = b.ypart;
   a.col_cnt = b.col_cnt;
   a.sync = b.sync;
-  a.tflag = b.sync + fused_tflag_word(p);
-  a.ghist = b.sync + fused_hist_word(p);
-  a.gmask = a.ghist + 2048;
+  a.tflag = b.sync + kTflagWord;
+  a.ghist = b.sync + kHistWord;
+  a.gmask = b.sync + kGmaskWord;
   a.pred = b.pred;
   a.n_p1 = p.ntile * p.nchunk;
   a.n_p2 = ts_mode ? 0 : 1;
   a.n_p3 = fused_n_p3(p);
   a.n_p4 = p.ncol * a.nrange;
   if (!ts_mode) {
-    if (norm.r) return p.bf16 ? fused_go<true, true, true>(a, s) : fused_go<false, true, true>(a, s);
+    if (o.norm_r) return p.bf16 ? fused_go<true, true, true>(a, s) : fused_go<false, true, true>(a, s);
     return p.bf16 ? fused_go<true, false, true>(a, s) : fused_go<false, false, true>(a, s);
   }
-  if (norm.r) return p.bf16 ? fused_go<true, true, false>(a, s) : fused_go<false, true, false>(a, s);
+  if (o.norm_r) return p.bf16 ? fused_go<true, true, false>(a, s) : fused_go<false, true, false>(a, s);
   return p.bf16 ? fused_go<true, false, false>(a, s) : fused_go<false, false, false>(a, s);
 }
 
 hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,
                              int *count, hipStream_t s) {
-  const unsigned *gmask = b.sync + fused_hist_word(p) + 2048;
+  const unsigned *gmask = b.sync + kGmaskWord;
   fused_list_kernel<<<1, kFT, 0, s>>>(gmask, b.sync + kSyncSelect, b.sabs, b.ssp, fused_n_p3(p),
                                       p.d_ff, k, sel, ssel, count);
   return hipGetLastError();

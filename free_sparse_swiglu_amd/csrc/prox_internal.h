@@ -54,6 +54,8 @@ struct Bufs {
   unsigned *sync;  // fused kernel: tickets, flags, histogram, masks (fused_sync_words)
   void *xbuf;      // [batch][d_model] dtype         stack: normalized input
   void *ybuf;      // [batch][d_model] dtype         stack: layer output
+  int *drows;      // [batch][d_model]               debug: Stage 1 survivors per 64-row slice
+  int *dcnt;       // [batch][d_model / 64]          debug: their counts
 };
 
 struct Plan {
@@ -68,18 +70,35 @@ struct Plan {
   int use_fused;    // batch-1 forwards run the persistent fused kernel
   int act;          // gate activation: 0 SiLU, 1 GELU (tanh form)
   int batch_mfma;   // bf16 batches of 2..8 tokens: up/gate on MFMA (default: VALU dot2)
-  int proxy_mfma;   // bf16 batches of 2..8 tokens: Stage 1 on MFMA over pq2
+  int proxy_mfma;   // bf16 batches of 3..8 tokens: Stage 1 on MFMA over pq2
+  unsigned wait_limit;  // polls before a bounded wait of the persistent kernel gives up
 };
 
+// Kernel choices of a layer (the prox_shape fields beyond the sizes).
+struct PlanChoice {
+  int path = 0;          // 0 persistent kernel for batch 1, 1 four kernels
+  int batch_stage1 = 0;  // 0 auto, 1 VALU, 2 MFMA
+  int batch_upgate = 0;  // 0 auto (VALU), 1 VALU, 2 MFMA
+};
+constexpr unsigned kDefaultWaitLimit = 1u << 22;
+
+// Workspace: the synchronisation block first, at a fixed size for the
+// largest supported shape (so layers of any shapes can share one workspace:
+// everything a launch expects to find zero, or leaves for the next launch,
+// is in it), then per-call scratch that every call writes before it reads.
 struct Layout {
   size_t weights, proxy, workspace;
   size_t o_wd, o_psc, o_pred, o_pq2;
-  size_t o_part, o_tile_cnt, o_sabs, o_sel, o_selw, o_ssp, o_uni, o_nuni, o_umask,
-      o_ypart, o_col_cnt, o_ucnt, o_sync, o_xbuf, o_ybuf;
+  size_t o_sync, o_tile_cnt, o_col_cnt, o_ucnt, hdr;  // synchronisation block
+  size_t o_part, o_sabs, o_sel, o_selw, o_ssp, o_uni, o_nuni, o_umask, o_ypart, o_xbuf,
+      o_ybuf, o_drows, o_dcnt;
 };
 
-Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act);
+Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act,
+               const PlanChoice &ch = PlanChoice());
 Layout make_layout(const Plan &p);
+// Bytes of the synchronisation block at the start of every workspace.
+size_t sync_block_bytes();
 
 // Kernel launchers (prox_kernels.hip).  Each returns hipSuccess or the launch
 // error.  `batch` is the number of tokens (1..kMaxBatch).
@@ -88,8 +107,10 @@ hipError_t launch_prepare(const Plan &p, const Bufs &b, const void *w_up,
                           hipStream_t s);
 hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
                                int8_t *codes, float *scales, hipStream_t s);
+// dbg: the Stage 1 kernel also writes each token's survivors per 64-row
+// slice (the m_x decision it took) into b.drows / b.dcnt.
 hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
-                        float tau, hipStream_t s);
+                        float tau, hipStream_t s, bool dbg = false);
 hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
                        hipStream_t s);
 // mode: 0 = one token over sel, 1 = batch over the union, 2 = dense
@@ -97,15 +118,20 @@ hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
                          int mode, int n, hipStream_t s);
 hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
                        void *y, float *resid, hipStream_t s);
-hipError_t launch_compact_debug(const Plan &p, const void *x, int batch,
-                                float tau, int *n1, int *idx, hipStream_t s);
+// The per-slice survivor lists a Stage 1 kernel wrote (b.drows, b.dcnt)
+// assembled into n1[batch] and the ascending idx[batch][d_model].
+hipError_t launch_survivors(const Plan &p, const Bufs &b, int batch, int *n1, int *idx,
+                            hipStream_t s);
+// Copy the workspace status word to *out and clear it; after a timed-out
+// wait (bit 0) also reset the synchronisation block and the layer's cut guess.
+hipError_t launch_read_status(const Plan &p, const Bufs &b, int *out, hipStream_t s);
 hipError_t launch_rmsnorm(const Plan &p, const float *resid, int batch,
                           float eps, void *x, hipStream_t s);
 hipError_t launch_zero_y(const Plan &p, void *y, int batch, hipStream_t s);
 
 // The batch-1 step as one persistent kernel (prox_fused.hip).
 bool fused_supported(const Plan &p);
-size_t fused_sync_words(const Plan &p);
+size_t fused_sync_words();  // words of the fused kernel's block (for the largest shape)
 int fused_ypart_rows(const Plan &p);  // partial-y rows the fused kernel needs
 // trace: optional [fused_items][4] u64 timeline (start, wait end, end,
 // block | phase << 32).  ts_mode: Stage 2 mask |s~| >= tau_s instead of top-k
@@ -113,14 +139,17 @@ int fused_ypart_rows(const Plan &p);  // partial-y rows the fused kernel needs
 // norm: when norm.r is set, x is not read; the kernel forms x = RMSNorm(r)
 // itself (batch 1, x of at most 32 KiB, bit-identical to launch_rmsnorm) and
 // writes it to norm.xout.
-struct FusedNorm {
-  const float *r = nullptr;
+struct FusedOpts {
+  unsigned long long *trace = nullptr;
+  bool ts_mode = false;
+  float tau_s = 0.0f;
+  const float *norm_r = nullptr;  // RMSNorm input (float32 residual), or null
   float eps = 0.0f;
-  void *xout = nullptr;
+  void *xout = nullptr;           // where the normalized x is written
+  bool dbg = false;               // Stage 1 survivor lists into b.drows / b.dcnt
 };
 hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, int k, void *y,
-                        float *resid, hipStream_t s, unsigned long long *trace = nullptr,
-                        bool ts_mode = false, float tau_s = 0.0f, FusedNorm norm = FusedNorm());
+                        float *resid, hipStream_t s, const FusedOpts &o = FusedOpts());
 // Can launch_fused normalize x itself for this layer?
 bool fused_norm_supported(const Plan &p);
 int fused_items(const Plan &p, bool ts_mode);

@@ -148,6 +148,7 @@ struct ProxyArgs {
   unsigned *tile_cnt;
   float *sabs;
   int act;  // gate activation (gate_act)
+  int *drows, *dcnt;  // debug: per-token survivors per 64-row slice (nullptr: off)
 };
 
 // 5..8 tokens: 8 rows per stage, so that the accumulators of all tokens and
@@ -184,6 +185,8 @@ __global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a)
     for (int b = 0; b < NB; ++b) {
       float xl;
       const uint64_t mk = slice_mask<BF16>(a.x, (size_t)b * a.d_model + sl * 64, a.tau, xl);
+      if (a.drows && t == 0)
+        export_slice(a.drows + (size_t)b * a.d_model, a.dcnt + (size_t)b * nsl, sl, mk);
       xm[b] = ((mk >> lane) & 1ull) ? xl : 0.0f;
       xsum[b] = wave_sum(xm[b]);
       un |= mk;
@@ -454,6 +457,20 @@ __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
     w[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, code_off(s), 0, kNT);
   // (kept ahead of the staging: the scheduler would sink them below it)
   __builtin_amdgcn_sched_barrier(0);
+  if (a.drows && t == 0) {
+    // the input mask this kernel applies, per token and 64-row slice
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row0 = r0 + 512 * h + 64 * wv;  // the wave's 64 rows
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint64_t mk = __ballot(fabsf(xv[h][b]) >= a.tau);
+        if (row0 < a.d_model)
+          export_slice(a.drows + (size_t)b * a.d_model, a.dcnt + (size_t)b * (a.d_model / 64),
+                       row0 / 64, mk);
+      }
+    }
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1114,38 +1131,45 @@ __global__ __launch_bounds__(NW * 64, NW == 16 ? 8 : 4) void down_kernel(DownArg
 }
 
 // ---------------------------------------------------------------------------
-// Verification helper: the Stage 1 survivors as an ascending list, built
-// with the same slice_mask() the proxy kernel uses.  One work-group per token.
+// Verification helpers (debug entries only).
 // ---------------------------------------------------------------------------
-template <bool BF16>
-__global__ __launch_bounds__(1024) void compact_debug_kernel(const void *x,
-                                                             int d_model,
-                                                             float tau, int *n1,
-                                                             int *idx) {
-  __shared__ int cnt[kMaxDff / 64];
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nslices = d_model / 64;
-  const void *xb = (const char *)x + (size_t)b * d_model * (BF16 ? 2 : 4);
-  for (int s = wv; s < nslices; s += 16) {
-    float xl;
-    const uint64_t m = slice_mask<BF16>(xb, (size_t)s * 64, tau, xl);
-    if (lane == 0) cnt[s] = __popcll(m);
+// The per-slice survivor lists a Stage 1 kernel exported (export_slice)
+// concatenated in slice order: n1[b] and the ascending idx[b][0..n1).  One
+// work-group per token.
+__global__ __launch_bounds__(256) void survivors_kernel(const int *rows, const int *cnt,
+                                                        int d_model, int *n1, int *idx) {
+  __shared__ int off[kMaxDmodel / 64 + 1];
+  const int b = blockIdx.x, nsl = d_model / 64;
+  const int *rb = rows + (size_t)b * d_model;
+  const int *cb = cnt + (size_t)b * nsl;
+  if (threadIdx.x == 0) {
+    int o = 0;
+    for (int q = 0; q < nsl; ++q) {
+      off[q] = o;
+      o += cb[q];
+    }
+    off[nsl] = o;
+    n1[b] = o;
   }
   __syncthreads();
-  for (int s = wv; s < nslices; s += 16) {
-    float xl;
-    const uint64_t m = slice_mask<BF16>(xb, (size_t)s * 64, tau, xl);
-    int off = 0;
-    for (int q = 0; q < s; ++q) off += cnt[q];
-    if ((m >> lane) & 1ull)
-      idx[(size_t)b * d_model + off + __popcll(m & ((1ull << lane) - 1ull))] =
-          s * 64 + lane;
-  }
-  if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int q = 0; q < nslices; ++q) tot += cnt[q];
-    n1[b] = tot;
+  for (int q = threadIdx.x; q < nsl; q += blockDim.x)
+    for (int i = 0; i < cb[q]; ++i) idx[(size_t)b * d_model + off[q] + i] = rb[q * 64 + i];
+}
+
+// The workspace status word: copied out and cleared; after a timed-out wait
+// (bit 0) the whole synchronisation block and the layer's cut guess are
+// reset as well, so the next launch starts from the state it expects.
+__global__ __launch_bounds__(1024) void read_status_kernel(unsigned *hdr, size_t nwords,
+                                                           int err_word, unsigned *pred,
+                                                           int *out) {
+  const unsigned e = xload_u(&hdr[err_word]);
+  __syncthreads();  // every thread has read the word before anyone clears it
+  if (threadIdx.x == 0) *out = (int)e;
+  if (e & 1u) {
+    for (size_t i = threadIdx.x; i < nwords; i += blockDim.x) xstore_u(&hdr[i], 0u);
+    if (threadIdx.x == 0) xstore_u(pred, 0u);
+  } else if (threadIdx.x == 0) {
+    xstore_u(&hdr[err_word], 0u);
   }
 }
 
@@ -1218,10 +1242,7 @@ hipError_t launch_prepare(const Plan &p, const Bufs &b, const void *w_up,
     retile_pq2_kernel<<<dim3(p.d_model / 8, p.ntile), 512, 0, s>>>(b.pq, b.pq2, p.d_model);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  e = hipMemsetAsync(b.tile_cnt, 0, sizeof(unsigned) * p.ntile, s);
-  if (e != hipSuccess) return e;
-  if ((e = hipMemsetAsync(b.col_cnt, 0, sizeof(unsigned) * p.ncol, s)) != hipSuccess) return e;
-  return hipMemsetAsync(b.ucnt, 0, sizeof(unsigned), s);
+  return hipSuccess;  // the caller zeroes the workspace's synchronisation block
 }
 
 hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
@@ -1233,15 +1254,18 @@ hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
 }
 
 hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
-                        float tau, hipStream_t s) {
+                        float tau, hipStream_t s, bool dbg) {
   ProxyArgs a{b.pq, b.pq2, b.psc, x, tau, p.d_model, p.d_ff, p.G, p.ngroups,
-              p.nchunk, b.part, b.tile_cnt, b.sabs, p.act};
+              p.nchunk, b.part, b.tile_cnt, b.sabs, p.act,
+              dbg ? b.drows : nullptr, dbg ? b.dcnt : nullptr};
   dim3 g(p.nchunk, p.ntile);
-  // From 3 tokens on the matrix cores: at 2 the VALU kernel is faster (it
-  // reads only the rows the union of the input masks keeps, about 3/4 of
-  // them; measured at the 70B shape 54 against 59 us, and 81 against 63 us
-  // at 4 tokens).  Its own grid: ceil(d_model / kMfmaRows) work-groups per tile.
-  if (p.proxy_mfma && b.pq2 && batch >= 3) {
+  // On the matrix cores from p.proxy_mfma tokens: 3 by default, since at 2
+  // the VALU kernel is faster (it reads only the rows the union of the input
+  // masks keeps, about 3/4 of them; measured at the 70B shape 54 against
+  // 59 us, and 81 against 63 us at 4 tokens); 2 when the layer asks for the
+  // matrix-core form.  Its own grid: ceil(d_model / kMfmaRows) work-groups
+  // per tile.
+  if (p.proxy_mfma && b.pq2 && batch >= p.proxy_mfma) {
     a.nchunk = (p.d_model + kMfmaRows - 1) / kMfmaRows;
     const dim3 gm(a.nchunk, p.ntile);
     PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB><<<gm, 512, 0, s>>>(a)));
@@ -1491,12 +1515,16 @@ hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
   return hipGetLastError();
 }
 
-hipError_t launch_compact_debug(const Plan &p, const void *x, int batch,
-                                float tau, int *n1, int *idx, hipStream_t s) {
-  if (p.bf16)
-    compact_debug_kernel<true><<<batch, 1024, 0, s>>>(x, p.d_model, tau, n1, idx);
-  else
-    compact_debug_kernel<false><<<batch, 1024, 0, s>>>(x, p.d_model, tau, n1, idx);
+hipError_t launch_survivors(const Plan &p, const Bufs &b, int batch, int *n1, int *idx,
+                            hipStream_t s) {
+  survivors_kernel<<<batch, 256, 0, s>>>(b.drows, b.dcnt, p.d_model, n1, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_status(const Plan &p, const Bufs &b, int *out, hipStream_t s) {
+  (void)p;
+  read_status_kernel<<<1, 1024, 0, s>>>(b.sync, sync_block_bytes() / sizeof(unsigned),
+                                        kFusedErrWord, b.pred, out);
   return hipGetLastError();
 }
 

@@ -22,6 +22,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "prox.h")
 PROX_OK, PROX_EINVAL, PROX_EUNSUPPORTED, PROX_EHIP = 0, -1, -2, -3
 PROX_F32, PROX_BF16 = 0, 1
 PROX_ACT_SILU, PROX_ACT_GELU_TANH = 0, 1
+PROX_PATH_PERSISTENT, PROX_PATH_MULTI = 0, 1
+PROX_FORM_AUTO, PROX_FORM_VALU, PROX_FORM_MFMA = 0, 1, 2
 _STATUS = {0: "PROX_OK", -1: "PROX_EINVAL", -2: "PROX_EUNSUPPORTED", -3: "PROX_EHIP"}
 
 
@@ -34,7 +36,9 @@ class ProxError(RuntimeError):
 class prox_shape(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int), ("d_ff", ctypes.c_int),
                 ("group_size", ctypes.c_int), ("dtype", ctypes.c_int),
-                ("max_batch", ctypes.c_int), ("activation", ctypes.c_int)]
+                ("max_batch", ctypes.c_int), ("activation", ctypes.c_int),
+                ("path", ctypes.c_int), ("batch_stage1", ctypes.c_int),
+                ("batch_upgate", ctypes.c_int)]
 
 
 class prox_debug(ctypes.Structure):
@@ -81,6 +85,9 @@ def load_library(path: str = LIB_PATH):
                                    F, P], I),
         "prox_ffn_forward_ts_debug": ([P, P, F, F, P, ctypes.POINTER(prox_debug), P], I),
         "prox_rmsnorm": ([P, P, I, F, P, P], I),
+        "prox_read_status": ([P, P, P], I),
+        "prox_sync_block_bytes": ([], ctypes.c_size_t),
+        "prox_set_wait_limit": ([P, ctypes.c_uint32], I),
         "prox_destroy_layer": ([P], None),
         "prox_last_error": ([], ctypes.c_char_p),
     }
@@ -128,9 +135,11 @@ def prox_last_error() -> str:
 
 
 def prox_query_sizes(d_model: int, d_ff: int, group_size: int, dtype, max_batch: int = 1,
-                     activation: int = 0):
+                     activation: int = 0, path: int = 0, batch_stage1: int = 0,
+                     batch_upgate: int = 0):
     """(weights_bytes, proxy_bytes, workspace_bytes) for a layer shape."""
-    sh = prox_shape(d_model, d_ff, group_size, _dtype_code(dtype), max_batch, activation)
+    sh = prox_shape(d_model, d_ff, group_size, _dtype_code(dtype), max_batch, activation, path,
+                    batch_stage1, batch_upgate)
     w, p, ws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(load_library().prox_query_sizes(ctypes.byref(sh), ctypes.byref(w),
                                            ctypes.byref(p), ctypes.byref(ws)))
@@ -164,11 +173,14 @@ class Layer:
 
 
 def prox_prepare_layer(w_up, w_gate, w_down, group_size: int, max_batch: int = 1,
-                       workspace=None, activation: int = 0) -> Layer:
+                       workspace=None, activation: int = 0, path: int = 0,
+                       batch_stage1: int = 0, batch_upgate: int = 0) -> Layer:
     """Relayout and quantize one layer (weights in the x.W layout, on the GPU).
 
     A workspace tensor may be shared by layers that run on one stream.
-    activation: PROX_ACT_SILU (SwiGLU, default) or PROX_ACT_GELU_TANH (GeGLU)."""
+    activation: PROX_ACT_SILU (SwiGLU, default) or PROX_ACT_GELU_TANH (GeGLU);
+    path: PROX_PATH_PERSISTENT (default) or PROX_PATH_MULTI for batch-1 calls;
+    batch_stage1 / batch_upgate: PROX_FORM_* of the batched kernels."""
     d_model, d_ff = w_up.shape
     dt = _dtype_code(w_up.dtype)
     for t in (w_up, w_gate, w_down):
@@ -176,18 +188,35 @@ def prox_prepare_layer(w_up, w_gate, w_down, group_size: int, max_batch: int = 1
             raise ProxError(PROX_EINVAL, "weights must be contiguous CUDA tensors of one dtype")
     if tuple(w_gate.shape) != (d_model, d_ff) or tuple(w_down.shape) != (d_ff, d_model):
         raise ProxError(PROX_EINVAL, "weight shapes do not match")
-    wb, pb, wsb = prox_query_sizes(d_model, d_ff, group_size, w_up.dtype, max_batch, activation)
+    wb, pb, wsb = prox_query_sizes(d_model, d_ff, group_size, w_up.dtype, max_batch, activation,
+                                   path, batch_stage1, batch_upgate)
     dev = w_up.device
     weights = torch.empty(wb, dtype=torch.uint8, device=dev)
     proxy = torch.empty(pb, dtype=torch.uint8, device=dev)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    sh = prox_shape(d_model, d_ff, group_size, dt, max_batch, activation)
+    sh = prox_shape(d_model, d_ff, group_size, dt, max_batch, activation, path, batch_stage1,
+                    batch_upgate)
     h = ctypes.c_void_p()
     _check(load_library().prox_prepare_layer(
         ctypes.byref(sh), _ptr(w_up), _ptr(w_gate), _ptr(w_down), _ptr(weights),
         _ptr(proxy), _ptr(workspace), _stream(), ctypes.byref(h)))
     return Layer(h, sh, weights, proxy, workspace)
+
+
+def prox_read_status(layer: Layer, out=None):
+    """The workspace status word (bit 0: a bounded wait timed out, results
+    invalid; bit 1: the select's slow exact path), read and cleared on the
+    current stream.  Returns a device int32 tensor [1]."""
+    if out is None:
+        out = torch.zeros(1, dtype=torch.int32, device=layer.weights.device)
+    _check(load_library().prox_read_status(layer.handle, _ptr(out), _stream()))
+    return out
+
+
+def prox_set_wait_limit(layer: Layer, polls: int):
+    """Polls before a bounded wait of the persistent kernel gives up."""
+    _check(load_library().prox_set_wait_limit(layer.handle, int(polls)))
 
 
 def prox_export_proxy(layer: Layer, matrix: int):

@@ -27,8 +27,13 @@
  *    PROX_EUNSUPPORTED (valid but unsupported shape), PROX_EHIP (a HIP call
  *    or launch failed).  prox_last_error() describes the last failure of the
  *    calling thread.
- *  - A layer's workspace is reused by every call on that layer: calls that
- *    share a layer (or a workspace) must be ordered on one stream.
+ *  - A layer's workspace is reused by every call on that layer.  Layers of
+ *    any shapes may share one workspace buffer as large as the largest of
+ *    their workspace_bytes: its synchronisation block (tickets, flags,
+ *    counters, the status word) sits at offset 0 with a size fixed for the
+ *    largest supported shape, and everything past it is scratch that each
+ *    call writes before it reads.  Calls that share a layer or a workspace
+ *    must be ordered on one stream.
  */
 #ifndef PROX_H_
 #define PROX_H_
@@ -56,21 +61,42 @@ typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
  * the layer's activation.                                                  */
 typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
 
-/* Shape of one FFN layer.
+/* Kernel path of batch-1 forwards: one persistent kernel that takes Stage 1,
+ * the top-k select, Stage 2 up/gate and Stage 2 down items in dependency
+ * order (the default), or four kernels, one per phase.                     */
+typedef enum { PROX_PATH_PERSISTENT = 0, PROX_PATH_MULTI = 1 } prox_path;
+
+/* Arithmetic form of a batched (2..8 token) step: PROX_FORM_AUTO picks the
+ * measured faster one (Stage 1: matrix cores from 3 tokens for bf16 layers
+ * whose G is a multiple of 64, else vector ALU; Stage 2 up/gate: vector ALU).
+ * PROX_FORM_VALU / PROX_FORM_MFMA force one (MFMA: bf16 layers only).       */
+typedef enum { PROX_FORM_AUTO = 0, PROX_FORM_VALU = 1, PROX_FORM_MFMA = 2 } prox_form;
+
+/* Shape of one FFN layer, and the kernel choices made for it at prepare time.
  *   d_model     input/output width, at most 16384, a multiple of group_size
  *               and of 512 (bf16) or 256 (f32); batch * d_model activations
  *               must fit in 160 KiB
  *   d_ff        intermediate width, 1..32768
  *   group_size  G, rows per INT4 proxy scale group: 64, 128 or 256
  *   dtype       prox_dtype of weights, x and y
- *   max_batch   largest batch a forward call may pass, 1..8            */
+ *   max_batch   largest batch a forward call may pass, 1..8
+ *   activation  prox_activation (0: SiLU, the default)
+ *   path        prox_path of batch-1 forwards (0: the persistent kernel)
+ *   batch_stage1, batch_upgate
+ *               prox_form of the Stage 1 proxy GEMV and of the Stage 2
+ *               up/gate GEMV for batches of 2..8 tokens (0: automatic)
+ * A zero-initialised prox_shape with the first five fields set is the
+ * default configuration.                                                    */
 typedef struct {
   int d_model;
   int d_ff;
   int group_size;
   int dtype;
   int max_batch;
-  int activation;    /* prox_activation (0: SiLU, the default)            */
+  int activation;
+  int path;
+  int batch_stage1;
+  int batch_upgate;
 } prox_shape;
 
 /* Opaque host-side handle: shape, launch plan and the caller's buffers. */
@@ -84,11 +110,17 @@ typedef struct prox_layer prox_layer;
  *                   layers with max_batch >= 2 (G a multiple of 64, d_model of 32)
  *                   hold the codes a second time, 8 rows of one column per
  *                   word, for the matrix-core Stage 1 of several tokens
- *   workspace_bytes per-call scratch: partial sums, counters, masks, s values
+ *   workspace_bytes the synchronisation block plus per-call scratch (partial
+ *                   sums, |s~|, masks, s values)
  * Pure host function.  PROX_EINVAL on a null pointer or an invalid shape,
  * PROX_EUNSUPPORTED on a shape outside the limits above.                    */
 prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
                              size_t *proxy_bytes, size_t *workspace_bytes);
+
+/* Bytes of the synchronisation block at offset 0 of every workspace: the
+ * same for every shape (sized for the largest supported one), so layers of
+ * different shapes can share a workspace; workspace_bytes includes it.     */
+size_t prox_sync_block_bytes(void);
 
 /* Build a layer (Sec. 4.3: the INT4 proxy of W_up and W_gate is computed once
  * and stays resident).  Enqueues on `stream`:
@@ -99,7 +131,7 @@ prox_status prox_query_sizes(const prox_shape *shape, size_t *weights_bytes,
  *     scale = max|W[i][j]| / 7 (float32), code = clamp(rint(W / scale), -7, 7)
  *     (float32 divide, ties to even; an all-zero group has scale 0, codes 0),
  *     stored as 4-bit (code + 8), packed along j per input row;
- *   - zeroing of the workspace counters.
+ *   - zeroing of the workspace's synchronisation block.
  * Source weights must stay valid until the stream has run these kernels.
  * The three buffers belong to the caller and must outlive the layer.
  * On success *out receives a handle to free with prox_destroy_layer.        */
@@ -117,8 +149,12 @@ prox_status prox_export_proxy(const prox_layer *layer, int matrix /*0 up, 1 gate
 
 /* One token: y = Prox-FFN(x) (batch 1, the decode hot path).  Runs as one
  * persistent kernel whose work-groups take Stage 1, top-k, Stage 2 up/gate
- * and Stage 2 down items in dependency order (setting the environment
- * variable PROX_PATH=multi before prepare selects the four-kernel form).
+ * and Stage 2 down items in dependency order (a layer prepared with
+ * path = PROX_PATH_MULTI runs four kernels instead).  The persistent kernel
+ * assumes that all of its work-groups are resident together (its grid is
+ * sized from the occupancy of the device); work running concurrently on
+ * other streams can break that, and its bounded waits then give up: the
+ * workspace status (prox_read_status) has bit 0 set and y is invalid.
  *   x          [d_model] layer dtype
  *   threshold  tau of the Stage 1 input mask; an input survives iff
  *              |x_i| >= threshold (so threshold <= 0 keeps every input and
@@ -147,9 +183,9 @@ typedef struct {
   float *s_sel;      /* [batch][d_ff]      exact s of sel[b][t] at t (k used) */
   int32_t *n_union;  /* [1]                size of the union of the masks     */
   int32_t *union_idx;/* [d_ff]             the union, ascending               */
-  int32_t *status;   /* [1]  0, or bit 0: a bounded wait of the fused batch-1
-                        kernel timed out (results invalid); bit 1: its top-k
-                        took the slow exact path (results valid)             */
+  int32_t *status;   /* [1]  the workspace status word of this call alone (see
+                        prox_read_status); the debug entries clear it before
+                        the call                                             */
   int32_t *n_sel;    /* [1]  number of kept channels (batch-1 persistent kernel:
                         k for top-k, the count for the threshold mask)      */
 } prox_debug;
@@ -159,6 +195,29 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x,
                                    int batch, float threshold, int k, void *y,
                                    const prox_debug *dbg, void *stream);
 
+/* Workspace status.  Every forward on the persistent kernel ORs its error
+ * bits into a sticky status word of the layer's workspace (shared by every
+ * layer prepared on that workspace); no forward entry clears it.
+ *   bit 0 (1)  a bounded wait timed out: the outputs of the calls since the
+ *              last read are invalid (a work-group was not resident, see
+ *              prox_ffn_forward, or a wait limit set with prox_set_wait_limit
+ *              was too small);
+ *   bit 1 (2)  the top-k select took its slow exact path (massive exact ties
+ *              of |s~| around the k-th value); results valid.
+ * Enqueues on `stream` one kernel that copies the word into `status` (device
+ * int32) and clears it; when bit 0 was set it also resets the workspace's
+ * synchronisation block (tickets, flags, counters, histogram), so the next
+ * call starts clean.  No host synchronisation; read `status` after the stream
+ * has run it.  PROX_EINVAL on NULL arguments.                              */
+prox_status prox_read_status(const prox_layer *layer, int32_t *status, void *stream);
+
+/* Poll limit of the persistent kernel's bounded waits for this layer (the
+ * default, 4194304 polls, is seconds: only a work-group that never runs
+ * reaches it).  A wait that reaches it sets bit 0 of the workspace status and
+ * lets its work item finish with whatever data it has (the kernel always
+ * exits).  For tests of the error path.  PROX_EINVAL on a NULL layer.       */
+prox_status prox_set_wait_limit(prox_layer *layer, uint32_t polls);
+
 /* Batch-1 forward with the calibrated Stage 2 threshold of Sec. 4.1 instead
  * of the per-token top-k: channel j is kept iff |s~_j| >= threshold_s (|s~|
  * in float32), so the number of kept channels varies per token.  Stage 1 is
@@ -166,7 +225,7 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x,
  * on the persistent kernel without its select phase: each Stage 2 item
  * starts as soon as the Stage 1 tile holding its channels is done.
  * Errors: PROX_EINVAL for a NaN threshold or bad pointers; PROX_EUNSUPPORTED
- * for a layer prepared with PROX_PATH=multi.                                 */
+ * for a layer prepared with path = PROX_PATH_MULTI.                                 */
 prox_status prox_ffn_forward_ts(const prox_layer *layer, const void *x,
                                 float threshold_x, float threshold_s, void *y,
                                 void *stream);
@@ -198,7 +257,7 @@ prox_status prox_stack_forward(const prox_layer *const *layers, int n_layers,
  * 1): x = cast(RMSNorm(r)), y = Prox-FFN_l(x) with |x_i| >= thresholds_x[l]
  * and |s~_j| >= thresholds_s[l], r = r + y.  Both threshold arrays are HOST
  * arrays [n_layers].  PROX_EUNSUPPORTED if a layer was prepared with
- * PROX_PATH=multi.                                                          */
+ * path = PROX_PATH_MULTI.                                                          */
 prox_status prox_stack_forward_ts(const prox_layer *const *layers, int n_layers,
                                   const float *thresholds_x,
                                   const float *thresholds_s, float *resid,
@@ -242,7 +301,7 @@ prox_status prox_dense_ffn_forward_profiled(const prox_layer *layer,
  * bits of the 4th word, its phase (1..4: Stage 1, select, up/gate, down) in
  * the high 32 bits.  y is the
  * same as prox_ffn_forward's.  PROX_EUNSUPPORTED when the layer runs the
- * multi-kernel path (PROX_PATH=multi at prepare time).                       */
+ * multi-kernel path (path = PROX_PATH_MULTI).                       */
 prox_status prox_ffn_forward_traced(const prox_layer *layer, const void *x,
                                    float threshold, int k, void *y,
                                    unsigned long long *trace, int trace_items,

@@ -19,7 +19,14 @@ import numpy as np
 BAND_REL = 1e-3
 
 
-def check_mask(sel_gpu, sel_or, s_t_or, k: int) -> dict:
+def _record(case, res):
+    if case is None:
+        return
+    from tests import conftest
+    conftest.BAND_RECORDS.append(dict(case=case, band=res["band"], diff=res["diff"]))
+
+
+def check_mask(sel_gpu, sel_or, s_t_or, k: int, case=None) -> dict:
     sel_gpu = np.asarray(sel_gpu, dtype=np.int64)
     sel_or = np.asarray(sel_or, dtype=np.int64)
     a = np.abs(np.asarray(s_t_or, dtype=np.float64))
@@ -33,14 +40,18 @@ def check_mask(sel_gpu, sel_or, s_t_or, k: int) -> dict:
     diff = np.setxor1d(sel_gpu, sel_or)
     if vk == 0.0:
         assert diff.size == 0, "k-th value is 0: selection must follow the lower-index rule exactly"
-        return dict(band=int(np.sum(a == 0.0)), diff=0)
+        res = dict(band=int(np.sum(a == 0.0)), diff=0)
+        _record(case, res)
+        return res
     band = np.abs(a - vk) <= BAND_REL * vk
     outside = [int(j) for j in diff if not band[j]]
     assert not outside, f"mask differs outside the tie band at channels {outside[:10]}"
-    return dict(band=int(band.sum()), diff=int(diff.size))
+    res = dict(band=int(band.sum()), diff=int(diff.size))
+    _record(case, res)
+    return res
 
 
-def check_threshold_mask(sel_gpu, sel_or, s_t_or, tau_s: float) -> dict:
+def check_threshold_mask(sel_gpu, sel_or, s_t_or, tau_s: float, case=None) -> dict:
     """Stage 2 threshold mask |s~| >= tau_s: the GPU list must be strictly
     ascending and in range, and may differ from the oracle's only at channels
     whose oracle |s~| lies within BAND_REL (relative) of tau_s, where the
@@ -56,7 +67,9 @@ def check_threshold_mask(sel_gpu, sel_or, s_t_or, tau_s: float) -> dict:
     band = np.abs(a - tau_s) <= BAND_REL * abs(tau_s)
     outside = [int(j) for j in diff if not band[j]]
     assert not outside, f"mask differs outside the threshold band at channels {outside[:10]}"
-    return dict(band=int(band.sum()), diff=int(diff.size))
+    res = dict(band=int(band.sum()), diff=int(diff.size))
+    _record(case, res)
+    return res
 
 
 def expected_y(sel_gpu, sel_or, y_or, s_exact_all, W_down) -> np.ndarray:

@@ -114,3 +114,61 @@ def test_costmodel_effective_sparsity_of_configs():
     assert [synth.k_for(14336, p) for p in (0.5, 0.6, 0.7)] == [7168, 5734, 4301]
     assert [synth.k_for(17408, p) for p in (0.6, 0.7)] == [6963, 5222]
     assert synth.k_for(28672, 0.7) == 8602 and synth.k_for(688, 0.7) == 206
+
+
+def _qs(sh):
+    w, p, ws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = prox.load_library().prox_query_sizes(ctypes.byref(sh), ctypes.byref(w),
+                                              ctypes.byref(p), ctypes.byref(ws))
+    return st, w.value, p.value, ws.value
+
+
+def test_kernel_choices_are_declared_shape_fields(lib):
+    """The kernel path and the batched forms are prox_shape fields, checked
+    like the sizes (no environment variable is read)."""
+    base = dict(d_model=1024, d_ff=2816, group_size=128, dtype=prox.PROX_BF16, max_batch=8)
+    ok = [dict(path=prox.PROX_PATH_MULTI), dict(batch_stage1=prox.PROX_FORM_VALU),
+          dict(batch_stage1=prox.PROX_FORM_MFMA), dict(batch_upgate=prox.PROX_FORM_MFMA),
+          dict(batch_upgate=prox.PROX_FORM_VALU)]
+    for extra in ok:
+        assert _qs(prox.prox_shape(**base, **extra))[0] == prox.PROX_OK, extra
+    for extra in (dict(path=2), dict(batch_stage1=3), dict(batch_upgate=-1)):
+        assert _qs(prox.prox_shape(**base, **extra))[0] == prox.PROX_EINVAL, extra
+    f32 = dict(base, dtype=prox.PROX_F32)
+    assert _qs(prox.prox_shape(**f32, batch_upgate=prox.PROX_FORM_MFMA))[0] == \
+        prox.PROX_EUNSUPPORTED
+    assert _qs(prox.prox_shape(**f32, batch_stage1=prox.PROX_FORM_MFMA))[0] == \
+        prox.PROX_EUNSUPPORTED
+    # the matrix-core Stage 1 keeps a second copy of the codes: the automatic
+    # choice holds it from 3 tokens, the VALU form never
+    auto = _qs(prox.prox_shape(**base))[2]
+    valu = _qs(prox.prox_shape(**base, batch_stage1=prox.PROX_FORM_VALU))[2]
+    assert auto - valu >= 1024 * 2816 // 2
+    two = dict(base, max_batch=2)
+    assert _qs(prox.prox_shape(**two))[2] == _qs(prox.prox_shape(**two, batch_stage1=1))[2]
+    assert _qs(prox.prox_shape(**two, batch_stage1=2))[2] > _qs(prox.prox_shape(**two))[2]
+
+
+def test_workspace_sync_block_is_shape_independent(lib):
+    """Every workspace starts with the same fixed-size synchronisation block,
+    so layers of different shapes (or max_batch) can share one workspace:
+    each one's scratch starts past the block whatever its shape."""
+    hdr = lib.prox_sync_block_bytes()
+    assert hdr > 0 and hdr % 256 == 0
+    shapes = [(4096, 14336, 128, prox.PROX_BF16, 1), (4096, 14336, 128, prox.PROX_BF16, 8),
+              (256, 688, 64, prox.PROX_F32, 1), (8192, 28672, 128, prox.PROX_BF16, 8),
+              (16384, 32768, 256, prox.PROX_BF16, 1)]
+    for sh in shapes:
+        st, _, _, ws = _q(*sh)
+        assert st == prox.PROX_OK
+        d_model, d_ff, _, dt, mb = sh
+        esz = 2 if dt == prox.PROX_BF16 else 4
+        # at least |s~|, s, x and y scratch past the block
+        assert ws >= hdr + mb * d_ff * 4 + d_ff * 4 + 2 * mb * d_model * esz
+    assert lib.prox_sync_block_bytes() == hdr
+
+
+def test_status_entries_reject_null(lib):
+    P = ctypes.c_void_p
+    assert lib.prox_read_status(None, P(256), None) == prox.PROX_EINVAL
+    assert lib.prox_set_wait_limit(None, 5) == prox.PROX_EINVAL
