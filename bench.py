@@ -342,7 +342,8 @@ def bench_single_layer(args, name):
                    GBps=round(ab["total"] / (gms * 1e-3) / 1e9, 1)),
         dense=dict(us_per_layer=round(dms * 1e3, 2),
                    GBps=round(3 * cfg.d_model * cfg.d_ff * 2 / (dms * 1e-3) / 1e9, 1),
-                   kernels=dict(upgate_us=round(dkms[0] * 1e3, 2), down_us=round(dkms[1] * 1e3, 2))),
+                   kernels=dict(upgate_us=round(dkms[0] * 1e3, 2),
+                                down_us=round(dkms[1] * 1e3, 2))),
         speedup_vs_dense=round(dms / ms, 3),
         other_sparsities=others,
         roofline=roof,
@@ -546,8 +547,11 @@ def bench_timeline(args):
     for i in range(args.warmup):
         prox.prox_ffn_forward(layers[i % R], X[i % R][i % 8], taus[i % R], k, y)
     names = {1: "stage1", 2: "select", 3: "upgate", 4: "down"}
-    per = {n: dict(first_start=[], med_start=[], last_end=[], med_wait=[], med_dur=[])
-           for n in names.values()}
+    # "mid" is the item's middle stamp: the end of its wait for earlier items;
+    # for a Stage 1 item the end of its code loop, for the select the moment
+    # b* is published
+    per = {n: dict(first_start=[], med_start=[], med_mid=[], last_mid=[], last_end=[],
+                   med_dur=[]) for n in names.values()}
     spans = []
     ncalls = max(4, min(args.steps, 40))
     for i in range(ncalls):
@@ -567,11 +571,15 @@ def bench_timeline(args):
             en = (t[m, 2] - t0) / 100.0
             per[nm]["first_start"].append(st.min())
             per[nm]["med_start"].append(np.median(st))
+            per[nm]["med_mid"].append(np.median(we - st))
+            per[nm]["last_mid"].append(we.max())
             per[nm]["last_end"].append(en.max())
-            per[nm]["med_wait"].append(np.median(we - st))
             per[nm]["med_dur"].append(np.median(en - st))
     out = {nm: {key: round(float(np.median(v)), 2) for key, v in d.items() if v}
            for nm, d in per.items()}
+    if args.dump:
+        # the raw per-ticket records of the last call, for offline analysis
+        np.save(args.dump, tr.cpu().numpy())
     return dict(metric="per-phase timeline of the persistent kernel, 8B-shaped, batch 1",
                 unit="us", n_gpus=1, calls=ncalls, k=k, counts=counts,
                 item_span_us=round(float(np.median(spans)), 2), phases=out)
@@ -599,6 +607,8 @@ def main():
     ap.add_argument("--ring", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dump", default=None,
+                    help="timeline workload: save the last call's raw trace (.npy) here")
     ap.add_argument("--batch-gemv", choices=["valu", "mfma"], default="valu",
                     help="form of the batched up/gate step the layers are prepared with")
     args = ap.parse_args()
