@@ -12,6 +12,7 @@
 
 #include <new>
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/prox.h"
@@ -21,6 +22,13 @@ struct prox_layer {
   prox::Plan plan;
   prox::Bufs bufs;
 };
+
+// Scratch of prox_ffn_forward_noalloc: one static device array per GPU
+// (every GPU the library runs on holds its own copy until the process ends),
+// standing in for the caller's workspace.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): it
+// uses the device address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[prox::kNoAllocScratchBytes];
 
 namespace {
 
@@ -88,6 +96,27 @@ prox_status check_shape(const prox_shape *sh) {
   if ((size_t)sh->d_ff * 2 * sh->d_model * esz >= (1ull << 32))
     return fail(PROX_EUNSUPPORTED, "up/gate weights above 4 GiB are not supported");
   return PROX_OK;
+}
+
+// Point the per-call buffers of a layer into the workspace at ws.
+void bind_workspace(const prox::Layout &lay, char *ws, prox::Bufs &b) {
+  b.part = (float *)(ws + lay.o_part);
+  b.tile_cnt = (unsigned *)(ws + lay.o_tile_cnt);
+  b.drows = (int *)(ws + lay.o_drows);
+  b.dcnt = (int *)(ws + lay.o_dcnt);
+  b.sabs = (float *)(ws + lay.o_sabs);
+  b.sel = (int *)(ws + lay.o_sel);
+  b.selw = (unsigned *)(ws + lay.o_selw);
+  b.ssp = (float *)(ws + lay.o_ssp);
+  b.uni = (int *)(ws + lay.o_uni);
+  b.nuni = (int *)(ws + lay.o_nuni);
+  b.umask = (uint8_t *)(ws + lay.o_umask);
+  b.ypart = (float *)(ws + lay.o_ypart);
+  b.col_cnt = (unsigned *)(ws + lay.o_col_cnt);
+  b.ucnt = (unsigned *)(ws + lay.o_ucnt);
+  b.sync = (unsigned *)(ws + lay.o_sync);
+  b.xbuf = ws + lay.o_xbuf;
+  b.ybuf = ws + lay.o_ybuf;
 }
 
 prox::Plan plan_of(const prox_shape *sh) {
@@ -280,6 +309,35 @@ prox_status check_forward_args(const prox_layer *L, const void *x, int batch,
   return PROX_OK;
 }
 
+// The scratch array's device address on the current device, taken once per
+// device (with the device current) and kept; its synchronisation block is
+// zeroed on `s` by the first call on each device (a fill kernel).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+prox_status scratch_for_current_device(hipStream_t s, char **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PROX_EUNSUPPORTED, "device %d above the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PROX_EHIP, "hipGetSymbolAddress(scratch) gave a null address");
+    // tickets, flags, counters and the status word start at zero
+    e = prox::launch_zero_bytes(p, prox::sync_block_bytes(), s);
+    if (e != hipSuccess) return hip_fail(e, "scratch clear kernel");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char *)g_scratch_ptr[dev];
+  return PROX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -332,23 +390,7 @@ prox_status prox_prepare_layer(const prox_shape *shape, const void *w_up,
   b.psc = (float *)(pb + lay.o_psc);
   b.pred = (unsigned *)(pb + lay.o_pred);
   b.pq2 = L->plan.proxy_mfma ? (unsigned *)(pb + lay.o_pq2) : nullptr;
-  b.part = (float *)(ws + lay.o_part);
-  b.tile_cnt = (unsigned *)(ws + lay.o_tile_cnt);
-  b.drows = (int *)(ws + lay.o_drows);
-  b.dcnt = (int *)(ws + lay.o_dcnt);
-  b.sabs = (float *)(ws + lay.o_sabs);
-  b.sel = (int *)(ws + lay.o_sel);
-  b.selw = (unsigned *)(ws + lay.o_selw);
-  b.ssp = (float *)(ws + lay.o_ssp);
-  b.uni = (int *)(ws + lay.o_uni);
-  b.nuni = (int *)(ws + lay.o_nuni);
-  b.umask = (uint8_t *)(ws + lay.o_umask);
-  b.ypart = (float *)(ws + lay.o_ypart);
-  b.col_cnt = (unsigned *)(ws + lay.o_col_cnt);
-  b.ucnt = (unsigned *)(ws + lay.o_ucnt);
-  b.sync = (unsigned *)(ws + lay.o_sync);
-  b.xbuf = ws + lay.o_xbuf;
-  b.ybuf = ws + lay.o_ybuf;
+  bind_workspace(lay, ws, b);
   hipError_t e = prox::launch_prepare(L->plan, b, w_up, w_gate, w_down, (hipStream_t)stream);
   // the synchronisation block (tickets, flags, counters, status) and the
   // layer's cut guess start at zero
@@ -379,6 +421,26 @@ prox_status prox_ffn_forward(const prox_layer *layer, const void *x, float thres
   prox_status st = check_forward_args(layer, x, 1, threshold, k, y);
   if (st != PROX_OK) return st;
   return run_forward(layer, x, 1, threshold, k, y, nullptr, (hipStream_t)stream);
+}
+
+prox_status prox_ffn_forward_noalloc(const prox_layer *layer, const void *x, float threshold,
+                                     int k, void *y, void *stream) {
+  g_err.clear();
+  prox_status st = check_forward_args(layer, x, 1, threshold, k, y);
+  if (st != PROX_OK) return st;
+  // the layer's batch-1 per-call buffers, laid out in the static scratch
+  prox_layer L = *layer;
+  L.plan.max_batch = 1;
+  const prox::Layout lay = prox::make_layout(L.plan);
+  if (lay.workspace > prox::kNoAllocScratchBytes)
+    return fail(PROX_EUNSUPPORTED,
+                "the layer needs %zu bytes of per-call scratch; the static scratch holds %zu",
+                lay.workspace, prox::kNoAllocScratchBytes);
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = nullptr;
+  if ((st = scratch_for_current_device(s, &ws)) != PROX_OK) return st;
+  bind_workspace(lay, ws, L.bufs);
+  return run_forward(&L, x, 1, threshold, k, y, nullptr, s);
 }
 
 prox_status prox_ffn_forward_batch(const prox_layer *layer, const void *x, int batch,

@@ -128,6 +128,12 @@ hipError_t launch_read_status(const Plan &p, const Bufs &b, int *out, hipStream_
 hipError_t launch_rmsnorm(const Plan &p, const float *resid, int batch,
                           float eps, void *x, hipStream_t s);
 hipError_t launch_zero_y(const Plan &p, void *y, int batch, hipStream_t s);
+// Zero `bytes` (a multiple of 4) at p with a fill kernel.
+hipError_t launch_zero_bytes(void *p, size_t bytes, hipStream_t s);
+
+// Size of the static device scratch of prox_ffn_forward_noalloc: the
+// batch-1 per-call buffers of layers up to the 70B shape (8192 x 28672).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
 
 // The batch-1 step as one persistent kernel (prox_fused.hip).
 bool fused_supported(const Plan &p);

@@ -15,6 +15,7 @@
 // work-groups is deterministic (partials + last-arriving work-group, fixed
 // summation order).
 #include "prox_device.h"
+#include <algorithm>
 
 namespace prox {
 
@@ -1534,6 +1535,19 @@ hipError_t launch_rmsnorm(const Plan &p, const float *resid, int batch,
     rmsnorm_kernel<true><<<batch, kRmsThreads, 0, s>>>(resid, p.d_model, eps, x);
   else
     rmsnorm_kernel<false><<<batch, kRmsThreads, 0, s>>>(resid, p.d_model, eps, x);
+  return hipGetLastError();
+}
+
+__global__ void zero_words_kernel(unsigned *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero_bytes(void *p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
+  zero_words_kernel<<<blocks, 256, 0, s>>>((unsigned *)p, n);
   return hipGetLastError();
 }
 

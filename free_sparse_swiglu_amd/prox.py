@@ -68,6 +68,7 @@ def load_library(path: str = LIB_PATH):
         "prox_prepare_layer": ([S, P, P, P, P, P, P, P, ctypes.POINTER(P)], I),
         "prox_export_proxy": ([P, I, P, P, P], I),
         "prox_ffn_forward": ([P, P, F, I, P, P], I),
+        "prox_ffn_forward_noalloc": ([P, P, F, I, P, P], I),
         "prox_ffn_forward_batch": ([P, P, I, F, I, P, P], I),
         "prox_ffn_forward_debug": ([P, P, I, F, I, P, ctypes.POINTER(prox_debug), P], I),
         "prox_dense_ffn_forward": ([P, P, I, P, P], I),

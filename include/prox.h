@@ -165,6 +165,25 @@ prox_status prox_export_proxy(const prox_layer *layer, int matrix /*0 up, 1 gate
 prox_status prox_ffn_forward(const prox_layer *layer, const void *x,
                              float threshold, int k, void *y, void *stream);
 
+/* prox_ffn_forward for callers that cannot allocate device memory or run
+ * allocating routines (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, but the
+ * per-call scratch (partial sums, |s~|, masks, tickets, flags) lives in one
+ * static device array of the library, 8 MiB per GPU (every GPU the library
+ * runs on holds its own copy until the process ends), instead of the layer's
+ * workspace.  The layer's weights and proxy buffers are read as usual.  The
+ * call allocates nothing (no hipMalloc/hipFree, no allocating library
+ * routine); on its first use on a device it takes the array's device address
+ * and zeroes its synchronisation block with a fill kernel on `stream`.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads)
+ * race.  The status word of these calls stays in the array (it is not read
+ * back by prox_read_status).  Errors as prox_ffn_forward, plus
+ * PROX_EUNSUPPORTED when the layer's batch-1 scratch exceeds 8 MiB (shapes
+ * above 8192 x 28672).                                                      */
+prox_status prox_ffn_forward_noalloc(const prox_layer *layer, const void *x,
+                                     float threshold, int k, void *y, void *stream);
+
 /* `batch` independent tokens (1 <= batch <= max_batch), x and y [batch][d_model].
  * Each token gets its own input mask and its own top-k mask; the union of
  * the masks decides which weight rows are streamed, and every token's s is
