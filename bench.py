@@ -78,7 +78,40 @@ def algorithmic_bytes(cfg, n1, groups_touched, k, batch=1, union=None):
                 total=stage1 + upgate + down + io)
 
 
-def build_ring(cfg, ring, max_batch=1, path=0, activation=0, batch_upgate=0):
+def saved_thresholds(name, recipe, compute):
+    """The thresholds of a workload from its saved calibration artifact
+    (calib/<name>.json) when its recipe matches; otherwise calibrated now and
+    saved (also under gpurun_out/calib/).  Returns (thresholds, source, path)."""
+    from free_sparse_swiglu_amd import thresholds
+    th = thresholds.load(name, recipe)
+    if th is not None:
+        return th, "loaded", thresholds.path_for(name)
+    th = compute()
+    p = thresholds.save(name, recipe, th)
+    try:
+        thresholds.save(name, recipe, th, out_dir=os.path.join(ROOT, "gpurun_out", "calib"))
+    except OSError:
+        pass
+    return th, "calibrated", p
+
+
+def ring_recipe(cfg, ring):
+    return dict(workload=cfg.name, d_model=cfg.d_model, d_ff=cfg.d_ff, dtype=cfg.dtype,
+                x_dist=cfg.x_dist, quantile=cfg.tau_quantile, n_calib=cfg.n_calib, ring=ring,
+                inputs="synth.make_inputs(cfg, n_calib, 'calib', layer, 'cuda')",
+                rule="tau_x = sorted |x| at floor(q (N - 1))")
+
+
+def ring_taus(cfg, ring):
+    """Per-layer input thresholds of a ring of seeded layers (saved artifact)."""
+    from free_sparse_swiglu_amd import synth
+    th, src, path = saved_thresholds(
+        f"{cfg.name}_ring{ring}", ring_recipe(cfg, ring),
+        lambda: dict(tau_x=[synth.layer_tau(cfg, l, "cuda") for l in range(ring)]))
+    return th["tau_x"], dict(source=src, path=os.path.relpath(path, ROOT))
+
+
+def build_ring(cfg, ring, max_batch=1, path=0, activation=0, batch_upgate=0, taus=None):
     """Prepare `ring` seeded layers sharing one workspace.  path=1
     (PROX_PATH_MULTI) prepares them for the multi-kernel path (one kernel per
     phase); activation 1 makes them GeGLU layers; batch_upgate is the
@@ -86,8 +119,10 @@ def build_ring(cfg, ring, max_batch=1, path=0, activation=0, batch_upgate=0):
     import torch
 
     from free_sparse_swiglu_amd import prox, synth
-    layers, taus = [], []
+    layers = []
     ws = None
+    if taus is None:
+        taus, _ = ring_taus(cfg, ring)
     for l in range(ring):
         W = synth.make_layer(cfg, l, "cuda")
         L = prox.prox_prepare_layer(*W, cfg.group, max_batch, workspace=ws,
@@ -97,8 +132,7 @@ def build_ring(cfg, ring, max_batch=1, path=0, activation=0, batch_upgate=0):
         torch.cuda.synchronize()
         del W
         layers.append(L)
-        taus.append(synth.layer_tau(cfg, l, "cuda"))
-    return layers, taus
+    return layers, list(taus)
 
 
 def time_loop(fn, steps, warmup):
@@ -114,6 +148,36 @@ def time_loop(fn, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps  # ms per step
+
+
+def time_repeats(fn, steps, warmup, repeats):
+    """`repeats` timed loops of exactly `steps` steps each (the warm-up runs
+    once, before the first); returns the list of ms per step."""
+    out = [time_loop(fn, steps, warmup)]
+    for _ in range(repeats - 1):
+        out.append(time_loop(fn, steps, 0))
+    return out
+
+
+def spread(ms_list):
+    import numpy as np
+    a = np.asarray(ms_list) * 1e3
+    return dict(repeats=len(a), median_us=round(float(np.median(a)), 3),
+                min_us=round(float(a.min()), 3), max_us=round(float(a.max()), 3))
+
+
+def measured_copy_peak(steps=20):
+    """Device-to-device copy of 1 GiB (bytes read + bytes written per second):
+    the streaming rate this GPU sustains, reported beside the published peak."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    ms = min(time_loop(lambda i: b.copy_(a), steps, 3) for _ in range(3))
+    del a, b
+    torch.cuda.synchronize()
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
 
 
 def profile_kernels(call, steps, n_events):
@@ -162,7 +226,8 @@ def bench_single_layer(args, name):
     from free_sparse_swiglu_amd import costmodel, prox, synth
     cfg = synth.CONFIGS[name]
     k = synth.k_for(cfg.d_ff, args.sparsity)
-    layers, taus = build_ring(cfg, args.ring)
+    taus0, tsrc = ring_taus(cfg, args.ring)
+    layers, taus = build_ring(cfg, args.ring, taus=taus0)
     R = len(layers)
     NX = 16
     X = [synth.make_inputs(cfg, NX, "bench", l, "cuda") for l in range(R)]
@@ -184,7 +249,9 @@ def bench_single_layer(args, name):
         l = i % R
         prox.prox_ffn_forward(layers[l], X[l][(i // R) % NX], taus[l], k, y)
 
-    ms = time_loop(step, args.steps, args.warmup)
+    reps = time_repeats(step, args.steps, args.warmup, args.repeats)
+    import numpy as _np
+    ms = float(_np.median(reps))
 
     def pstep(i, evs):
         l = i % R
@@ -195,7 +262,8 @@ def bench_single_layer(args, name):
     def dstep(i):
         l = i % R
         prox.prox_dense_ffn_forward(layers[l], X[l][(i // R) % NX], y)
-    dms = time_loop(dstep, args.steps, args.warmup)
+    dreps = time_repeats(dstep, args.steps, args.warmup, args.repeats)
+    dms = float(_np.median(dreps))
 
     def dpstep(i, evs):
         l = i % R
@@ -307,11 +375,15 @@ def bench_single_layer(args, name):
     dom_us = ms * 1e3
     achieved = ab["total"] / (dom_us * 1e-6) / 1e9
     traffic = load_traffic(name)
+    copy_peak = measured_copy_peak()
     roof = dict(bound="hbm", kernel=dom, launch_us=round(dom_us, 2),
                 achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
                 bytes_per_launch=int(ab["total"]),
-                traffic=(traffic or {}).get("bytes_per_launch") if traffic else None)
+                traffic=(traffic or {}).get("bytes_per_launch") if traffic else None,
+                measured_peak=copy_peak,
+                measured_peak_kind="1 GiB device copy, bytes read + written per second",
+                frac_of_measured=round(achieved / copy_peak, 4))
 
     s1 = 1.0 - n1m / cfg.d_model
     s2 = 1.0 - k / cfg.d_ff
@@ -323,11 +395,13 @@ def bench_single_layer(args, name):
         n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms, 5),
         us_per_layer=round(ms * 1e3, 2),
+        repeats=spread(reps),
         us_per_layer_graph=round(graph_ms * 1e3, 2) if graph_ms else None,
         hbm_frac=round(ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16", data="synthetic",
         config=dict(workload=f"{name}-shaped single FFN layer, batch 1",
+                    threshold_artifact=tsrc,
                     d_model=cfg.d_model, d_ff=cfg.d_ff, group=cfg.group, k=k,
                     sparsity=args.sparsity, ring_layers=R, tau_quantile=cfg.tau_quantile,
                     mean_n1=round(n1m, 1), realised_s1=round(s1, 4), s2=round(s2, 4),
@@ -340,7 +414,7 @@ def bench_single_layer(args, name):
                             speedup_vs_dense=round(dms / tms, 3)),
         geglu=dict(us_per_layer=round(gms * 1e3, 2),
                    GBps=round(ab["total"] / (gms * 1e-3) / 1e9, 1)),
-        dense=dict(us_per_layer=round(dms * 1e3, 2),
+        dense=dict(us_per_layer=round(dms * 1e3, 2), repeats=spread(dreps),
                    GBps=round(3 * cfg.d_model * cfg.d_ff * 2 / (dms * 1e-3) / 1e9, 1),
                    kernels=dict(upgate_us=round(dkms[0] * 1e3, 2),
                                 down_us=round(dkms[1] * 1e3, 2))),
@@ -404,8 +478,21 @@ def bench_stack(args):
         torch.cuda.synchronize()
         del W
         layers.append(L)
-    calib = synth.make_inputs(cfg, cfg.n_calib, "calib", 0, "cuda").float()
-    taus = calibrate.sequential_thresholds(layers, calib, cfg.tau_quantile, k)
+    from free_sparse_swiglu_amd import costmodel
+    s1, s2 = costmodel.allocate(0.7)
+    recipe = dict(workload=cfg.name, layers=cfg.layers, d_model=cfg.d_model, d_ff=cfg.d_ff,
+                  k=k, quantile=cfg.tau_quantile, n_calib=cfg.n_calib, n_calib_ts=64,
+                  s1=round(s1, 6), s2=round(s2, 6), eps=1e-5,
+                  inputs="synth.make_inputs(cfg, n_calib, 'calib', 0, 'cuda') as residuals",
+                  rule="sequential in depth order (Algorithm 1, App. A.7)")
+
+    def calibrate_stack():
+        calib = synth.make_inputs(cfg, cfg.n_calib, "calib", 0, "cuda").float()
+        taus = calibrate.sequential_thresholds(layers, calib, cfg.tau_quantile, k)
+        tx, ts = calibrate.sequential_thresholds_ts(layers, calib[:64], s1, s2)
+        return dict(tau_x_topk=taus, tau_x=tx, tau_s=ts)
+    th, tsrc, tpath = saved_thresholds(f"{cfg.name}", recipe, calibrate_stack)
+    taus, tx, ts = th["tau_x_topk"], th["tau_x"], th["tau_s"]
     ntok = 128
     R0 = synth.make_inputs(cfg, ntok, "stack", 0, "cuda").float()
     r = R0.clone()
@@ -423,15 +510,38 @@ def bench_stack(args):
     sec = run_tokens(k)
     dsec = run_tokens(-1)
 
+    # The same 32-layer step captured once as a HIP graph (torch.cuda.graph
+    # around one prox_stack_forward call on a fixed residual buffer) and
+    # replayed 128 times: launch overhead of graph replay against stream
+    # launches of the same kernels.
+    graph_tps = None
+    try:
+        rg = R0[0].clone()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            prox.prox_stack_forward(layers, taus, k, rg)
+        torch.cuda.current_stream().wait_stream(gs)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            prox.prox_stack_forward(layers, taus, k, rg)
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(ntok):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_tps = round(ntok / (time.perf_counter() - t0), 1)
+    except Exception as e:  # capture unsupported: stream numbers only
+        print(f"graph capture skipped: {e}", file=sys.stderr)
+
     # The pages' own operating mode: calibrated thresholds for both stages
     # (Sec. 4.1 masks), allocated for a 70% effective sparsity target (Sec. 4.2:
     # s1 = 0.7, s2 = 0.767), calibrated sequentially (App. A.7, Algorithm 1)
     # on 64 tokens, timed on the same 128 tokens, runtime sparsity measured on
     # 16 other tokens.
-    from free_sparse_swiglu_amd import costmodel
-    s1, s2 = costmodel.allocate(0.7)
-    tx, ts = calibrate.sequential_thresholds_ts(layers, calib[:64], s1, s2)
-
     def run_tokens_ts():
         r.copy_(R0)
         torch.cuda.synchronize()
@@ -456,6 +566,8 @@ def bench_stack(args):
                 data="synthetic", higher_is_better=True,
                 config=dict(workload="32 x 8B-shaped FFN layers + RMSNorm + residual, "
                                      "128 sequential tokens", k=k, layers=cfg.layers),
+                graph_tokens_per_s=graph_tps,
+                threshold_artifact=dict(source=tsrc, path=os.path.relpath(tpath, ROOT)),
                 dense_tokens_per_s=round(ntok / dsec, 1), speedup_vs_dense=round(dsec / sec, 3),
                 us_per_layer=round(sec / ntok / cfg.layers * 1e6, 2),
                 thresholds=[round(t, 5) for t in taus],
@@ -604,6 +716,8 @@ def main():
     ap.add_argument("--workload", default="8b",
                     choices=["8b", "14b", "70b", "stack8b", "alpha", "copy", "timeline"])
     ap.add_argument("--sparsity", type=float, default=0.7)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed loops of --steps steps each; the median is reported")
     ap.add_argument("--ring", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
