@@ -249,9 +249,9 @@ def bench_single_layer(args, name):
         l = i % R
         prox.prox_ffn_forward(layers[l], X[l][(i // R) % NX], taus[l], k, y)
 
-    reps = time_repeats(step, args.steps, args.warmup, args.repeats)
+    srep = time_repeats(step, args.steps, args.warmup, args.repeats)
     import numpy as _np
-    ms = float(_np.median(reps))
+    ms = float(_np.median(srep))
 
     def pstep(i, evs):
         l = i % R
@@ -262,8 +262,8 @@ def bench_single_layer(args, name):
     def dstep(i):
         l = i % R
         prox.prox_dense_ffn_forward(layers[l], X[l][(i // R) % NX], y)
-    dreps = time_repeats(dstep, args.steps, args.warmup, args.repeats)
-    dms = float(_np.median(dreps))
+    drep = time_repeats(dstep, args.steps, args.warmup, args.repeats)
+    dms = float(_np.median(drep))
 
     def dpstep(i, evs):
         l = i % R
@@ -395,7 +395,7 @@ def bench_single_layer(args, name):
         n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms, 5),
         us_per_layer=round(ms * 1e3, 2),
-        repeats=spread(reps),
+        repeats=spread(srep),
         us_per_layer_graph=round(graph_ms * 1e3, 2) if graph_ms else None,
         hbm_frac=round(ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         higher_is_better=True, scaling="weak", vs_baseline=None,
@@ -414,7 +414,7 @@ def bench_single_layer(args, name):
                             speedup_vs_dense=round(dms / tms, 3)),
         geglu=dict(us_per_layer=round(gms * 1e3, 2),
                    GBps=round(ab["total"] / (gms * 1e-3) / 1e9, 1)),
-        dense=dict(us_per_layer=round(dms * 1e3, 2), repeats=spread(dreps),
+        dense=dict(us_per_layer=round(dms * 1e3, 2), repeats=spread(drep),
                    GBps=round(3 * cfg.d_model * cfg.d_ff * 2 / (dms * 1e-3) / 1e9, 1),
                    kernels=dict(upgate_us=round(dkms[0] * 1e3, 2),
                                 down_us=round(dkms[1] * 1e3, 2))),
