@@ -23,9 +23,11 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, incremental: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False, extra_flags=()) -> str:
     """Compile every source (incremental: only those whose object is older
-    than the source or a header) and link libprox.so."""
+    than the source or a header) and link libprox.so.  extra_flags go on
+    every compile and on the link line (the CPU sanitizer run passes
+    -Xarch_host -fsanitize=... here)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     os.makedirs(OBJDIR, exist_ok=True)
     headers = [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")]
@@ -38,7 +40,7 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
             t = os.path.getmtime(obj)
             if t > os.path.getmtime(os.path.join(CSRC, src)) and t > newest_hdr:
                 return obj
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", "-o", obj, os.path.join(CSRC, src)]
+        cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-c", "-o", obj, os.path.join(CSRC, src)]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         subprocess.check_call(cmd)
@@ -47,10 +49,15 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *extra_flags,
+                           "-o", tmp, *objs])
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, incremental="-i" in sys.argv))
+    # python build.py [-i] [--sanitize]: --sanitize builds the host code with
+    # AddressSanitizer and UndefinedBehaviorSanitizer (device code untouched).
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer"] if "--sanitize" in sys.argv else []
+    print(build(verbose=True, incremental="-i" in sys.argv, extra_flags=san))

@@ -39,12 +39,14 @@ _LIB = os.path.join(_HERE, "libprox_oracle.so")
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile prox_oracle.c with gcc (IEEE arithmetic: no fast-math)."""
+def build(force: bool = False, cc: str = "gcc", extra_flags=()) -> str:
+    """Compile prox_oracle.c (IEEE arithmetic: no fast-math, no contraction).
+    cc / extra_flags let the CPU sanitizer run build it with clang and
+    -fsanitize=address,undefined."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+            [cc, "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", *extra_flags,
              "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
