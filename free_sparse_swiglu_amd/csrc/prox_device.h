@@ -89,10 +89,37 @@ __device__ __forceinline__ float xsum_strided(const float *p, int n, size_t stri
   return acc;
 }
 
+// Wait until this wave's vector memory operations are complete (loads
+// returned, stores acknowledged, direct-to-LDS loads landed).  It is the
+// compiler's own instruction, so the compiler's wait bookkeeping learns that
+// the direct-to-LDS loads have landed; after an opaque asm wait it would
+// still count them as pending and make later barriers wait for every
+// outstanding store again.  The empty asm statements keep memory accesses
+// from moving across it.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited for
+  asm volatile("" ::: "memory");
+}
+
+// Counts this work-group's arrival at *cnt (after its own stores have
+// completed) and returns true in every thread of the last of `total` to
+// arrive.  The counter is left at `total` (for waiters that poll it); the
+// caller resets it later.
+__device__ __forceinline__ bool arrive_count(unsigned *cnt, unsigned total, int *s_flag) {
+  wait_vmem();      // own partial stores done
+  __syncthreads();  // ... in every wave
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              total - 1u;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 // Returns true in every thread of the last work-group to arrive at *cnt
 // (of `total`), which also resets the counter for the next launch.
 __device__ __forceinline__ bool arrive_last(unsigned *cnt, unsigned total, int *s_flag) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own partial stores done
+  wait_vmem();  // own partial stores done
   __syncthreads();                                   // ... in every wave
   if (threadIdx.x == 0) {
     const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,

@@ -85,13 +85,13 @@ struct FusedArgs {
   void *y;
   float *resid;
   float *part;
-  unsigned *tile_cnt;
   float *sabs;
   float *sdense;    // [d_ff] exact s of each kept channel (others stale)
   float *ypart;
   unsigned *col_cnt;
   unsigned *sync;
-  unsigned *tflag;  // per P1 tile: |s~| written (word t * kSyncStride)
+  unsigned *tflag;  // per P1 tile t, on line t: word t * kSyncStride = |s~| written,
+                    // the next word = chunks arrived (stays at nchunk until the exit reset)
   unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
   unsigned *gmask;  // [n_p3][4] per P3 item: 64-bit masks of the channels above bin b*
                     // and of those in it (low word first)
@@ -168,6 +168,7 @@ struct P2Smem {
 struct P3Smem {
   u4 x[2048];  // x when d_model * element size <= 32 KB
   float ured[2 * kP3Ch];  // dot product of each unit (row) of the item
+  unsigned key[kP3Ch];    // |s~| bits of the item's channels
   unsigned lo, bstar;
 };
 // P4 rows (bf16, 512 bytes each) taken straight into LDS ahead of the wait,
@@ -216,6 +217,15 @@ __shared__ FusedShared<SEL> g_fs;
 template <bool SEL>
 __device__ __forceinline__ void stamp_wait(const FusedArgs &a) {
   if (a.trace) g_fs<SEL>.twait = __builtin_amdgcn_s_memrealtime();
+}
+
+// |s~| of tile column col from the tile's partial sums (nchunk chunks of
+// [256 up | 256 gate] floats), added in chunk order.  The tile epilogue and
+// the P3 items both call this, so they get the same bits.
+__device__ __forceinline__ float tile_key(const float *tp, int col, int nchunk, int act) {
+  const float u = xsum_strided(&tp[col], nchunk, 512);
+  const float g = xsum_strided(&tp[256 + col], nchunk, 512);
+  return fabsf(u * gate_act(g, act));
 }
 
 // ---------------------------------------------------------------------------
@@ -360,7 +370,9 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
     for (int q = 1; q < kFW; ++q) v += sm.red[q][e];
     xstore(&part[e], v);
   }
-  if (!arrive_last(&a.tile_cnt[t], (unsigned)a.nchunk, s_flag)) return;
+  // The tile's counter stays at nchunk once every chunk is in: P3 items wait
+  // on it (the exit reset clears it).
+  if (!arrive_count(&a.tflag[t * kSyncStride + 1], (unsigned)a.nchunk, s_flag)) return;
   __builtin_amdgcn_s_setprio(3);  // the tile epilogue gates the select and P3: issue first
 
   // Tile epilogue: |s~| = |u~ * SiLU(g~)| of the tile's 256 channels, and the
@@ -372,11 +384,9 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
   const float *tp = a.part + (size_t)t * a.nchunk * 512;
   if (threadIdx.x < 256) {
     const int col = threadIdx.x;
-    const float u = xsum_strided(&tp[col], a.nchunk, 512);
-    const float gg = xsum_strided(&tp[256 + col], a.nchunk, 512);
+    const float v = tile_key(tp, col, a.nchunk, a.act);
     const int j = t * kTile + col;
     if (j < a.d_ff) {
-      const float v = fabsf(u * gate_act(gg, a.act));
       xstore(&a.sabs[j], v);
       if (!a.ts_mode) atomicAdd(&h[__float_as_uint(v) >> 20], 1u);
     }
@@ -388,7 +398,7 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
       if (c) __hip_atomic_fetch_add(&a.ghist[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
     xstore_u(&a.tflag[t * kSyncStride], 1u);
@@ -529,7 +539,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
   if (!pre)
     for (int i = tid; i < 2048; i += kFT) sm.h[i] = xload_u(&a.ghist[i]);
   for (int i = tid; i < kGroups; i += kFT) sm.ceq[i] = 0u;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // what went straight into LDS, too
+  wait_vmem();  // what went straight into LDS, too
   // The histogram is in LDS and nothing else reads it: clear it for the next
   // launch here rather than at the exit.
   for (int i = tid; i < 2048; i += kFT) xstore_u(&a.ghist[i], 0u);
@@ -557,7 +567,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rk, (__attribute__((address_space(3))) void *)&sm.keys[m * kFT + wu * 64], 4,
             (uint32_t)tid * 4u, (uint32_t)((e0 + m) * kFT) * 4u, 0, kSelBits);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmem();
     }
     // Each thread marks its candidate slots in a bit mask (all LDS reads in
     // flight at once, no branches); one wave scan places them.
@@ -841,7 +851,11 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
     unsigned lo = 0u;
     const unsigned pb = a.ts_mode ? 0u : xload_u(a.pred);
     if (a.ts_mode || pb >= 2u) {
-      wait_geq(&a.tflag[(c0 / kTile) * kSyncStride], 1u, &a.sync[kSyncErr], a.wlim);
+      // every chunk of the item's Stage 1 tile has stored its partial sums
+      // (the item forms its keys from them, rather than waiting for the
+      // tile epilogue to publish them)
+      wait_geq(&a.tflag[(c0 / kTile) * kSyncStride + 1], (unsigned)a.nchunk, &a.sync[kSyncErr],
+               a.wlim);
       lo = pb >= 2u ? pb - 1u : 0u;
     } else {
       wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr], a.wlim);
@@ -856,7 +870,14 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
   const int n = a.d_ff;
   const int j = c0 + lane;
   const bool valid = lane < kP3Ch && j < n;
-  const unsigned key = __float_as_uint(xload(&a.sabs[min(j, n - 1)]));
+  // |s~| of the item's channels (the bits the tile epilogue stores in sabs),
+  // formed by wave 0 and shared through LDS
+  static_assert(kTile % kP3Ch == 0, "a P3 item lies in one Stage 1 tile");
+  if (wv == 0 && lane < kP3Ch)
+    sm.key[lane] = __float_as_uint(
+        tile_key(a.part + (size_t)(c0 / kTile) * a.nchunk * 512, (c0 % kTile) + lane, a.nchunk, a.act));
+  __syncthreads();
+  const unsigned key = sm.key[min(lane, kP3Ch - 1)];
   const unsigned d1 = key >> 20;
   // Two passes: the first set, then (top-k) what b* adds to it.  Each
   // computes s of the channels of the wave-uniform mask cm, stored by
@@ -907,7 +928,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
     xstore_u(&a.gmask[4 * item + 2], (unsigned)bm);
     xstore_u(&a.gmask[4 * item + 3], (unsigned)(bm >> 32));
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) xstore_u(&a.sync[kSyncP3 + item * kSyncStride], 1u);
 }
@@ -1055,7 +1076,7 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
     }
     if constexpr (ND > 0) {
       if (b0 == 0 && nr > NB0) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the LDS rows have landed
+        wait_vmem();  // the LDS rows have landed
 #pragma unroll 4
         for (int rr = NB0 + wv; rr < min(nr, NB0 + ND); rr += kFW) {
           const u2 w = sm.rows[rr - NB0][lane];
@@ -1184,7 +1205,10 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     // control words and P3 flags (consecutive lines), then the tile flags
     for (int i = threadIdx.x; i < kCtl + a.n_p3; i += kFT)
       if (i * kSyncStride != kSyncErr) xstore_u(&a.sync[i * kSyncStride], 0u);
-    for (int i = threadIdx.x; i < a.ntile; i += kFT) xstore_u(&a.tflag[i * kSyncStride], 0u);
+    for (int i = threadIdx.x; i < a.ntile; i += kFT) {
+      xstore_u(&a.tflag[i * kSyncStride], 0u);
+      xstore_u(&a.tflag[i * kSyncStride + 1], 0u);
+    }
     if (threadIdx.x == 0) xstore_u(&a.sync[kSyncSelect + 1], 0u);
   }
 }
@@ -1321,7 +1345,6 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
   a.y = y;
   a.resid = resid;
   a.part = b.part;
-  a.tile_cnt = b.tile_cnt;
   a.sabs = b.sabs;
   a.sdense = b.ssp;
   a.ypart = b.ypart;
