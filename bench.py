@@ -135,6 +135,28 @@ def build_ring(cfg, ring, max_batch=1, path=0, activation=0, batch_upgate=0, tau
     return layers, list(taus)
 
 
+def torch_dense_ms(cfg, X, steps, warmup, ring=4):
+    """The dense SwiGLU FFN step in plain PyTorch (torch.matmul on the bf16
+    weights in their x.W layout, i.e. the vendor BLAS, plus SiLU and the
+    product), over a ring of `ring` freshly generated layers: context for the
+    library's own dense path, not part of the product."""
+    import torch
+    from free_sparse_swiglu_amd import synth
+    W = [synth.make_layer(cfg, l, "cuda") for l in range(ring)]
+    nx = X[0].shape[0]
+
+    def step(i):
+        wu, wg, wd = W[i % ring]
+        x = X[i % len(X)][(i // ring) % nx][None]
+        u = torch.matmul(x, wu)
+        g = torch.matmul(x, wg)
+        torch.matmul(u * torch.nn.functional.silu(g), wd)
+    ms = time_loop(step, steps, warmup)
+    del W
+    torch.cuda.synchronize()
+    return ms
+
+
 def time_loop(fn, steps, warmup):
     import torch
     for i in range(warmup):
@@ -264,6 +286,7 @@ def bench_single_layer(args, name):
         prox.prox_dense_ffn_forward(layers[l], X[l][(i // R) % NX], y)
     drep = time_repeats(dstep, args.steps, args.warmup, args.repeats)
     dms = float(_np.median(drep))
+    tdms = torch_dense_ms(cfg, X, args.steps, args.warmup)
 
     def dpstep(i, evs):
         l = i % R
@@ -417,7 +440,8 @@ def bench_single_layer(args, name):
         dense=dict(us_per_layer=round(dms * 1e3, 2), repeats=spread(drep),
                    GBps=round(3 * cfg.d_model * cfg.d_ff * 2 / (dms * 1e-3) / 1e9, 1),
                    kernels=dict(upgate_us=round(dkms[0] * 1e3, 2),
-                                down_us=round(dkms[1] * 1e3, 2))),
+                                down_us=round(dkms[1] * 1e3, 2)),
+                   torch_matmul_us_per_layer=round(tdms * 1e3, 2)),
         speedup_vs_dense=round(dms / ms, 3),
         other_sparsities=others,
         roofline=roof,
