@@ -261,12 +261,16 @@ prox_status run_forward(const prox_layer *L, const void *x, int batch, float tau
   if ((e = prox::launch_proxy(p, b, x, batch, tau, s, dbg)) != hipSuccess)
     return hip_fail(e, "stage 1 proxy kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
-  // Several tokens: Stage 2 runs over the union, built from mask words, so
-  // the per-token lists are written only when asked for.
-  if ((e = prox::launch_topk(p, b, batch, k, batch == 1 || lists, s)) != hipSuccess)
+  // Several tokens: Stage 2 runs over the union of the tokens' masks, taken
+  // from their mask words by the Stage 2 kernels themselves (mode 3); the
+  // matrix-core up/gate form reads a union list (mode 1), which the top-k
+  // launch then builds, as it does for the debug entry.  The per-token lists
+  // are written only when asked for.
+  const int mode = batch == 1 ? 0 : (p.bf16 && p.batch_mfma ? 1 : 3);
+  if ((e = prox::launch_topk(p, b, batch, k, batch == 1 || lists, mode == 1 || lists, s)) !=
+      hipSuccess)
     return hip_fail(e, "top-k kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
-  const int mode = batch == 1 ? 0 : 1;  // several tokens: the top-k launch also built the union
   if ((e = prox::launch_upgate(p, b, x, batch, mode, k, s)) != hipSuccess)
     return hip_fail(e, "stage 2 up/gate kernel");
   if ((e = lg.mark(s)) != hipSuccess) return hip_fail(e, "event record");
@@ -505,13 +509,12 @@ prox_status prox_ffn_forward_debug(const prox_layer *layer, const void *x, int b
           (e = hipMemcpyAsync(dbg->union_idx, b.uni, (size_t)p.d_ff * 4,
                               hipMemcpyDeviceToDevice, s)) != hipSuccess)
         return hip_fail(e, "copy union");
-      // s is kept as [position][token] (row stride nbp): copy out token-major
-      const size_t nbp = (size_t)((batch + 3) & ~3);
-      for (int t = 0; t < batch && dbg->s_sel; ++t)
-        if ((e = hipMemcpy2DAsync((float *)dbg->s_sel + (size_t)t * p.d_ff, 4, b.ssp + t,
-                                  nbp * 4, 4, (size_t)p.d_ff, hipMemcpyDeviceToDevice, s)) !=
-            hipSuccess)
-          return hip_fail(e, "copy s");
+      // s is kept as [channel][token] (mode 3) or [union position][token]
+      // (mode 1), row stride nbp: copied out token-major by union position
+      if (dbg->s_sel &&
+          (e = prox::launch_union_s(p, b, batch, !(p.bf16 && p.batch_mfma), (float *)dbg->s_sel,
+                                    s)) != hipSuccess)
+        return hip_fail(e, "copy s");
     }
   }
   return PROX_OK;

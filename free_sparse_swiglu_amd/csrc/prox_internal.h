@@ -111,9 +111,14 @@ hipError_t launch_export_proxy(const Plan &p, const Bufs &b, int matrix,
 // slice (the m_x decision it took) into b.drows / b.dcnt.
 hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
                         float tau, hipStream_t s, bool dbg = false);
+// lists: the per-token lists (sel); union_list (several tokens): the union
+// list uni / nuni / umask, built by the last work-group (mode 1 of Stage 2
+// and the debug entry need it; mode 3 does not).
 hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
-                       hipStream_t s);
-// mode: 0 = one token over sel, 1 = batch over the union, 2 = dense
+                       bool union_list, hipStream_t s);
+// mode: 0 = one token over sel, 1 = batch over the union list, 2 = dense,
+// 3 = batch over the tokens' mask words (no union list; s by channel; the
+// VALU forms only)
 hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
                          int mode, int n, hipStream_t s);
 hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
@@ -122,6 +127,10 @@ hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
 // assembled into n1[batch] and the ascending idx[batch][d_model].
 hipError_t launch_survivors(const Plan &p, const Bufs &b, int batch, int *n1, int *idx,
                             hipStream_t s);
+// Debug: out[t][p] = s of token t at union entry p (0 past the union), from
+// b.ssp kept by channel (mode 3) or by union position (mode 1).
+hipError_t launch_union_s(const Plan &p, const Bufs &b, int batch, bool by_channel, float *out,
+                          hipStream_t s);
 // Copy the workspace status word to *out and clear it; after a timed-out
 // wait (bit 0) also reset the synchronisation block and the layer's cut guess.
 hipError_t launch_read_status(const Plan &p, const Bufs &b, int *out, hipStream_t s);

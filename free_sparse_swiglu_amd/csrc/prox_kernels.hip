@@ -824,7 +824,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
 // channel's up row and gate row are one contiguous run of 2*d_model elements
 // (channel-major layout), read 16 bytes per lane per step; x sits in LDS.
 // mode 0: position p -> channel sel[p] (one token); mode 1: channel uni[p],
-// s zeroed for tokens whose own mask lacks it; mode 2: dense, channel p.
+// s zeroed for tokens whose own mask lacks it; mode 2: dense, channel p;
+// mode 3 (several tokens): channel p if the union of the tokens' mask words
+// holds it (else skipped), s zeroed for tokens whose own mask lacks it and
+// stored by channel, so no union list is built.
 // Exact s of the selected channels: one token, ssp[p] for list position p;
 // NB >= 2 tokens, ssp[p * sstride(NB) + b], the tokens of a position side by
 // side (stride rounded up to 4 floats, so a row's values are whole 16-byte
@@ -841,7 +844,18 @@ struct UpGateArgs {
   const uint8_t *umask;
   float *ssp;
   int act;  // gate activation (gate_act)
+  const unsigned *selw;  // mode 3: [NB][ceil(d_ff / 32)] per-token mask words
 };
+
+// Tokens (bit b) whose mask words hold channel j (mode 3 of the Stage 2 kernels).
+template <int NB>
+__device__ __forceinline__ unsigned token_bits(const unsigned *selw, int d_ff, int j) {
+  const int words = (d_ff + 31) >> 5;
+  unsigned tok = 0u;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) tok |= ((selw[(size_t)b * words + (j >> 5)] >> (j & 31)) & 1u) << b;
+  return tok;
+}
 
 template <int NB, bool BF16, int MODE, int NWV>
 __global__ __launch_bounds__(NWV * 64) void upgate_kernel(UpGateArgs a) {
@@ -860,7 +874,12 @@ __global__ __launch_bounds__(NWV * 64) void upgate_kernel(UpGateArgs a) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wug, a.wug_bytes);
   const int W = gridDim.x * NWV;
   for (int p = blockIdx.x * NWV + wv; p < n; p += W) {
-    const int j = (MODE == 2) ? p : a.list[p];
+    unsigned tok = 0xffu;
+    if constexpr (MODE == 3) {
+      tok = token_bits<NB>(a.selw, a.d_ff, p);  // wave-uniform: p is
+      if (!tok) continue;
+    }
+    const int j = (MODE == 2 || MODE == 3) ? p : a.list[p];
     const uint32_t ubase = (uint32_t)j * 2u * (uint32_t)a.d_model * ESZ;
     const uint32_t gbase = ubase + (uint32_t)a.d_model * ESZ;
     float au[NB], ag[NB];
@@ -888,7 +907,6 @@ __global__ __launch_bounds__(NWV * 64) void upgate_kernel(UpGateArgs a) {
         }
       }
     }
-    unsigned tok = 0xffu;
     if (MODE == 1) tok = a.umask[p];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -967,7 +985,11 @@ struct DownArgs {
   unsigned *col_cnt;
   void *y;
   float *resid;
+  const unsigned *selw;  // mode 3: [NB][ceil(d_ff / 32)] per-token mask words
 };
+// Mode 3 of the down kernel: work-group row ranges of whole mask words, each
+// holding at most this many channels (its union list sits in LDS).
+constexpr int kDownLocal = 4096;
 
 // s of list position pc for NB tokens (zeros unless ok): one float for one
 // token, else whole 16-byte loads of the position's row of ssp.
@@ -998,13 +1020,50 @@ __global__ __launch_bounds__(NW * 64, NW == 16 ? 8 : 4) void down_kernel(DownArg
   constexpr int CPL = BF16 ? 8 : 4;      // columns per lane
   __shared__ float red[NW][NB][kDownCols];
   __shared__ int s_last;
+  // mode 3: this work-group's union channels, ascending
+  __shared__ uint16_t s_list[MODE == 3 ? kDownLocal : 1];
+  __shared__ unsigned wsum[NW];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cc = blockIdx.x, rc = blockIdx.y;
-  const int n = a.n_ptr ? *a.n_ptr : a.n;
-  const int R = (n + a.nrc - 1) / a.nrc;
-  const int p0 = rc * R;
-  const int p1 = min(n, p0 + R);
+  int p0, p1;  // list positions of this work-group
+  if constexpr (MODE == 3) {
+    // Channels [c0, c1), whole mask words: the union of the tokens' words,
+    // one word per thread, placed by a block scan of the popcounts.
+    // (c0 stays a multiple of 32; past d_ff the range is empty: c1 <= c0)
+    const int R = (((a.d_ff + a.nrc - 1) / a.nrc) + 31) & ~31;
+    const int c0 = rc * R, c1 = min(a.d_ff, c0 + R);
+    const int w = (c0 >> 5) + (int)threadIdx.x;
+    unsigned u = 0u;
+    if (w * 32 < c1) {
+      const int words = (a.d_ff + 31) >> 5;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) u |= a.selw[(size_t)b * words + w];
+      if (c1 - w * 32 < 32) u &= (1u << (c1 - w * 32)) - 1u;
+    }
+    unsigned tot;
+    unsigned pos = block_excl_scan<NW>((unsigned)__popc(u), wsum, tot);
+    while (u) {
+      const int bit = __builtin_ctz(u);
+      u &= u - 1u;
+      s_list[pos++] = (uint16_t)(w * 32 + bit);
+    }
+    __syncthreads();
+    p0 = 0;
+    p1 = (int)tot;
+  } else {
+    const int n = a.n_ptr ? *a.n_ptr : a.n;
+    const int R = (n + a.nrc - 1) / a.nrc;
+    p0 = rc * R;
+    p1 = min(n, p0 + R);
+  }
+  // channel of list position pp, and where its s is kept (by position, or by
+  // channel in mode 3)
+  auto row_of = [&](int pp) -> int {
+    if constexpr (MODE == 2) return pp;
+    else if constexpr (MODE == 3) return (int)s_list[pp];
+    else return a.list[pp];
+  };
   // this chunk's rows: [d_ff][256] elements starting at chunk cc
   const size_t chunk_bytes = (size_t)a.d_ff * kDownCols * ESZ;
   const __amdgpu_buffer_rsrc_t rs =
@@ -1032,7 +1091,7 @@ __global__ __launch_bounds__(NW * 64, NW == 16 ? 8 : 4) void down_kernel(DownArg
       for (int u = 0; u < U; ++u) {
         const int pp = pb + 2 * NW * u + h;
         const int ppc = pp < p1 ? pp : p0;
-        jn[u] = (MODE == 2) ? ppc : a.list[ppc];
+        jn[u] = row_of(ppc);
       }
     };
     const int pstart = p0 + 2 * wv;
@@ -1049,7 +1108,7 @@ __global__ __launch_bounds__(NW * 64, NW == 16 ? 8 : 4) void down_kernel(DownArg
         const int pp = p + 2 * NW * u + h;
         const bool ok = pp < p1;
         // unconditional loads of a valid slot, then select: no branch
-        load_s<NB>(a.ssp, ok ? pp : p0, ok, sv[u]);
+        load_s<NB>(a.ssp, MODE == 3 ? jn[u] : (ok ? pp : p0), ok, sv[u]);
       }
       fetch_j(p + STEP);  // past the end: clamped, valid, unused
       __builtin_amdgcn_sched_barrier(0);
@@ -1091,8 +1150,8 @@ __global__ __launch_bounds__(NW * 64, NW == 16 ? 8 : 4) void down_kernel(DownArg
         const int pp = p + NW * u;
         const bool ok = pp < p1;
         const int ppc = ok ? pp : p;
-        const int j = (MODE == 2) ? ppc : a.list[ppc];
-        load_s<NB>(a.ssp, ppc, ok, sv[u]);
+        const int j = row_of(ppc);
+        load_s<NB>(a.ssp, MODE == 3 ? j : ppc, ok, sv[u]);
         const uint32_t rowoff = (uint32_t)j * (uint32_t)(kDownCols * ESZ);
         const u4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, rowoff, kNT);
         wf[u][0] = __uint_as_float(w.x);
@@ -1280,23 +1339,25 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
 
 template <int PER>
 static void topk_launch(const Plan &p, const Bufs &b, int batch, int k, bool lists,
-                        hipStream_t s) {
-  // one token: the list only (it drives Stage 2); several: the mask words and
-  // their union (built by the last work-group), the lists only when asked for
+                        bool union_list, hipStream_t s) {
+  // one token: the list only (it drives Stage 2); several: the mask words,
+  // their union list (built by the last work-group) only when asked for, and
+  // the per-token lists only when asked for
   const bool several = batch > 1;
   topk_kernel<PER><<<batch, 1024, 0, s>>>(b.sabs, p.d_ff, k, lists ? b.sel : nullptr,
-                                          several ? b.selw : nullptr, several ? b.ucnt : nullptr,
+                                          several ? b.selw : nullptr,
+                                          several && union_list ? b.ucnt : nullptr,
                                           b.uni, b.nuni, b.umask);
 }
 
 hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
-                       hipStream_t s) {
+                       bool union_list, hipStream_t s) {
   const int per = (p.d_ff + 1023) / 1024;
-  if (per <= 1) topk_launch<1>(p, b, batch, k, lists, s);
-  else if (per <= 4) topk_launch<4>(p, b, batch, k, lists, s);
-  else if (per <= 8) topk_launch<8>(p, b, batch, k, lists, s);
-  else if (per <= 16) topk_launch<16>(p, b, batch, k, lists, s);
-  else if (per <= 32) topk_launch<32>(p, b, batch, k, lists, s);
+  if (per <= 1) topk_launch<1>(p, b, batch, k, lists, union_list, s);
+  else if (per <= 4) topk_launch<4>(p, b, batch, k, lists, union_list, s);
+  else if (per <= 8) topk_launch<8>(p, b, batch, k, lists, union_list, s);
+  else if (per <= 16) topk_launch<16>(p, b, batch, k, lists, union_list, s);
+  else if (per <= 32) topk_launch<32>(p, b, batch, k, lists, union_list, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -1441,9 +1502,11 @@ hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
                          int mode, int n, hipStream_t s) {
   UpGateArgs a{b.wug, (uint32_t)((size_t)p.d_ff * 2 * p.d_model * p.esz), x,
                p.d_model, p.d_ff, n, nullptr,
-               mode == 0 ? b.sel : b.uni, b.umask, b.ssp, p.act};
+               mode == 0 ? b.sel : b.uni, b.umask, b.ssp, p.act, b.selw};
   if (mode == 1) a.n_ptr = b.nuni;
-  const int maxn = (mode == 1) ? p.d_ff : n;
+  if (mode == 3) a.n = p.d_ff;
+  const int maxn = (mode == 1 || mode == 3) ? p.d_ff : a.n;
+  if (mode == 3 && (batch < 2 || (p.bf16 && p.batch_mfma))) return hipErrorInvalidValue;
   if (maxn <= 0) return hipSuccess;
   if (batch == 1 && mode != 1) {
     hipError_t e1 = hipSuccess;
@@ -1475,10 +1538,12 @@ hipError_t launch_upgate(const Plan &p, const Bufs &b, const void *x, int batch,
   if (p.bf16) {
     if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 0>(a, maxn, cap, lds, s))); }
     else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 1>(a, maxn, cap, lds, s))); }
+    else if (mode == 3) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 3>(a, maxn, cap, lds, s))); }
     else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, true, 2>(a, maxn, cap, lds, s))); }
   } else {
     if (mode == 0) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 0>(a, maxn, cap, lds, s))); }
     else if (mode == 1) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 1>(a, maxn, cap, lds, s))); }
+    else if (mode == 3) { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 3>(a, maxn, cap, lds, s))); }
     else { PROX_DISPATCH_NB(batch, (e = upgate_go<NB, false, 2>(a, maxn, cap, lds, s))); }
   }
   return e;
@@ -1500,8 +1565,10 @@ hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
   const int nrc = (mode == 2 && batch == 1) ? std::max(1, std::min(p.nrc, 256 / p.ncol)) : p.nrc;
   DownArgs a{b.wd, (uint32_t)((size_t)p.d_ff * p.d_model * p.esz), p.d_model,
              p.d_ff, n, nrc, nullptr, mode == 0 ? b.sel : b.uni, b.ssp,
-             b.ypart, b.col_cnt, y, resid};
+             b.ypart, b.col_cnt, y, resid, b.selw};
   if (mode == 1) a.n_ptr = b.nuni;
+  if (mode == 3 && (batch < 2 || (((p.d_ff + nrc - 1) / nrc + 31) & ~31) > kDownLocal))
+    return hipErrorInvalidValue;
   dim3 g(p.ncol, nrc);
   // Waves per work-group: 16 for one token (two for float32), else 8, so
   // that two work-groups fit a CU; float32 layers of 5..8 tokens take 4
@@ -1511,13 +1578,36 @@ hipError_t launch_down(const Plan &p, const Bufs &b, int batch, int mode, int n,
   if (p.bf16) {
     if (mode == 0) { PROX_DOWN(true, 0); }
     else if (mode == 1) { PROX_DOWN(true, 1); }
+    else if (mode == 3) { PROX_DOWN(true, 3); }
     else { PROX_DOWN(true, 2); }
   } else {
     if (mode == 0) { PROX_DOWN(false, 0); }
     else if (mode == 1) { PROX_DOWN(false, 1); }
+    else if (mode == 3) { PROX_DOWN(false, 3); }
     else { PROX_DOWN(false, 2); }
   }
 #undef PROX_DOWN
+  return hipGetLastError();
+}
+
+// Debug: s of the union list by position, token-major (out[t][p] = s of
+// token t at union entry p), from s kept by channel (mode 3) or by position.
+__global__ __launch_bounds__(256) void union_s_kernel(const float *ssp, int nbp, const int *uni,
+                                                      const int *nuni, int d_ff, int batch,
+                                                      int by_channel, float *out) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.y;
+  if (p >= d_ff || t >= batch) return;
+  const int nu = *nuni;
+  const int row = p < nu ? (by_channel ? uni[p] : p) : 0;
+  out[(size_t)t * d_ff + p] = p < nu ? ssp[(size_t)row * nbp + t] : 0.0f;
+}
+
+hipError_t launch_union_s(const Plan &p, const Bufs &b, int batch, bool by_channel, float *out,
+                          hipStream_t s) {
+  const dim3 g((p.d_ff + 255) / 256, batch);
+  union_s_kernel<<<g, 256, 0, s>>>(b.ssp, (batch + 3) & ~3, b.uni, b.nuni, p.d_ff, batch,
+                                   by_channel ? 1 : 0, out);
   return hipGetLastError();
 }
 
