@@ -1035,8 +1035,12 @@ __device__ __forceinline__ void load_s(const float *ssp, int pc, bool ok, float 
 template <int NB, bool BF16, int MODE, int NW>
 __global__ __launch_bounds__(NW * 64, NW == 16 ? 8 : 4) void down_kernel(DownArgs a) {
   // rows in flight per wave: float32 one row per load (16 bytes a lane);
-  // bfloat16 two rows per load (lanes 0-31 and 32-63, 16 bytes a lane)
-  constexpr int U = BF16 ? (NB > 6 ? 3 : NB > 4 ? 4 : NB != 2 ? 6 : 8) : 8;
+  // bfloat16 two rows per load (lanes 0-31 and 32-63, 16 bytes a lane).
+  // 3 and 4 tokens take 8 loads in the dense and mask-word modes (70B-shaped
+  // 4-token step 263 us against 272 with 6; 10 spills), 6 in the list modes,
+  // where 8 would spill.
+  constexpr int U = BF16 ? (NB > 6 ? 3 : NB > 4 ? 4 : NB == 2 ? 8 : NB == 1 ? 6 : MODE >= 2 ? 8 : 6)
+                         : 8;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int CPL = BF16 ? 8 : 4;      // columns per lane
   __shared__ float red[NW][NB][kDownCols];
