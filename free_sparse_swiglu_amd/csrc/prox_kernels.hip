@@ -409,40 +409,46 @@ __global__ __launch_bounds__(512) void retile_pq2_kernel(const uint8_t *pq, unsi
 // and the tile counter use kMfmaRows-row chunks).
 constexpr int kMfmaRows = 1024;
 
-template <int NB>
+// CH: rows per chunk, kMfmaRows or 2 * kMfmaRows (the latter for G a
+// multiple of 128, so that its groups' scales fit the same LDS).
+template <int NB, int CH>
 __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
-  constexpr int KS = 32;  // 32-row steps per chunk of kMfmaRows rows
+  constexpr int KS = CH / 32;  // 32-row steps per chunk
   constexpr int WIN = 16;  // steps of codes in flight per wave
-  __shared__ __attribute__((aligned(16))) uint16_t xs[NB][kMfmaRows];  // masked x (bf16 bits)
-  __shared__ float xk[NB][KS];                                         // its sum over each step
-  __shared__ float ss[kMfmaRows / 64][512];  // group scales of the chunk's groups (G >= 64)
+  constexpr int GMIN = CH == kMfmaRows ? 64 : 128;  // smallest group size served
+  constexpr int NGC = CH / GMIN;                     // groups a chunk can touch
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NB][CH];  // masked x (bf16 bits)
+  __shared__ float xk[NB][KS];                                  // its sum over each step
+  __shared__ float ss[NGC][512];  // group scales of the chunk's groups
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int chunk = blockIdx.x, t = blockIdx.y;
-  const int r0 = chunk * kMfmaRows;
+  const int r0 = chunk * CH;
   const int nks = min(KS, (a.d_model - r0) / 32);
   const int c0 = wv * 64;
   const int grp0 = r0 / a.G;
   const int ngc = (r0 + 32 * nks - 1) / a.G - grp0 + 1;  // groups the chunk touches
 
-  // Masked x of the chunk's rows per token and the group scales go out
-  // first; the first WIN steps of codes (16 bytes per lane per step) right
-  // behind them, so that the staging below waits only for its own loads.
-  // Each later step's codes are requested as a step is consumed.
+  // Masked x of the chunk's first 1024 rows per token and the group scales
+  // go out first; the first WIN steps of codes (16 bytes per lane per step)
+  // right behind them, so that the staging below waits only for its own
+  // loads.  Each later step's codes are requested as a step is consumed.
   const int i0 = threadIdx.x;
   float xv[2][NB];
+  auto load_x = [&](int half0) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // clamped loads, no branch: every load in flight at once
-      const int row = r0 + i0 + 512 * h;
-      const float v = ld_elem<true>(a.x, (size_t)b * a.d_model + min(row, a.d_model - 1));
-      xv[h][b] = row < a.d_model ? v : 0.0f;
-    }
-  constexpr int NGC = kMfmaRows / 64;
+      for (int b = 0; b < NB; ++b) {
+        // clamped loads, no branch: every load in flight at once
+        const int row = r0 + i0 + 512 * (half0 + h);
+        const float v = ld_elem<true>(a.x, (size_t)b * a.d_model + min(row, a.d_model - 1));
+        xv[h][b] = row < a.d_model ? v : 0.0f;
+      }
+  };
+  load_x(0);
   float sv[NGC];
 #pragma unroll
   for (int q = 0; q < NGC; ++q)
@@ -458,31 +464,38 @@ __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
     w[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, code_off(s), 0, kNT);
   // (kept ahead of the staging: the scheduler would sink them below it)
   __builtin_amdgcn_sched_barrier(0);
-  if (a.drows && t == 0) {
-    // the input mask this kernel applies, per token and 64-row slice
+  // Staging, 1024 rows at a time (the next rows' x loads go out once these
+  // are in LDS).
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row0 = r0 + 512 * h + 64 * wv;  // the wave's 64 rows
+  for (int half0 = 0; half0 < CH / 512; half0 += 2) {
+    if (half0 > 0) load_x(half0);
+    if (a.drows && t == 0) {
+      // the input mask this kernel applies, per token and 64-row slice
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint64_t mk = __ballot(fabsf(xv[h][b]) >= a.tau);
-        if (row0 < a.d_model)
-          export_slice(a.drows + (size_t)b * a.d_model, a.dcnt + (size_t)b * (a.d_model / 64),
-                       row0 / 64, mk);
+      for (int h = 0; h < 2; ++h) {
+        const int row0 = r0 + 512 * (half0 + h) + 64 * wv;  // the wave's 64 rows
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const uint64_t mk = __ballot(fabsf(xv[h][b]) >= a.tau);
+          if (row0 < a.d_model)
+            export_slice(a.drows + (size_t)b * a.d_model, a.dcnt + (size_t)b * (a.d_model / 64),
+                         row0 / 64, mk);
+        }
       }
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = i0 + 512 * (half0 + h);
+        float v = fabsf(xv[h][b]) >= a.tau ? xv[h][b] : 0.0f;
+        xs[b][i] = (uint16_t)(__float_as_uint(v) >> 16);
+        // sum over the 32 rows of this half-wave
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        if ((lane & 31) == 0) xk[b][i >> 5] = v;
+      }
   }
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float v = fabsf(xv[h][b]) >= a.tau ? xv[h][b] : 0.0f;
-      xs[b][i0 + 512 * h] = (uint16_t)(__float_as_uint(v) >> 16);
-      // sum over the 32 rows of this half-wave
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-      if ((lane & 31) == 0) xk[b][(i0 + 512 * h) >> 5] = v;
-    }
 #pragma unroll
   for (int q = 0; q < NGC; ++q)
     if (q < ngc) ss[q][i0] = sv[q];
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
   // rows.
   __syncthreads();  // every wave is done with the scales
   float (*red)[512] = ss;
-  static_assert(NB <= KS, "partials fit the scale array");
+  static_assert(NB <= NGC, "partials fit the scale array");
   if (m < NB) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1348,12 +1361,31 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
   // the VALU kernel is faster (it reads only the rows the union of the input
   // masks keeps, about 3/4 of them; measured at the 70B shape 54 against
   // 59 us, and 81 against 63 us at 4 tokens); 2 when the layer asks for the
-  // matrix-core form.  Its own grid: ceil(d_model / kMfmaRows) work-groups
-  // per tile.
+  // matrix-core form.  Its own grid: ceil(d_model / CH) work-groups
+  // per tile, CH = 2 * kMfmaRows rows when the 1024-row grid would take more
+  // than one round of the resident work-groups (two per CU) and the
+  // 2048-row grid still fills three quarters of one (70B shape: 448
+  // work-groups instead of 896), else kMfmaRows.
   if (p.proxy_mfma && b.pq2 && batch >= p.proxy_mfma) {
-    a.nchunk = (p.d_model + kMfmaRows - 1) / kMfmaRows;
+    static int cus = 0;
+    if (!cus) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    }
+    const int g1 = (p.d_model + kMfmaRows - 1) / kMfmaRows * p.ntile;
+    const int g2 = (p.d_model + 2 * kMfmaRows - 1) / (2 * kMfmaRows) * p.ntile;
+    const bool big = p.G % 128 == 0 && (2 * kMfmaRows) % p.G == 0 && g1 > 2 * cus &&
+                     4 * g2 >= 3 * 2 * cus;
+    const int ch = big ? 2 * kMfmaRows : kMfmaRows;
+    a.nchunk = (p.d_model + ch - 1) / ch;
     const dim3 gm(a.nchunk, p.ntile);
-    PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB><<<gm, 512, 0, s>>>(a)));
+    if (big) {
+      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, 2 * kMfmaRows><<<gm, 512, 0, s>>>(a)));
+    } else {
+      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, kMfmaRows><<<gm, 512, 0, s>>>(a)));
+    }
   } else if (p.bf16) {
     PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true><<<g, 512, 0, s>>>(a)));
   } else {
