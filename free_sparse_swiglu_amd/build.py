@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source additions.  Every atomic of the persistent kernel is issued by a
+# single lane, where the atomic optimizer's wave-wide scan only adds work.
+FILE_FLAGS = {"prox_fused.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def build(verbose: bool = False, incremental: bool = False, extra_flags=()) -> str:
@@ -40,7 +43,8 @@ def build(verbose: bool = False, incremental: bool = False, extra_flags=()) -> s
             t = os.path.getmtime(obj)
             if t > os.path.getmtime(os.path.join(CSRC, src)) and t > newest_hdr:
                 return obj
-        cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-c", "-o", obj, os.path.join(CSRC, src)]
+        cmd = [hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *extra_flags, "-c", "-o", obj,
+               os.path.join(CSRC, src)]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         subprocess.check_call(cmd)

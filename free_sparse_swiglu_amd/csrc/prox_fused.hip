@@ -37,9 +37,10 @@
 // the P3 items of its range); those are held by running work-groups, and P1 items wait
 // for nothing, so the schedule cannot deadlock.  Every wait is bounded.  Data
 // passed between work-groups goes through agent-coherent accesses
-// (xstore/xload, sc1 buffer loads); the last work-group to leave resets the
-// ticket and the flags for the next launch (the select clears the
-// histogram as soon as it has read it).
+// (xstore/xload, sc1 buffer loads).  The flags of consecutive launches
+// alternate between two halves of the sync words, each launch clearing the
+// half it does not use (the select clears the histogram as soon as it has
+// read it).
 #include <type_traits>
 
 #include "prox_device.h"
@@ -49,15 +50,25 @@ namespace prox {
 // Sync words at the start of the fused workspace block.  Each control word
 // and each P3 flag sits on its own 256-byte line (kSyncStride words), so that
 // polling one flag does not contend with the atomics on another.
+//
+// Every per-launch word comes twice, as two halves: words 0 (and 1) of its
+// line for launches of parity 0, words 2 (and 3) for parity 1.  A launch
+// works in the half of its parity, whose words are all zero when it starts,
+// and each of its work-groups clears a small share of the other half (the
+// previous launch's) as it leaves, rather than the last one resetting every
+// word on its way out.  The parity is bit 31 of the ticket count, which
+// the last draw of a launch resets with the bit flipped (and of a word of its
+// own, which the work-groups that start without a draw read).
 enum : int {
-  kSyncTicket = 0 * kSyncStride,  // next ticket
+  kSyncTicket = 0 * kSyncStride,  // ticket draws (bits 0..30) and the launch parity (bit 31)
   kSyncTiles = 1 * kSyncStride,   // P1 tiles finished
   kSyncSelect = 2 * kSyncStride,  // one 64-bit word: T (low), J + 1 (high; 0 until published);
-                                  // T, J again at +2, +3 (kept after the launch)
+                                  // T, J of the last top-k launch at +4, +5 (kept)
   kSyncInv = 3 * kSyncStride,     // in-kernel RMSNorm: bits of 1/rms(r) once known (0 before)
   kSyncErr = 4 * kSyncStride,     // sticky error bits (1: a wait timed out, 2: select fallback used)
   kSyncBin = 5 * kSyncStride,     // b* + 1 once published (0 before)
-  kSyncP3 = 6 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
+  kSyncPar = 6 * kSyncStride,     // the launch parity again (bit 31), read by the first items
+  kSyncP3 = 7 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
 };
 static_assert(kSyncErr == kFusedErrWord, "error word index");
 
@@ -91,7 +102,8 @@ struct FusedArgs {
   unsigned *col_cnt;
   unsigned *sync;
   unsigned *tflag;  // per P1 tile t, on line t: word t * kSyncStride = |s~| written,
-                    // the next word = chunks arrived (stays at nchunk until the exit reset)
+                    // the next word = chunks arrived (stays at nchunk); offset by the
+                    // launch's half
   unsigned *ghist;  // [2048] digit-1 histogram of |s~| (zero between launches)
   unsigned *gmask;  // [n_p3][4] per P3 item: 64-bit masks of the channels above bin b*
                     // and of those in it (low word first)
@@ -194,6 +206,7 @@ struct P4Smem {
 // 80 KB union would need an address register wherever it is used.
 template <bool SEL>
 struct FusedShared {
+  unsigned hw;  // word offset of the launch's half in each sync line: 2 x parity
   // wave partial sums of the RMSNorm reduction (block_inv_rms); a work-group
   // of kRmsThreads, like the standalone RMSNorm kernel, gives the same bits
   float rms_part[kFW];
@@ -201,6 +214,7 @@ struct FusedShared {
   // ended (thread 0 only; 100 MHz s_memrealtime clock)
   unsigned long long twait;
   int ticket, flag;
+  float inv;  // in-kernel RMSNorm: 1/rms(r) of the first Stage 1 item, until published
   union {
     P1Smem p1;
     P2Smem<SEL> p2;
@@ -233,8 +247,35 @@ __device__ __forceinline__ float tile_key(const float *tp, int col, int nchunk, 
 // (see there): one wave per 64-row slice, survivors by ballot, nibble pairs
 // decoded under the bf16 exponent byte for bf16 layers.
 // ---------------------------------------------------------------------------
+// Share `q` of `nq` of the words of half `hw` that a launch may set (the
+// other half of the running launch: the previous launch used it and the next
+// one will): the control words, the P3 flags, the tile flags.
+constexpr int kMaxP3Items = kMaxDff / kP3Ch;
+constexpr int kMaxTiles = kMaxDff / kTile;
+constexpr int kHalfWords = 5 + kMaxP3Items + 2 * kMaxTiles;
+__device__ __forceinline__ void clear_half_share(const FusedArgs &a, unsigned hw, int q, int nq) {
+  const int per = (kHalfWords + nq - 1) / nq;
+  for (int i = threadIdx.x; i < per; i += kFT) {
+    const int e = q * per + i;
+    if (e >= kHalfWords) break;
+    unsigned *w;
+    if (e < 5)
+      w = &a.sync[e == 0 ? kSyncTiles : e == 1 ? kSyncSelect : e == 2 ? kSyncSelect + 1
+                                      : e == 3 ? kSyncInv : kSyncBin];
+    else if (e < 5 + kMaxP3Items)
+      w = &a.sync[kSyncP3 + (e - 5) * kSyncStride];
+    else
+      w = &a.tflag[((e - 5 - kMaxP3Items) >> 1) * kSyncStride + ((e - 5 - kMaxP3Items) & 1)];
+    xstore_u(w + hw, 0u);
+  }
+}
+
+// The half of the launch is known by the partial-sum barrier: from the parity
+// word `pw` that the work-group loaded as its first item started (`resolve`;
+// the load is waited for only here) or from an earlier draw.
 template <bool BF16, bool NORM, bool SEL>
-__device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag) {
+__device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag,
+                                        unsigned pw, bool resolve) {
   constexpr int U = 16;
   const int chunk = item % a.nchunk, t = item / a.nchunk;
   const int lane = threadIdx.x & 63;
@@ -251,7 +292,8 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
     rv = a.rnorm[min(chunk * kFT + (int)threadIdx.x, a.d_model - 1)];
     inv = block_inv_rms<kFT>(a.rnorm, a.d_model, a.eps, g_fs<SEL>.rms_part);
     // for the Stage 2 items, which scale r by it without reducing again
-    if (item == 0 && threadIdx.x == 0) xstore_u(&a.sync[kSyncInv], __float_as_uint(inv));
+    // (published at the partial-sum barrier, where the half is known)
+    if (item == 0 && threadIdx.x == 0) g_fs<SEL>.inv = inv;
   }
   if (sl < nsl) {
     // the slice's scales first, so that their latency hides behind the rest
@@ -361,7 +403,11 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
   float4 *rp = (float4 *)&sm.red[wv][lane * 8];
   rp[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   rp[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (resolve && threadIdx.x == 0) g_fs<SEL>.hw = (pw >> 31) * 2u;
   __syncthreads();
+  const unsigned hw = g_fs<SEL>.hw;
+  if (NORM && item == 0 && threadIdx.x == 0)
+    xstore_u(&a.sync[kSyncInv + hw], __float_as_uint(g_fs<SEL>.inv));
   float *part = a.part + ((size_t)t * a.nchunk + chunk) * 512;
   {
     const int e = threadIdx.x;
@@ -371,8 +417,8 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
     xstore(&part[e], v);
   }
   // The tile's counter stays at nchunk once every chunk is in: P3 items wait
-  // on it (the exit reset clears it).
-  if (!arrive_count(&a.tflag[t * kSyncStride + 1], (unsigned)a.nchunk, s_flag)) return;
+  // on it (until the half is cleared for its next use).
+  if (!arrive_count(&a.tflag[t * kSyncStride + hw + 1], (unsigned)a.nchunk, s_flag)) return;
   __builtin_amdgcn_s_setprio(3);  // the tile epilogue gates the select and P3: issue first
 
   // Tile epilogue: |s~| = |u~ * SiLU(g~)| of the tile's 256 channels, and the
@@ -401,8 +447,8 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
   wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    xstore_u(&a.tflag[t * kSyncStride], 1u);
-    __hip_atomic_fetch_add(&a.sync[kSyncTiles], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    xstore_u(&a.tflag[t * kSyncStride + hw], 1u);
+    __hip_atomic_fetch_add(&a.sync[kSyncTiles + hw], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -468,6 +514,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
   const int n = a.d_ff;
   const int per = (n + kFT - 1) / kFT;
   const unsigned k = (unsigned)a.k;
+  const unsigned hw = g_fs<SEL>.hw;
   // Keys in flight before the last tile is done: when every key fits the
   // LDS array (per <= kPreSlots) and every tile flag one lane (ntile <= 64),
   // each wave polls all tile flags at once and, slot by slot, copies the keys
@@ -480,7 +527,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.sabs, (uint32_t)n * 4u);
     const uint32_t koff = (uint32_t)tid * 4u;
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    const unsigned *fl = &a.tflag[min(lane, a.ntile - 1) * kSyncStride];
+    const unsigned *fl = &a.tflag[min(lane, a.ntile - 1) * kSyncStride + hw];
     uint64_t done = 0ull;  // tiles seen done (bit t), wave-uniform
     unsigned spins = 0;
 #pragma unroll 1
@@ -523,7 +570,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
           rh, (__attribute__((address_space(3))) void *)&sm.h[q * kFT + wu * 64], 4, koff,
           (uint32_t)(q * kFT) * 4u, 0, kSelBits);
   } else if (threadIdx.x == 0) {
-    wait_geq(&a.sync[kSyncTiles], (unsigned)a.ntile, &a.sync[kSyncErr], a.wlim);
+    wait_geq(&a.sync[kSyncTiles + hw], (unsigned)a.ntile, &a.sync[kSyncErr], a.wlim);
   }
   if (threadIdx.x == 0) stamp_wait<SEL>(a);
   __syncthreads();
@@ -550,7 +597,7 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
   const unsigned bstar = sm.misc[2];
   unsigned kk = sm.misc[3];
   if (tid == 0) {
-    xstore_u(&a.sync[kSyncBin], bstar + 1u);
+    xstore_u(&a.sync[kSyncBin + hw], bstar + 1u);
     xstore_u(a.pred, bstar + 1u);  // the next call's guess of the cut bin
   }
   unsigned T;
@@ -717,9 +764,9 @@ __device__ __forceinline__ void p2_select(const FusedArgs &a, P2Smem<SEL> &sm) {
     // earlier store to land first.
     if (lane == 0) {
       // a copy that outlives the launch's reset, for the list kernel
-      xstore_u(&a.sync[kSyncSelect + 2], T);
-      xstore_u(&a.sync[kSyncSelect + 3], (unsigned)J);
-      xstore_tj(&a.sync[kSyncSelect], T, J);
+      xstore_u(&a.sync[kSyncSelect + 4], T);
+      xstore_u(&a.sync[kSyncSelect + 5], (unsigned)J);
+      xstore_tj(&a.sync[kSyncSelect + hw], T, J);
     }
   }
   __builtin_amdgcn_s_setprio(0);
@@ -789,6 +836,10 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int i, int lane) {
 
 template <bool BF16, bool NORM, bool SEL>
 __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm) {
+  const unsigned hw = g_fs<SEL>.hw;
+  // every launch has P3 items: they clear the other half between them (off
+  // the Stage 1 chains, and long before the item's own flag)
+  clear_half_share(a, hw ^ 2u, item, a.n_p3);
   const int c0 = item * kP3Ch;
   // x to LDS when it fits (every item reads it, so it is L2-resident), before
   // the wait: it does not depend on Stage 1.
@@ -809,11 +860,11 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
 #pragma unroll
         for (int q = 0; q < EPS16; ++q) r0[q] = a.rnorm[(size_t)i0 * EPS16 + q];
       }
-      unsigned ib = xload_u(&a.sync[kSyncInv]);
+      unsigned ib = xload_u(&a.sync[kSyncInv + hw]);
       if (__syncthreads_or(ib == 0u)) {
-        if (threadIdx.x == 0) wait_geq(&a.sync[kSyncInv], 1u, &a.sync[kSyncErr], a.wlim);
+        if (threadIdx.x == 0) wait_geq(&a.sync[kSyncInv + hw], 1u, &a.sync[kSyncErr], a.wlim);
         __syncthreads();
-        ib = xload_u(&a.sync[kSyncInv]);
+        ib = xload_u(&a.sync[kSyncInv + hw]);
       }
       const float inv = __uint_as_float(ib);
       auto put = [&](int i, const float *r) {
@@ -854,12 +905,12 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
       // every chunk of the item's Stage 1 tile has stored its partial sums
       // (the item forms its keys from them, rather than waiting for the
       // tile epilogue to publish them)
-      wait_geq(&a.tflag[(c0 / kTile) * kSyncStride + 1], (unsigned)a.nchunk, &a.sync[kSyncErr],
+      wait_geq(&a.tflag[(c0 / kTile) * kSyncStride + hw + 1], (unsigned)a.nchunk, &a.sync[kSyncErr],
                a.wlim);
       lo = pb >= 2u ? pb - 1u : 0u;
     } else {
-      wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr], a.wlim);
-      lo = xload_u(&a.sync[kSyncBin]) - 1u;
+      wait_geq(&a.sync[kSyncBin + hw], 1u, &a.sync[kSyncErr], a.wlim);
+      lo = xload_u(&a.sync[kSyncBin + hw]) - 1u;
     }
     sm.lo = lo;
     stamp_wait<SEL>(a);
@@ -894,8 +945,8 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
       // and J (digit 1 = b*, computed before T is known so nothing here
       // waits for the select)
       if (threadIdx.x == 0) {
-        wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr], a.wlim);
-        sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
+        wait_geq(&a.sync[kSyncBin + hw], 1u, &a.sync[kSyncErr], a.wlim);
+        sm.bstar = xload_u(&a.sync[kSyncBin + hw]) - 1u;
       }
       __syncthreads();
       const unsigned bstar = sm.bstar;
@@ -930,7 +981,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
   }
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) xstore_u(&a.sync[kSyncP3 + item * kSyncStride], 1u);
+  if (threadIdx.x == 0) xstore_u(&a.sync[kSyncP3 + item * kSyncStride + hw], 1u);
 }
 
 // ---------------------------------------------------------------------------
@@ -943,6 +994,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
 // ---------------------------------------------------------------------------
 template <bool BF16, bool SEL>
 __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL> &sm, int *s_flag) {
+  const unsigned hw = g_fs<SEL>.hw;
   // rows per wave per batch: 10 rows x 512 B; 20 measured 0.5 us slower at 8B
   // (more bytes in flight behind which the dependent round trips queue)
   constexpr int U = BF16 ? 10 : 8;
@@ -961,11 +1013,11 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
     if (tid < 64) {
       constexpr int TPR = kP4Ch / kTile;  // tiles per range
       const int t0 = r * TPR, t1 = min(a.ntile, t0 + TPR) - 1;
-      wave_wait_flags(&a.tflag[min(t0 + lane, t1) * kSyncStride], &a.sync[kSyncErr], a.wlim);
+      wave_wait_flags(&a.tflag[min(t0 + lane, t1) * kSyncStride + hw], &a.sync[kSyncErr], a.wlim);
     }
   } else if (tid == 0) {
-    wait_geq(&a.sync[kSyncBin], 1u, &a.sync[kSyncErr], a.wlim);
-    sm.bstar = xload_u(&a.sync[kSyncBin]) - 1u;
+    wait_geq(&a.sync[kSyncBin + hw], 1u, &a.sync[kSyncErr], a.wlim);
+    sm.bstar = xload_u(&a.sync[kSyncBin + hw]) - 1u;
   }
   __syncthreads();
   {
@@ -1028,7 +1080,8 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   }
   if (tid < 64) {
     const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
-    wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride], &a.sync[kSyncErr], a.wlim);
+    wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride + hw], &a.sync[kSyncErr],
+                    a.wlim);
     if (lane == 0) stamp_wait<SEL>(a);
   }
   __syncthreads();
@@ -1038,7 +1091,8 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   {
     const float sj = tid < nr ? xload(&a.sdense[sm.rs[tid]]) : 0.0f;
     if (!a.ts_mode) {
-      if (tid == 0) wait_tj(&a.sync[kSyncSelect], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
+      if (tid == 0)
+        wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
       __syncthreads();
     }
     const unsigned T = a.ts_mode ? 0u : sm.tj[0];
@@ -1145,6 +1199,11 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
 // NORM: x = RMSNorm(a.rnorm) is formed inside (a separate instance, so the
 // plain forward keeps its register budget).  SEL: top-k (with the select
 // item) rather than the threshold mask.
+__device__ __forceinline__ unsigned draw_ticket(unsigned *ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
 template <bool BF16, bool NORM, bool SEL>
 __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) void ffn_fused_kernel(
     FusedArgs a) {
@@ -1154,16 +1213,37 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int total = a.n_p1 + a.n_p2 + a.n_p3 + a.n_p4;
   // The first min(grid, n_p1) tickets are the work-groups' own indices (all
   // work-groups of the grid are resident at once, see the launcher), which
-  // spares the launch burst on the ticket counter; the rest come from it.
+  // spares the launch burst on the ticket counter; the rest are drawn.  Every
+  // work-group stops at its first draw past the end, so a launch makes
+  // exactly total - nfirst + grid draws, and the last of them resets the
+  // count with the parity bit flipped for the next launch.
   const int nfirst = min((int)gridDim.x, a.n_p1);
+  const unsigned last_draw = (unsigned)(total - nfirst) + gridDim.x - 1u;
   bool first = (int)blockIdx.x < nfirst;
+  // On a work-group's first item thread 0 loads the parity word (used at the
+  // item's partial-sum barrier); later items learn the parity from their draw.
+  unsigned pw = 0u;
   for (;;) {
     __syncthreads();  // the previous item is done with the LDS
-    if (threadIdx.x == 0)
-      s_ticket = first ? (int)blockIdx.x
-                       : nfirst + (int)__hip_atomic_fetch_add(&a.sync[kSyncTicket], 1u,
-                                                              __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      int t;
+      if (first) {
+        t = (int)blockIdx.x;
+        pw = xload_u(&a.sync[kSyncPar]);
+      } else {
+        const unsigned raw = draw_ticket(&a.sync[kSyncTicket]);
+        const unsigned c = raw & 0x7fffffffu;
+        g_fs<SEL>.hw = (raw >> 31) * 2u;
+        if (c == last_draw) {
+          const unsigned next = ~raw & 0x80000000u;
+          xstore_u(&a.sync[kSyncPar], next);
+          xstore_u(&a.sync[kSyncTicket], next);
+        }
+        t = nfirst + (int)c;
+      }
+      s_ticket = t;
+    }
+    const bool resolve = first;  // the half arrives with the parity word
     first = false;
     __syncthreads();
     const int t = s_ticket;
@@ -1177,7 +1257,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     int r = t;
     if (r < a.n_p1) {
       phase = 1;
-      p1_item<BF16, NORM, SEL>(a, r, sm.p1, &s_flag);
+      p1_item<BF16, NORM, SEL>(a, r, sm.p1, &s_flag, pw, resolve);
     } else if ((r -= a.n_p1) < a.n_p2) {
       phase = 2;
       if constexpr (SEL) p2_select<SEL>(a, sm.p2);
@@ -1196,21 +1276,6 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       e[3] = (unsigned long long)blockIdx.x | ((unsigned long long)phase << 32);
     }
   }
-  // The last work-group out clears the ticket and the flags for the next
-  // launch (the select clears the histogram once it has read it).  Every work-group leaves on exactly one ticket >= total from
-  // the counter, so the counter itself says who is last: the one that drew
-  // ticket total + grid - 1 (no second atomic on the way out).
-  if ((unsigned)s_ticket == (unsigned)total + gridDim.x - 1u) {
-    constexpr int kCtl = kSyncP3 / kSyncStride;  // control words before the P3 flags
-    // control words and P3 flags (consecutive lines), then the tile flags
-    for (int i = threadIdx.x; i < kCtl + a.n_p3; i += kFT)
-      if (i * kSyncStride != kSyncErr) xstore_u(&a.sync[i * kSyncStride], 0u);
-    for (int i = threadIdx.x; i < a.ntile; i += kFT) {
-      xstore_u(&a.tflag[i * kSyncStride], 0u);
-      xstore_u(&a.tflag[i * kSyncStride + 1], 0u);
-    }
-    if (threadIdx.x == 0) xstore_u(&a.sync[kSyncSelect + 1], 0u);
-  }
 }
 
 // The ascending list of kept channels and their s, from the P3 masks, the
@@ -1224,8 +1289,8 @@ __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, 
   __shared__ unsigned base;
   if (threadIdx.x == 0) base = 0u;
   __syncthreads();
-  const unsigned T = tj[2];
-  const int J = (int)tj[3];
+  const unsigned T = tj[0];
+  const int J = (int)tj[1];
   for (int q0 = 0; q0 < n_p3; q0 += kFT) {
     const int q = q0 + (int)threadIdx.x;
     uint64_t m = 0ull;
@@ -1369,7 +1434,7 @@ hipError_t launch_fused(const Plan &p, const Bufs &b, const void *x, float tau, 
 hipError_t launch_fused_list(const Plan &p, const Bufs &b, int k, int *sel, float *ssel,
                              int *count, hipStream_t s) {
   const unsigned *gmask = b.sync + kGmaskWord;
-  fused_list_kernel<<<1, kFT, 0, s>>>(gmask, b.sync + kSyncSelect, b.sabs, b.ssp, fused_n_p3(p),
+  fused_list_kernel<<<1, kFT, 0, s>>>(gmask, b.sync + kSyncSelect + 4, b.sabs, b.ssp, fused_n_p3(p),
                                       p.d_ff, k, sel, ssel, count);
   return hipGetLastError();
 }

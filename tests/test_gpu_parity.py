@@ -457,8 +457,10 @@ def test_multi_kernel_path_parity(name):
 
 
 def test_fused_path_repeated_launches_are_identical():
-    """The persistent kernel resets its ticket and flags on exit: many
-    back-to-back launches on one stream give the same bits."""
+    """The persistent kernel alternates its flags between two halves of the
+    sync words (each launch clears the half it does not use, the last ticket
+    draw flips the parity): many back-to-back launches on one stream, an odd
+    and an even number, give the same bits."""
     case = get_case(RAGGED)
     k = synth.k_for(RAGGED.d_ff, 0.7)
     x = case.inputs(1, "repeat")[0].to(DEV)
