@@ -470,6 +470,42 @@ def test_fused_path_repeated_launches_are_identical():
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
 
 
+def test_fused_instances_alternate_halves_on_one_workspace():
+    """The persistent kernel keeps its per-launch sync words in two halves,
+    one per launch parity (the last ticket draw of a launch flips it), and
+    each launch clears the half it does not use.  Its top-k and threshold-mask
+    instances interleaved on one layer, in an irregular order and across a
+    status read, must give the bits of the same calls on a freshly prepared
+    layer (whose sync words are all zero, parity 0)."""
+    case = get_case(RAGGED)
+    W = [w.to(DEV) for w in synth.make_layer(RAGGED, 0, "cpu")]
+    L = prox.prox_prepare_layer(*W, RAGGED.group, 1)
+    Xc = synth.make_inputs(RAGGED, 4, "halves", 0, "cpu")
+    X = Xc.to(DEV)
+    k = synth.k_for(RAGGED.d_ff, 0.7)
+    tau = case.tau
+    tau_s = float(np.quantile(np.abs(oracle.forward(case.ol, Xc[0].float().numpy(), tau, 1)["s_t"]),
+                              0.7))
+    order = ["topk", "ts", "ts", "topk", "status", "topk", "ts", "topk", "topk", "ts"]
+    for i, op in enumerate(order):
+        if op == "status":
+            st = prox.prox_read_status(L)
+            torch.cuda.synchronize()
+            assert int(st[0]) == 0
+            continue
+        x = X[i % X.shape[0]]
+        fresh = prox.prox_prepare_layer(*W, RAGGED.group, 1)
+        if op == "topk":
+            y = prox.prox_ffn_forward(L, x, tau, k)
+            y0 = prox.prox_ffn_forward(fresh, x, tau, k)
+        else:
+            y = prox.prox_ffn_forward_ts(L, x, tau, tau_s)
+            y0 = prox.prox_ffn_forward_ts(fresh, x, tau, tau_s)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), f"call {i} ({op})"
+        del fresh
+
+
 @pytest.mark.parametrize("name", ["ragged", "8b"])
 def test_fused_cut_guess_changes_no_bits(name):
     """A layer keeps the last call's b* as a guess of the next cut, only to
