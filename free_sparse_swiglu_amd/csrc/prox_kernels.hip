@@ -410,11 +410,15 @@ __global__ __launch_bounds__(512) void retile_pq2_kernel(const uint8_t *pq, unsi
 constexpr int kMfmaRows = 1024;
 
 // CH: rows per chunk, kMfmaRows or 2 * kMfmaRows (the latter for G a
-// multiple of 128, so that its groups' scales fit the same LDS).
-template <int NB, int CH>
-__global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
+// multiple of 128, so that its groups' scales fit the same LDS).  GS: G / 32
+// when G is known at compile time (4: G = 128), else 0; then the group ends
+// are fixed steps, and the first step of a group starts its MFMA sums from
+// zero instead of clearing them at the previous group's end.
+template <int NB, int CH, int GS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) void proxy_mfma_kernel(
+    ProxyArgs a) {
   constexpr int KS = CH / 32;  // 32-row steps per chunk
-  constexpr int WIN = 16;  // steps of codes in flight per wave
+  constexpr int WIN = 12;  // steps of codes in flight per wave (16 measured no faster)
   constexpr int GMIN = CH == kMfmaRows ? 64 : 128;  // smallest group size served
   constexpr int NGC = CH / GMIN;                     // groups a chunk can touch
   __shared__ __attribute__((aligned(16))) uint16_t xs[NB][CH];  // masked x (bf16 bits)
@@ -489,7 +493,9 @@ __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
       for (int b = 0; b < NB; ++b) {
         const int i = i0 + 512 * (half0 + h);
         float v = fabsf(xv[h][b]) >= a.tau ? xv[h][b] : 0.0f;
-        xs[b][i] = (uint16_t)(__float_as_uint(v) >> 16);
+        // K order of each 8-row block as the A operand holds it (rows 0, 2,
+        // 4, 6, 1, 3, 5, 7; see the decode below)
+        xs[b][(i & ~7) | ((i & 1) << 2) | ((i >> 1) & 3)] = (uint16_t)(__float_as_uint(v) >> 16);
         // sum over the 32 rows of this half-wave
 #pragma unroll
         for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -510,39 +516,51 @@ __global__ __launch_bounds__(512) void proxy_mfma_kernel(ProxyArgs a) {
     acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     d[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  uint32_t nib_mask;
+  uint32_t nib_mask, c43;
   asm volatile("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(nib_mask));
+  asm volatile("s_mov_b32 %0, 0x43434343" : "=s"(c43));
   float xg = 0.0f;  // sum of this lane's token's masked x over the current group
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const uint32_t wd[4] = {w[s % WIN].x, w[s % WIN].y, w[s % WIN].z, w[s % WIN].w};
     if (s + WIN < KS) w[s % WIN] = __builtin_amdgcn_raw_buffer_load_b128(rs, code_off(s + WIN), 0, kNT);
+    // (the bound also keeps the compiler from hoisting every group's scale
+    // reads to the top, which spilled registers)
     if (s < nks) {
       bf16x8_t B;
       __builtin_memcpy(&B, &xs[tok][32 * s + 8 * g], 16);
+      // a chunk starts on a group boundary (CH and r0 are multiples of G)
+      constexpr bool kNone = false;
+      const bool gbeg = GS ? (s % (GS ? GS : 1) == 0) : kNone;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        // lo holds the codes of rows 0, 2, 4, 6 of the 8-row word (one per
+        // byte), hi those of rows 1, 3, 5, 7; each bf16 is 128 + code, the
+        // code byte under the exponent byte 0x43, so one v_perm from
+        // (0x43434343, lo or hi) makes two of them.  The A operand's K order
+        // is therefore rows 0, 2, 4, 6, 1, 3, 5, 7, and x is staged in LDS in
+        // the same order.
         const uint32_t lo = wd[r] & nib_mask, hi = (wd[r] >> 4) & nib_mask;
-        uint32_t q[4];
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          q[qq] = __builtin_amdgcn_perm(hi, lo, (uint32_t)qq | 0x0c00u | ((uint32_t)(4 + qq) << 16) |
-                                                    0x0c000000u) |
-                  0x43004300u;
+        const uint32_t q[4] = {__builtin_amdgcn_perm(c43, lo, 0x04010400u),
+                               __builtin_amdgcn_perm(c43, lo, 0x04030402u),
+                               __builtin_amdgcn_perm(c43, hi, 0x04010400u),
+                               __builtin_amdgcn_perm(c43, hi, 0x04030402u)};
         bf16x8_t A;
         __builtin_memcpy(&A, q, 16);
-        d[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, d[r], 0, 0, 0);
+        d[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            A, B, gbeg ? f32x4_t{0.0f, 0.0f, 0.0f, 0.0f} : d[r], 0, 0, 0);
       }
       xg += xk[tok][s];
       const int row_end = r0 + 32 * (s + 1);
-      if (s == nks - 1 || row_end % a.G == 0) {
-        const int gi = (row_end - 1) / a.G - grp0;
+      const bool gend = GS ? ((s + 1) % (GS ? GS : 1) == 0) : (s == nks - 1 || row_end % a.G == 0);
+      if (gend) {
+        const int gi = GS ? s / (GS ? GS : 1) : (row_end - 1) / a.G - grp0;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             acc[r][i] += ss[gi][c0 + 16 * g + 4 * i + r] * (d[r][i] - 136.0f * xg);
-            d[r][i] = 0.0f;
+            if (!GS) d[r][i] = 0.0f;
           }
         xg = 0.0f;
       }
@@ -1381,10 +1399,15 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
     const int ch = big ? 2 * kMfmaRows : kMfmaRows;
     a.nchunk = (p.d_model + ch - 1) / ch;
     const dim3 gm(a.nchunk, p.ntile);
-    if (big) {
-      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, 2 * kMfmaRows><<<gm, 512, 0, s>>>(a)));
+    const bool g128 = p.G == 128;
+    if (big && g128) {
+      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, 2 * kMfmaRows, 4><<<gm, 512, 0, s>>>(a)));
+    } else if (big) {
+      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, 2 * kMfmaRows, 0><<<gm, 512, 0, s>>>(a)));
+    } else if (g128) {
+      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, kMfmaRows, 4><<<gm, 512, 0, s>>>(a)));
     } else {
-      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, kMfmaRows><<<gm, 512, 0, s>>>(a)));
+      PROX_DISPATCH_NB(batch, (proxy_mfma_kernel<NB, kMfmaRows, 0><<<gm, 512, 0, s>>>(a)));
     }
   } else if (p.bf16) {
     PROX_DISPATCH_NB(batch, (proxy_kernel<NB, true><<<g, 512, 0, s>>>(a)));
