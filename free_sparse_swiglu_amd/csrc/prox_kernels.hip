@@ -16,6 +16,8 @@
 // summation order).
 #include "prox_device.h"
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 namespace prox {
 
@@ -708,6 +710,17 @@ __device__ __forceinline__ void mask_union(const unsigned *selw, int d_ff, int n
   if (w == 0) *nuni = (int)total;
 }
 
+// f(std::integral_constant<int, 0>{}), ..., f(<N - 1>): a loop whose index
+// is a compile-time constant in the body.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // With several tokens (ucnt set) the last work-group to finish also builds
 // the union of the masks, so top-k and union are one launch.
 template <int PER>
@@ -781,15 +794,25 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
 
   // No list wanted and every key equal to T kept (h3 counts the keys equal
   // to T): the mask is key >= T, written as bit words only.
+  // The mask words of this wave's channels: slot e's 64 channels are words
+  // 32 e + 2 w and 32 e + 2 w + 1, gathered into lanes 2 e and 2 e + 1 and
+  // written by one store (a store per word cost 4 us of issue on this CU).
+  unsigned mw = 0u;
+  auto put_words = [&](auto e, uint64_t km) {
+    constexpr int l0 = 2 * decltype(e)::value;
+    mw = lane == l0 ? (unsigned)km : mw;
+    mw = lane == l0 + 1 ? (unsigned)(km >> 32) : mw;
+  };
+  auto store_words = [&]() {
+    const int wi = (lane >> 1) * 32 + w * 2 + (lane & 1);
+    if (lane < 2 * PER && wi < words) xstore_u(&outw[wi], mw);
+  };
   if (!sel && outw && kk == h3[s_bin]) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int j = e * 1024 + tid;
-      const uint64_t km = __ballot(j < d_ff && key[e] >= T);
-      const int wi = e * 32 + w * 2;
-      if (lane == 0 && wi < words) xstore_u(&outw[wi], (unsigned)km);
-      if (lane == 1 && wi + 1 < words) xstore_u(&outw[wi + 1], (unsigned)(km >> 32));
-    }
+    static_for<PER>([&](auto e) {
+      const int j = decltype(e)::value * 1024 + tid;
+      put_words(e, __ballot(j < d_ff && key[decltype(e)::value] >= T));
+    });
+    store_words();
   } else {
 
     // Compaction.  Pass A: per (slot, wave) counts of keys > T and == T.
@@ -824,23 +847,18 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
     // Pass B: positions.  Before this key: gt_b keys > T and eq_b keys == T;
     // it is kept if > T, or == T with eq_b < kk; its position is gt_b + min(eq_b, kk).
     const uint64_t below = (1ull << lane) - 1ull;
-  #pragma unroll
-    for (int e = 0; e < PER; ++e) {
+    static_for<PER>([&](auto ec) {
+      constexpr int e = decltype(ec)::value;
       const int j = e * 1024 + tid;
       const unsigned base = cnt[e * 16 + w];
       const unsigned gt_b = (base & 0xffffu) + (unsigned)__popcll(mgt[e] & below);
       const unsigned eq_b = (base >> 16) + (unsigned)__popcll(meq[e] & below);
       const bool kept = j < d_ff && (key[e] > T || (key[e] == T && eq_b < kk));
       if (kept && out) out[key[e] > T ? gt_b + min(eq_b, kk) : gt_b + eq_b] = j;
-      // The same mask as bit words: this wave's 64 channels are words
-      // 32 e + 2 w and 32 e + 2 w + 1.
-      if (outw) {
-        const uint64_t km = __ballot(kept);
-        const int wi = e * 32 + w * 2;
-        if (lane == 0 && wi < words) xstore_u(&outw[wi], (unsigned)km);
-        if (lane == 1 && wi + 1 < words) xstore_u(&outw[wi + 1], (unsigned)(km >> 32));
-      }
-    }
+      // the same mask as bit words
+      if (outw) put_words(ec, __ballot(kept));
+    });
+    if (outw) store_words();
   }
   if (ucnt) {
     if (!arrive_last(ucnt, gridDim.x, &s_last)) return;
