@@ -746,10 +746,11 @@ def test_stage1_entry_matches_oracle():
 
 
 # ---------------------------------------------------------------------------
-# Matrix-core Stage 1 of several tokens at other group sizes and a d_model
-# whose last 1024-row chunk is partial (1536 = 1024 + 512)
+# Matrix-core Stage 1 of several tokens at three group sizes (128 has its own
+# instance with fixed group ends) and a d_model whose last 1024-row chunk is
+# partial (1536 = 1024 + 512)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("G", [64, 256])
+@pytest.mark.parametrize("G", [64, 128, 256])
 @pytest.mark.parametrize("B", [3, 8])
 def test_batch_stage1_mfma_group_sizes(G, B):
     cfg = synth.Config(f"mfma1536g{G}", 1536, 3000, G, "bf16", "student_t", 0.5, 32, (0.7,))
