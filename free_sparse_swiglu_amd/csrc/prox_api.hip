@@ -153,14 +153,13 @@ Plan make_plan(int d_model, int d_ff, int G, int bf16, int max_batch, int act,
   p.upgate_cap = 4096;
   p.use_fused = fused_supported(p) && ch.path == PROX_PATH_PERSISTENT;
   p.batch_mfma = ch.batch_upgate == PROX_FORM_MFMA;
-  // Stage 1 on the matrix cores: forced (from 2 tokens), or automatically
-  // from 3 tokens (measured faster there; at 2 the VALU kernel reads only
-  // the rows the union of the input masks keeps).
+  // Stage 1 of several tokens on the matrix cores unless the vector form is
+  // asked for (measured faster from 2 tokens, although at 2 the vector
+  // kernel reads only the rows the union of the input masks keeps: 8B 67.1
+  // against 69.5 us, 70B 182.6 against 183.5-187.1 us per 2-token step).
   const bool mfma_ok = bf16 && G % 64 == 0 && d_model % 32 == 0;
-  if (ch.batch_stage1 == PROX_FORM_MFMA && mfma_ok && max_batch >= 2)
+  if (ch.batch_stage1 != PROX_FORM_VALU && mfma_ok && max_batch >= 2)
     p.proxy_mfma = 2;
-  else if (ch.batch_stage1 == PROX_FORM_AUTO && mfma_ok && max_batch >= 3)
-    p.proxy_mfma = 3;
   else
     p.proxy_mfma = 0;
   p.wait_limit = kDefaultWaitLimit;

@@ -70,7 +70,7 @@ struct Plan {
   int use_fused;    // batch-1 forwards run the persistent fused kernel
   int act;          // gate activation: 0 SiLU, 1 GELU (tanh form)
   int batch_mfma;   // bf16 batches of 2..8 tokens: up/gate on MFMA (default: VALU dot2)
-  int proxy_mfma;   // bf16 batches of 3..8 tokens: Stage 1 on MFMA over pq2
+  int proxy_mfma;   // bf16 batches of 2..8 tokens: Stage 1 on MFMA over pq2 (0: VALU)
   unsigned wait_limit;  // polls before a bounded wait of the persistent kernel gives up
 };
 

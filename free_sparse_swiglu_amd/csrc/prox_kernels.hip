@@ -1393,11 +1393,10 @@ hipError_t launch_proxy(const Plan &p, const Bufs &b, const void *x, int batch,
               p.nchunk, b.part, b.tile_cnt, b.sabs, p.act,
               dbg ? b.drows : nullptr, dbg ? b.dcnt : nullptr};
   dim3 g(p.nchunk, p.ntile);
-  // On the matrix cores from p.proxy_mfma tokens: 3 by default, since at 2
-  // the VALU kernel is faster (it reads only the rows the union of the input
-  // masks keeps, about 3/4 of them; measured at the 70B shape 54 against
-  // 59 us, and 81 against 63 us at 4 tokens); 2 when the layer asks for the
-  // matrix-core form.  Its own grid: ceil(d_model / CH) work-groups
+  // On the matrix cores from p.proxy_mfma (2) tokens unless the layer asks
+  // for the vector form, which reads only the rows the union of the input
+  // masks keeps (about 3/4 of them at 2 tokens) but decodes and multiplies
+  // on the VALU.  Its own grid: ceil(d_model / CH) work-groups
   // per tile, CH = 2 * kMfmaRows rows when the 1024-row grid would take more
   // than one round of the resident work-groups (two per CU) and the
   // 2048-row grid still fills three quarters of one (70B shape: 448

@@ -67,7 +67,7 @@ typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
 typedef enum { PROX_PATH_PERSISTENT = 0, PROX_PATH_MULTI = 1 } prox_path;
 
 /* Arithmetic form of a batched (2..8 token) step: PROX_FORM_AUTO picks the
- * measured faster one (Stage 1: matrix cores from 3 tokens for bf16 layers
+ * measured faster one (Stage 1: matrix cores from 2 tokens for bf16 layers
  * whose G is a multiple of 64, else vector ALU; Stage 2 up/gate: vector ALU).
  * PROX_FORM_VALU / PROX_FORM_MFMA force one (MFMA: bf16 layers only).       */
 typedef enum { PROX_FORM_AUTO = 0, PROX_FORM_VALU = 1, PROX_FORM_MFMA = 2 } prox_form;

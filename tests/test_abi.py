@@ -140,13 +140,15 @@ def test_kernel_choices_are_declared_shape_fields(lib):
     assert _qs(prox.prox_shape(**f32, batch_stage1=prox.PROX_FORM_MFMA))[0] == \
         prox.PROX_EUNSUPPORTED
     # the matrix-core Stage 1 keeps a second copy of the codes: the automatic
-    # choice holds it from 3 tokens, the VALU form never
+    # choice holds it from 2 tokens, the VALU form never
     auto = _qs(prox.prox_shape(**base))[2]
     valu = _qs(prox.prox_shape(**base, batch_stage1=prox.PROX_FORM_VALU))[2]
     assert auto - valu >= 1024 * 2816 // 2
     two = dict(base, max_batch=2)
-    assert _qs(prox.prox_shape(**two))[2] == _qs(prox.prox_shape(**two, batch_stage1=1))[2]
-    assert _qs(prox.prox_shape(**two, batch_stage1=2))[2] > _qs(prox.prox_shape(**two))[2]
+    assert _qs(prox.prox_shape(**two))[2] == _qs(prox.prox_shape(**two, batch_stage1=2))[2]
+    assert _qs(prox.prox_shape(**two, batch_stage1=1))[2] < _qs(prox.prox_shape(**two))[2]
+    one = dict(base, max_batch=1)
+    assert _qs(prox.prox_shape(**one))[2] == _qs(prox.prox_shape(**one, batch_stage1=1))[2]
 
 
 def test_workspace_sync_block_is_shape_independent(lib):
