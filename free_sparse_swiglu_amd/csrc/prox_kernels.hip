@@ -884,10 +884,11 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
 __host__ __device__ constexpr int sstride(int nb) { return nb == 1 ? 1 : (nb + 3) & ~3; }
 
 // Channels per wave block of the mode-3 up/gate kernel: one at 2 tokens,
-// 8 from 3 tokens (measured 70B-shaped steps: 2 tokens 189 us with one
-// channel per block against 202 with 8; 8 tokens 325 against 335 us).  A
-// power of two up to 32, so a block lies in one mask word.
-__host__ __device__ constexpr int upgate_block(int nb) { return nb <= 2 ? 1 : 8; }
+// 4 at 3 and 4 tokens, 8 from 5 (measured 70B-shaped steps: 2 tokens 189 us
+// with one channel per block against 202 with 8; 4 tokens 246.4 us with 4
+// against 249.5 with 8 and 248.1 with 2; 8 tokens 310 with 8 against 314
+// with 4).  A power of two up to 32, so a block lies in one mask word.
+__host__ __device__ constexpr int upgate_block(int nb) { return nb <= 2 ? 1 : nb <= 4 ? 4 : 8; }
 
 struct UpGateArgs {
   const void *wug;
@@ -1449,11 +1450,16 @@ static void topk_launch(const Plan &p, const Bufs &b, int batch, int k, bool lis
 
 hipError_t launch_topk(const Plan &p, const Bufs &b, int batch, int k, bool lists,
                        bool union_list, hipStream_t s) {
+  // Key slots per thread: instances sized for the 8B (14) and 70B (28)
+  // widths, whose passes then walk no empty slot (70B 8-token top-k
+  // 16.8 -> 15.8 us against the 32-slot instance).
   const int per = (p.d_ff + 1023) / 1024;
   if (per <= 1) topk_launch<1>(p, b, batch, k, lists, union_list, s);
   else if (per <= 4) topk_launch<4>(p, b, batch, k, lists, union_list, s);
   else if (per <= 8) topk_launch<8>(p, b, batch, k, lists, union_list, s);
+  else if (per <= 14) topk_launch<14>(p, b, batch, k, lists, union_list, s);
   else if (per <= 16) topk_launch<16>(p, b, batch, k, lists, union_list, s);
+  else if (per <= 28) topk_launch<28>(p, b, batch, k, lists, union_list, s);
   else if (per <= 32) topk_launch<32>(p, b, batch, k, lists, union_list, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
