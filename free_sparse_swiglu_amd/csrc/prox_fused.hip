@@ -18,7 +18,7 @@
 //       bin b* (about twice as many as will be kept), so nothing waits for T.
 //       Once the layer has run a top-k call, an item does not wait for b*
 //       either: as soon as its Stage 1 tile is done it computes every channel
-//       from the previous call's b* up (a guess of the cut kept per layer),
+//       above the previous call's b* (a guess of the cut kept per layer),
 //       then, when b* is out, any channel of digit 1 >= b* that
 //       the guess missed.  The guess moves work earlier; it never changes
 //       which channels are kept or any value;
@@ -891,13 +891,17 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
     xs = sm.x;
   }
   // What to compute first.  Threshold: |s~| >= tau_s, once the item's Stage 1
-  // tile is done.  Top-k: every channel whose digit 1 is at least the b* of
-  // the layer's previous call (a guess of the cut, which moves little from
-  // token to token), also as soon as the tile is done, so Stage 2 overlaps the
-  // rest of Stage 1 and the select; once b* is out, whatever the guess missed
+  // tile is done.  Top-k: every channel whose digit 1 is above the b* of the
+  // layer's previous call (a guess of the cut, which moves little from token
+  // to token), also as soon as the tile is done, so Stage 2 overlaps the rest
+  // of Stage 1 and the select; once b* is out, whatever the guess missed
   // (digit 1 >= b*).  With no guess yet: digit 1 >= b*, after b*.  Only the
-  // timing depends on the guess, never the result.  (Starting one bin lower,
-  // to catch more of a falling cut, measured 0.3 us slower at 8B.)
+  // timing depends on the guess, never the result.  Measured at 8B against
+  // starting from the previous b* itself: one bin lower 0.3 us slower, one
+  // bin higher (this) 0.1 us faster, since a bin the cut has left is a whole
+  // bin of rows streamed for nothing, while the bin it reaches costs only a
+  // short second pass; a start from the previous k-th key (1/16 to 1/4 of an
+  // octave below it) was slower still.
   if (threadIdx.x == 0) {
     unsigned lo = 0u;
     const unsigned pb = a.ts_mode ? 0u : xload_u(a.pred);
@@ -907,7 +911,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
       // tile epilogue to publish them)
       wait_geq(&a.tflag[(c0 / kTile) * kSyncStride + hw + 1], (unsigned)a.nchunk, &a.sync[kSyncErr],
                a.wlim);
-      lo = pb >= 2u ? pb - 1u : 0u;
+      lo = pb >= 2u ? pb : 0u;
     } else {
       wait_geq(&a.sync[kSyncBin + hw], 1u, &a.sync[kSyncErr], a.wlim);
       lo = xload_u(&a.sync[kSyncBin + hw]) - 1u;
