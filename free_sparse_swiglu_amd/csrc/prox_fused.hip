@@ -40,7 +40,10 @@
 // (xstore/xload, sc1 buffer loads).  The flags of consecutive launches
 // alternate between two halves of the sync words, each launch clearing the
 // half it does not use (the select clears the histogram as soon as it has
-// read it).
+// read it).  A P4 item waits for the s of each channel it lists itself: a
+// Stage 1 item marks its tile's s as not yet computed before the tile's
+// arrival, and the P3 item's store of s is the signal (no P3 flag and no
+// wait for its stores to land).
 #include <type_traits>
 
 #include "prox_device.h"
@@ -48,8 +51,8 @@
 namespace prox {
 
 // Sync words at the start of the fused workspace block.  Each control word
-// and each P3 flag sits on its own 256-byte line (kSyncStride words), so that
-// polling one flag does not contend with the atomics on another.
+// and each tile flag sits on its own 256-byte line (kSyncStride words), so
+// that polling one flag does not contend with the atomics on another.
 //
 // Every per-launch word comes twice, as two halves: words 0 (and 1) of its
 // line for launches of parity 0, words 2 (and 3) for parity 1.  A launch
@@ -68,7 +71,7 @@ enum : int {
   kSyncErr = 4 * kSyncStride,     // sticky error bits (1: a wait timed out, 2: select fallback used)
   kSyncBin = 5 * kSyncStride,     // b* + 1 once published (0 before)
   kSyncPar = 6 * kSyncStride,     // the launch parity again (bit 31), read by the first items
-  kSyncP3 = 7 * kSyncStride       // P3 item q finished: word kSyncP3 + q * kSyncStride
+  kSyncCtl = 7 * kSyncStride      // control words end here (the tile flags follow)
 };
 static_assert(kSyncErr == kFusedErrWord, "error word index");
 
@@ -82,6 +85,7 @@ constexpr int kKC = 32;            // key slots loaded per round of a select pas
 constexpr int kP3Ch = 32;          // channels per P3 item (at most 64: one per lane of a mask)
 constexpr int kP4Ch = 512;         // channels per P4 item (kP4Ch / kP3Ch P3 items)
 constexpr int kSelBits = 16;       // buffer-load aux bit: sc1 (agent-coherent)
+constexpr unsigned kSNone = 0xffffffffu;  // s of a channel not yet computed in this launch (a NaN)
 
 struct FusedArgs {
   const uint8_t *pq;
@@ -249,10 +253,9 @@ __device__ __forceinline__ float tile_key(const float *tp, int col, int nchunk, 
 // ---------------------------------------------------------------------------
 // Share `q` of `nq` of the words of half `hw` that a launch may set (the
 // other half of the running launch: the previous launch used it and the next
-// one will): the control words, the P3 flags, the tile flags.
-constexpr int kMaxP3Items = kMaxDff / kP3Ch;
+// one will): the control words and the tile flags.
 constexpr int kMaxTiles = kMaxDff / kTile;
-constexpr int kHalfWords = 5 + kMaxP3Items + 2 * kMaxTiles;
+constexpr int kHalfWords = 5 + 2 * kMaxTiles;
 __device__ __forceinline__ void clear_half_share(const FusedArgs &a, unsigned hw, int q, int nq) {
   const int per = (kHalfWords + nq - 1) / nq;
   for (int i = threadIdx.x; i < per; i += kFT) {
@@ -262,10 +265,8 @@ __device__ __forceinline__ void clear_half_share(const FusedArgs &a, unsigned hw
     if (e < 5)
       w = &a.sync[e == 0 ? kSyncTiles : e == 1 ? kSyncSelect : e == 2 ? kSyncSelect + 1
                                       : e == 3 ? kSyncInv : kSyncBin];
-    else if (e < 5 + kMaxP3Items)
-      w = &a.sync[kSyncP3 + (e - 5) * kSyncStride];
     else
-      w = &a.tflag[((e - 5 - kMaxP3Items) >> 1) * kSyncStride + ((e - 5 - kMaxP3Items) & 1)];
+      w = &a.tflag[((e - 5) >> 1) * kSyncStride + ((e - 5) & 1)];
     xstore_u(w + hw, 0u);
   }
 }
@@ -408,6 +409,10 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
   const unsigned hw = g_fs<SEL>.hw;
   if (NORM && item == 0 && threadIdx.x == 0)
     xstore_u(&a.sync[kSyncInv + hw], __float_as_uint(g_fs<SEL>.inv));
+  // s of the tile's channels is marked not yet computed (before the tile's
+  // arrival, so before any up/gate item of the tile can store it)
+  if (chunk == 0 && threadIdx.x < kTile && t * kTile + (int)threadIdx.x < a.d_ff)
+    xstore_u((unsigned *)&a.sdense[t * kTile + threadIdx.x], kSNone);
   float *part = a.part + ((size_t)t * a.nchunk + chunk) * 512;
   {
     const int e = threadIdx.x;
@@ -983,9 +988,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
     xstore_u(&a.gmask[4 * item + 2], (unsigned)bm);
     xstore_u(&a.gmask[4 * item + 3], (unsigned)(bm >> 32));
   }
-  wait_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0) xstore_u(&a.sync[kSyncP3 + item * kSyncStride + hw], 1u);
+
 }
 
 // ---------------------------------------------------------------------------
@@ -1003,8 +1006,6 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   // (more bytes in flight behind which the dependent round trips queue)
   constexpr int U = BF16 ? 10 : 8;
   constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int QPR = kP4Ch / kP3Ch;  // P3 items per range
-  static_assert(QPR < 64, "one wave polls the range's P3 flags and the select flag");
   const int r = item / a.ncol, cc = item % a.ncol;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1082,18 +1083,24 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
             (uint32_t)lane * 4u, rowoff + (uint32_t)h * 256u, 0, kNT);
     }
   }
-  if (tid < 64) {
-    const int q0 = r * QPR, q1 = min(a.n_p3, q0 + QPR) - 1;
-    wave_wait_flags(&a.sync[kSyncP3 + min(q0 + lane, q1) * kSyncStride + hw], &a.sync[kSyncErr],
-                    a.wlim);
-    if (lane == 0) stamp_wait<SEL>(a);
-  }
-  __syncthreads();
-  // 3. s of each listed channel (final once the range's P3 items are done,
-  // the bin-b* ones included), loaded while the select may still run; then
-  // 0 for a bin-b* channel below the cut.
+  // 3. s of each listed channel, polled until its up/gate item has stored it
+  // (the bin-b* ones included), while the select may still run; then 0 for a
+  // bin-b* channel below the cut.
   {
-    const float sj = tid < nr ? xload(&a.sdense[sm.rs[tid]]) : 0.0f;
+    float sj = 0.0f;
+    if (tid < nr) {
+      const unsigned *sp = (const unsigned *)&a.sdense[sm.rs[tid]];
+      unsigned v, spins = 0;
+      while ((v = xload_u(sp)) == kSNone) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > a.wlim) {
+          atomicOr(&a.sync[kSyncErr], 1u);
+          break;
+        }
+      }
+      sj = __uint_as_float(v);
+    }
+    if (tid == 0) stamp_wait<SEL>(a);
     if (!a.ts_mode) {
       if (tid == 0)
         wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
@@ -1358,11 +1365,11 @@ bool fused_supported(const Plan &p) {
 
 static int fused_n_p3(const Plan &p) { return (p.d_ff + kP3Ch - 1) / kP3Ch; }
 
-// Sync block: control words, P3 flags, tile flags (one line each), the
-// digit-1 histogram, the P3 masks, each at a fixed word index sized for the
+// Sync block: control words, tile flags (one line each), the digit-1
+// histogram, the P3 masks, each at a fixed word index sized for the
 // largest supported d_ff (so layers of any shapes can share one block).
 constexpr size_t kMaxP3 = kMaxDff / kP3Ch;
-constexpr size_t kTflagWord = (size_t)kSyncP3 + kMaxP3 * kSyncStride;
+constexpr size_t kTflagWord = (size_t)kSyncCtl;
 constexpr size_t kHistWord = kTflagWord + (size_t)(kMaxDff / kTile) * kSyncStride;
 constexpr size_t kGmaskWord = kHistWord + 2048;
 
