@@ -413,6 +413,15 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
   // arrival, so before any up/gate item of the tile can store it)
   if (chunk == 0 && threadIdx.x < kTile && t * kTile + (int)threadIdx.x < a.d_ff)
     xstore_u((unsigned *)&a.sdense[t * kTile + threadIdx.x], kSNone);
+  // ... and so is this item's share of the down items' partial sums, long
+  // before any down item stores one
+  {
+    const int tot = a.nrange * a.d_model;
+    const int per = (tot + a.n_p1 - 1) / a.n_p1;
+    const int e1 = min(tot, item * per + per);
+    for (int e = item * per + (int)threadIdx.x; e < e1; e += kFT)
+      xstore_u((unsigned *)&a.ypart[e], kSNone);
+  }
   float *part = a.part + ((size_t)t * a.nchunk + chunk) * 512;
   {
     const int e = threadIdx.x;
@@ -1163,7 +1172,18 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
     for (int q = 1; q < kFW; ++q) v += sm.red[q][c];
     xstore(&a.ypart[(size_t)r * a.d_model + cc * kDownCols + c], v);
   }
-  if (!arrive_last(&a.col_cnt[cc], (unsigned)a.nrange, s_flag)) return;
+  // The last of the chunk's items to arrive adds the partials; it polls each
+  // one until it has landed, so no item waits for its own stores first.
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(&a.col_cnt[cc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == (unsigned)a.nrange - 1u;
+    if (last) __hip_atomic_store(&a.col_cnt[cc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  if (!*s_flag) return;
   // Sum of the range partials of the chunk: wave q adds ranges q, q + 8, ...
   // of 4 columns per lane (agent-coherent 16-byte loads), then the 8 wave
   // sums are added in wave order.
@@ -1182,6 +1202,16 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (r0 + kFW * u < a.nrange) {
+          unsigned spins = 0;
+          while (v[u].x == kSNone || v[u].y == kSNone || v[u].z == kSNone || v[u].w == kSNone) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > a.wlim) {
+              atomicOr(&a.sync[kSyncErr], 1u);
+              break;
+            }
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(yr, coff, (uint32_t)(r0 + kFW * u) * a.d_model * 4u,
+                                                         kSelBits);
+          }
           s4.x += __uint_as_float(v[u].x);
           s4.y += __uint_as_float(v[u].y);
           s4.z += __uint_as_float(v[u].z);
