@@ -278,7 +278,20 @@ template <bool BF16, bool NORM, bool SEL>
 __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm, int *s_flag,
                                         unsigned pw, bool resolve) {
   constexpr int U = 16;
-  const int chunk = item % a.nchunk, t = item / a.nchunk;
+  // Work-group b runs on XCD b % 8.  With a multiple of 8 tiles, the chunks
+  // of a tile go to one XCD: the chunks of one index then no longer all sit
+  // on one XCD, whose Stage 1 items ran 2.5 us behind the others (the tiles'
+  // codes are 1 MB apart, so one chunk index of every tile fell on the same
+  // memory interleave).
+  int t, chunk;
+  if ((a.ntile & 7) == 0) {
+    const int j = item >> 3;
+    t = 8 * (j / a.nchunk) + (item & 7);
+    chunk = j % a.nchunk;
+  } else {
+    chunk = item % a.nchunk;
+    t = item / a.nchunk;
+  }
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sl = chunk * kFW + wv;
@@ -1096,6 +1109,10 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   // (the bin-b* ones included), while the select may still run; then 0 for a
   // bin-b* channel below the cut.
   {
+    // T and J first, by the last thread: they are usually out long before the
+    // last listed s, so their round trip hides behind the polls
+    if (!a.ts_mode && tid == kFT - 1)
+      wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
     float sj = 0.0f;
     if (tid < nr) {
       const unsigned *sp = (const unsigned *)&a.sdense[sm.rs[tid]];
@@ -1110,11 +1127,7 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
       sj = __uint_as_float(v);
     }
     if (tid == 0) stamp_wait<SEL>(a);
-    if (!a.ts_mode) {
-      if (tid == 0)
-        wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
-      __syncthreads();
-    }
+    __syncthreads();
     const unsigned T = a.ts_mode ? 0u : sm.tj[0];
     const int J = a.ts_mode ? n : (int)sm.tj[1];
     if (tid < nr) {
