@@ -427,8 +427,9 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
   if (chunk == 0 && threadIdx.x < kTile && t * kTile + (int)threadIdx.x < a.d_ff)
     xstore_u((unsigned *)&a.sdense[t * kTile + threadIdx.x], kSNone);
   // ... and so is this item's share of the down items' partial sums, long
-  // before any down item stores one
-  {
+  // before any down item stores one (except in the top-k instance that
+  // normalizes its input, see the down item)
+  if constexpr (!(NORM && SEL)) {
     const int tot = a.nrange * a.d_model;
     const int per = (tot + a.n_p1 - 1) / a.n_p1;
     const int e1 = min(tot, item * per + per);
@@ -918,17 +919,15 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
     xs = sm.x;
   }
   // What to compute first.  Threshold: |s~| >= tau_s, once the item's Stage 1
-  // tile is done.  Top-k: every channel whose digit 1 is above the b* of the
-  // layer's previous call (a guess of the cut, which moves little from token
-  // to token), also as soon as the tile is done, so Stage 2 overlaps the rest
-  // of Stage 1 and the select; once b* is out, whatever the guess missed
+  // tile is done.  Top-k: every channel whose digit 1 is at least the b* of
+  // the layer's previous call (a guess of the cut, which moves little from
+  // token to token), also as soon as the tile is done, so Stage 2 overlaps the
+  // rest of Stage 1 and the select; once b* is out, whatever the guess missed
   // (digit 1 >= b*).  With no guess yet: digit 1 >= b*, after b*.  Only the
-  // timing depends on the guess, never the result.  Measured at 8B against
-  // starting from the previous b* itself: one bin lower 0.3 us slower, one
-  // bin higher (this) 0.1 us faster, since a bin the cut has left is a whole
-  // bin of rows streamed for nothing, while the bin it reaches costs only a
-  // short second pass; a start from the previous k-th key (1/16 to 1/4 of an
-  // octave below it) was slower still.
+  // timing depends on the guess, never the result.  (Measured at 8B: one bin
+  // lower 0.3 us slower; one bin higher within 0.1 us on a single layer but
+  // 0.6 us slower per layer in the 32-layer stack; a start 1/16 to 1/4 octave
+  // below the previous call's k-th key slower.)
   if (threadIdx.x == 0) {
     unsigned lo = 0u;
     const unsigned pb = a.ts_mode ? 0u : xload_u(a.pred);
@@ -938,7 +937,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
       // tile epilogue to publish them)
       wait_geq(&a.tflag[(c0 / kTile) * kSyncStride + hw + 1], (unsigned)a.nchunk, &a.sync[kSyncErr],
                a.wlim);
-      lo = pb >= 2u ? pb : 0u;
+      lo = pb >= 2u ? pb - 1u : 0u;
     } else {
       wait_geq(&a.sync[kSyncBin + hw], 1u, &a.sync[kSyncErr], a.wlim);
       lo = xload_u(&a.sync[kSyncBin + hw]) - 1u;
@@ -1021,7 +1020,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
 // may be kept (digit 1 >= b*) start loading before the range's P3 items and
 // the select are done; a bin-b* channel below the cut gets s = 0.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool SEL>
+template <bool BF16, bool NORM, bool SEL>
 __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL> &sm, int *s_flag) {
   const unsigned hw = g_fs<SEL>.hw;
   // rows per wave per batch: 10 rows x 512 B; 20 measured 0.5 us slower at 8B
@@ -1110,8 +1109,13 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   // bin-b* channel below the cut.
   {
     // T and J first, by the last thread: they are usually out long before the
-    // last listed s, so their round trip hides behind the polls
-    if (!a.ts_mode && tid == kFT - 1)
+    // last listed s, so their round trip hides behind the polls.  (In the
+    // top-k instance that normalizes its input, which is at the register
+    // budget, the T/J wait after the polls and the reduction of the partial
+    // sums behind a wait for their stores, as below, measured 1.9 us per
+    // layer faster in the 32-layer stack: the other forms spill registers on
+    // its Stage 1 path.)
+    if (!NORM && !a.ts_mode && tid == kFT - 1)
       wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
     float sj = 0.0f;
     if (tid < nr) {
@@ -1127,6 +1131,8 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
       sj = __uint_as_float(v);
     }
     if (tid == 0) stamp_wait<SEL>(a);
+    if (NORM && !a.ts_mode && tid == 0)
+      wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
     __syncthreads();
     const unsigned T = a.ts_mode ? 0u : sm.tj[0];
     const int J = a.ts_mode ? n : (int)sm.tj[1];
@@ -1186,17 +1192,22 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
     xstore(&a.ypart[(size_t)r * a.d_model + cc * kDownCols + c], v);
   }
   // The last of the chunk's items to arrive adds the partials; it polls each
-  // one until it has landed, so no item waits for its own stores first.
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add(&a.col_cnt[cc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == (unsigned)a.nrange - 1u;
-    if (last) __hip_atomic_store(&a.col_cnt[cc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last;
+  // one until it has landed, so no item waits for its own stores first
+  // (except in the normalizing top-k instance, see above).
+  if constexpr (NORM && SEL) {
+    if (!arrive_last(&a.col_cnt[cc], (unsigned)a.nrange, s_flag)) return;
+  } else {
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old =
+          __hip_atomic_fetch_add(&a.col_cnt[cc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == (unsigned)a.nrange - 1u;
+      if (last) __hip_atomic_store(&a.col_cnt[cc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_flag = last;
+    }
+    __syncthreads();
+    if (!*s_flag) return;
   }
-  __syncthreads();
-  if (!*s_flag) return;
   // Sum of the range partials of the chunk: wave q adds ranges q, q + 8, ...
   // of 4 columns per lane (agent-coherent 16-byte loads), then the 8 wave
   // sums are added in wave order.
@@ -1216,7 +1227,8 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
       for (int u = 0; u < 8; ++u) {
         if (r0 + kFW * u < a.nrange) {
           unsigned spins = 0;
-          while (v[u].x == kSNone || v[u].y == kSNone || v[u].z == kSNone || v[u].w == kSNone) {
+          while (!(NORM && SEL) &&
+                 (v[u].x == kSNone || v[u].y == kSNone || v[u].z == kSNone || v[u].w == kSNone)) {
             __builtin_amdgcn_s_sleep(1);
             if (++spins > a.wlim) {
               atomicOr(&a.sync[kSyncErr], 1u);
@@ -1320,7 +1332,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       p3_item<BF16, NORM, SEL>(a, r, sm.p3);
     } else {
       phase = 4;
-      p4_item<BF16, SEL>(a, r - a.n_p3, sm.p4, &s_flag);
+      p4_item<BF16, NORM, SEL>(a, r - a.n_p3, sm.p4, &s_flag);
     }
     if (a.trace && threadIdx.x == 0) {
       unsigned long long *e = a.trace + 4 * (size_t)t;
