@@ -219,6 +219,7 @@ struct FusedShared {
   unsigned long long twait;
   int ticket, flag;
   float inv;  // in-kernel RMSNorm: 1/rms(r) of the first Stage 1 item, until published
+  unsigned ibits;  // in-kernel RMSNorm: the published 1/rms(r), read by an up/gate item
   union {
     P1Smem p1;
     P2Smem<SEL> p2;
@@ -427,9 +428,8 @@ __device__ __forceinline__ void p1_item(const FusedArgs &a, int item, P1Smem &sm
   if (chunk == 0 && threadIdx.x < kTile && t * kTile + (int)threadIdx.x < a.d_ff)
     xstore_u((unsigned *)&a.sdense[t * kTile + threadIdx.x], kSNone);
   // ... and so is this item's share of the down items' partial sums, long
-  // before any down item stores one (except in the top-k instance that
-  // normalizes its input, see the down item)
-  if constexpr (!(NORM && SEL)) {
+  // before any down item stores one
+  {
     const int tot = a.nrange * a.d_model;
     const int per = (tot + a.n_p1 - 1) / a.n_p1;
     const int e1 = min(tot, item * per + per);
@@ -888,13 +888,18 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
 #pragma unroll
         for (int q = 0; q < EPS16; ++q) r0[q] = a.rnorm[(size_t)i0 * EPS16 + q];
       }
-      unsigned ib = xload_u(&a.sync[kSyncInv + hw]);
-      if (__syncthreads_or(ib == 0u)) {
-        if (threadIdx.x == 0) wait_geq(&a.sync[kSyncInv + hw], 1u, &a.sync[kSyncErr], a.wlim);
-        __syncthreads();
-        ib = xload_u(&a.sync[kSyncInv + hw]);
+      // read by thread 0 and shared through LDS (a work-group-wide vote
+      // would keep all three thread coordinates live through the kernel)
+      if (threadIdx.x == 0) {
+        unsigned ib = xload_u(&a.sync[kSyncInv + hw]);
+        if (ib == 0u) {
+          wait_geq(&a.sync[kSyncInv + hw], 1u, &a.sync[kSyncErr], a.wlim);
+          ib = xload_u(&a.sync[kSyncInv + hw]);
+        }
+        g_fs<SEL>.ibits = ib;
       }
-      const float inv = __uint_as_float(ib);
+      __syncthreads();
+      const float inv = __uint_as_float(g_fs<SEL>.ibits);
       auto put = [&](int i, const float *r) {
         uint32_t w[4];
 #pragma unroll
@@ -1020,7 +1025,7 @@ __device__ __forceinline__ void p3_item(const FusedArgs &a, int item, P3Smem &sm
 // may be kept (digit 1 >= b*) start loading before the range's P3 items and
 // the select are done; a bin-b* channel below the cut gets s = 0.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool NORM, bool SEL>
+template <bool BF16, bool SEL>
 __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL> &sm, int *s_flag) {
   const unsigned hw = g_fs<SEL>.hw;
   // rows per wave per batch: 10 rows x 512 B; 20 measured 0.5 us slower at 8B
@@ -1109,13 +1114,8 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
   // bin-b* channel below the cut.
   {
     // T and J first, by the last thread: they are usually out long before the
-    // last listed s, so their round trip hides behind the polls.  (In the
-    // top-k instance that normalizes its input, which is at the register
-    // budget, the T/J wait after the polls and the reduction of the partial
-    // sums behind a wait for their stores, as below, measured 1.9 us per
-    // layer faster in the 32-layer stack: the other forms spill registers on
-    // its Stage 1 path.)
-    if (!NORM && !a.ts_mode && tid == kFT - 1)
+    // last listed s, so their round trip hides behind the polls
+    if (!a.ts_mode && tid == kFT - 1)
       wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
     float sj = 0.0f;
     if (tid < nr) {
@@ -1131,8 +1131,6 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
       sj = __uint_as_float(v);
     }
     if (tid == 0) stamp_wait<SEL>(a);
-    if (NORM && !a.ts_mode && tid == 0)
-      wait_tj(&a.sync[kSyncSelect + hw], &a.sync[kSyncErr], &sm.tj[0], &sm.tj[1], a.wlim);
     __syncthreads();
     const unsigned T = a.ts_mode ? 0u : sm.tj[0];
     const int J = a.ts_mode ? n : (int)sm.tj[1];
@@ -1192,22 +1190,17 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
     xstore(&a.ypart[(size_t)r * a.d_model + cc * kDownCols + c], v);
   }
   // The last of the chunk's items to arrive adds the partials; it polls each
-  // one until it has landed, so no item waits for its own stores first
-  // (except in the normalizing top-k instance, see above).
-  if constexpr (NORM && SEL) {
-    if (!arrive_last(&a.col_cnt[cc], (unsigned)a.nrange, s_flag)) return;
-  } else {
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned old =
-          __hip_atomic_fetch_add(&a.col_cnt[cc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = old == (unsigned)a.nrange - 1u;
-      if (last) __hip_atomic_store(&a.col_cnt[cc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *s_flag = last;
-    }
-    __syncthreads();
-    if (!*s_flag) return;
+  // one until it has landed, so no item waits for its own stores first.
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(&a.col_cnt[cc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == (unsigned)a.nrange - 1u;
+    if (last) __hip_atomic_store(&a.col_cnt[cc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
   }
+  __syncthreads();
+  if (!*s_flag) return;
   // Sum of the range partials of the chunk: wave q adds ranges q, q + 8, ...
   // of 4 columns per lane (agent-coherent 16-byte loads), then the 8 wave
   // sums are added in wave order.
@@ -1227,8 +1220,7 @@ __device__ __forceinline__ void p4_item(const FusedArgs &a, int item, P4Smem<SEL
       for (int u = 0; u < 8; ++u) {
         if (r0 + kFW * u < a.nrange) {
           unsigned spins = 0;
-          while (!(NORM && SEL) &&
-                 (v[u].x == kSNone || v[u].y == kSNone || v[u].z == kSNone || v[u].w == kSNone)) {
+          while (v[u].x == kSNone || v[u].y == kSNone || v[u].z == kSNone || v[u].w == kSNone) {
             __builtin_amdgcn_s_sleep(1);
             if (++spins > a.wlim) {
               atomicOr(&a.sync[kSyncErr], 1u);
@@ -1332,7 +1324,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       p3_item<BF16, NORM, SEL>(a, r, sm.p3);
     } else {
       phase = 4;
-      p4_item<BF16, NORM, SEL>(a, r - a.n_p3, sm.p4, &s_flag);
+      p4_item<BF16, SEL>(a, r - a.n_p3, sm.p4, &s_flag);
     }
     if (a.trace && threadIdx.x == 0) {
       unsigned long long *e = a.trace + 4 * (size_t)t;
