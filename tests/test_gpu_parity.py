@@ -820,6 +820,11 @@ def test_layers_of_different_shapes_share_a_workspace():
     assert Lb.workspace.data_ptr() == La.workspace.data_ptr()
     Ra = prox.prox_prepare_layer(*Wa, RAGGED.group, 8)
     Rb = prox.prox_prepare_layer(*Wb, cfg_b.group, 1)
+    # a multi-kernel layer on the same workspace: its kernels write the s and
+    # partial-sum buffers that the persistent kernel marks and polls
+    Lc = prox.prox_prepare_layer(*Wb, cfg_b.group, 1, workspace=La.workspace,
+                                 path=prox.PROX_PATH_MULTI)
+    Rc = prox.prox_prepare_layer(*Wb, cfg_b.group, 1, path=prox.PROX_PATH_MULTI)
     xa = synth.make_inputs(RAGGED, 3, "share", 0, "cpu").to(DEV)
     xb = synth.make_inputs(cfg_b, 3, "share", 0, "cpu").to(DEV)
     ka, kb = synth.k_for(RAGGED.d_ff, 0.7), synth.k_for(cfg_b.d_ff, 0.7)
@@ -827,13 +832,21 @@ def test_layers_of_different_shapes_share_a_workspace():
         ya = prox.prox_ffn_forward(La, xa[t], 0.5, ka)
         yab = prox.prox_ffn_forward_batch(La, xa, 0.5, ka)
         yb = prox.prox_ffn_forward(Lb, xb[t], 0.5, kb)
+        yc = prox.prox_ffn_forward(Lc, xb[t], 0.5, kb)
+        yd = prox.prox_dense_ffn_forward(La, xa[t])
+        ya2 = prox.prox_ffn_forward(La, xa[t], 0.5, ka)
         ra = prox.prox_ffn_forward(Ra, xa[t], 0.5, ka)
         rab = prox.prox_ffn_forward_batch(Ra, xa, 0.5, ka)
         rb = prox.prox_ffn_forward(Rb, xb[t], 0.5, kb)
+        rc = prox.prox_ffn_forward(Rc, xb[t], 0.5, kb)
+        rd = prox.prox_dense_ffn_forward(Ra, xa[t])
         torch.cuda.synchronize()
         assert torch.equal(ya.view(torch.int16), ra.view(torch.int16))
+        assert torch.equal(ya2.view(torch.int16), ra.view(torch.int16))
         assert torch.equal(yab.view(torch.int16), rab.view(torch.int16))
         assert torch.equal(yb.view(torch.int16), rb.view(torch.int16))
+        assert torch.equal(yc.view(torch.int16), rc.view(torch.int16))
+        assert torch.equal(yd.view(torch.int16), rd.view(torch.int16))
     st = prox.prox_read_status(La)
     torch.cuda.synchronize()
     assert int(st[0]) & 1 == 0
