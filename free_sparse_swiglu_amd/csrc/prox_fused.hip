@@ -44,6 +44,7 @@
 // Stage 1 item marks its tile's s as not yet computed before the tile's
 // arrival, and the P3 item's store of s is the signal (no P3 flag and no
 // wait for its stores to land).
+#include <atomic>
 #include <type_traits>
 
 #include "prox_device.h"
@@ -1388,17 +1389,24 @@ __global__ __launch_bounds__(kFT) void fused_list_kernel(const unsigned *gmask, 
 template <bool BF16, bool NORM, bool SEL>
 static hipError_t fused_go(FusedArgs &a, hipStream_t s) {
   auto fn = ffn_fused_kernel<BF16, NORM, SEL>;
-  static int cap = 0;
+  // Work-groups the current device holds at once for this instance, queried
+  // once per device (per instance) and kept; threads that race on the first
+  // query store the same value.
+  constexpr int kDevCache = 64;
+  static std::atomic<int> caps[kDevCache];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int cap = dev < kDevCache ? caps[dev].load(std::memory_order_relaxed) : 0;
   if (!cap) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, kFT, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     cap = per_cu * cus;
+    if (dev < kDevCache) caps[dev].store(cap, std::memory_order_relaxed);
   }
   const int total = a.n_p1 + a.n_p2 + a.n_p3 + a.n_p4;
   const int grid = total < cap ? total : cap;
