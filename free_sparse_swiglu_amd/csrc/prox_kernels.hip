@@ -178,6 +178,11 @@ __global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a)
     for (int c = 0; c < 8; ++c) acc[b][c] = 0.0f;
 
   if (sl < nsl) {
+    // the slice's group scales first, so that their latency hides behind
+    // the mask and the code stream instead of following it
+    const int g = (sl * 64) / a.G;
+    const float4 *sp = (const float4 *)(a.psc + ((size_t)t * a.ngroups + g) * 512 + (size_t)lane * 8);
+    const float4 s0 = sp[0], s1 = sp[1];
     // Input mask of the slice's rows (Sec. 4.1, m_x), compacted in LDS: the
     // union over tokens decides which rows are read; each token keeps its
     // own x or 0.
@@ -307,9 +312,6 @@ __global__ __launch_bounds__(512, NB > 4 ? 2 : 1) void proxy_kernel(ProxyArgs a)
     }
     // Group scale and code offset: contribution = scale * (acc - off * sum x).
     const float off = BF16 ? 136.0f : 8.0f;
-    const int g = (sl * 64) / a.G;
-    const float4 *sp = (const float4 *)(a.psc + ((size_t)t * a.ngroups + g) * 512 + (size_t)lane * 8);
-    const float4 s0 = sp[0], s1 = sp[1];
     const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
     for (int b = 0; b < NB; ++b)
