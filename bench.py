@@ -732,6 +732,38 @@ def bench_copy(args):
                 GBps=round(2 * n / (ms * 1e-3) / 1e9, 1))
 
 
+def other_workloads(args):
+    """Short runs of the 70B-shaped batch step (1/2/4/8 tokens, 4-layer ring,
+    50 timed steps per point) and of the 32-layer 8B-shaped stack, summarised
+    beside the 8B line so that one default run reports every workload."""
+    import copy
+    import gc
+
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+    a = copy.copy(args)
+    a.steps, a.warmup, a.ring = 50, 5, 4
+    b = bench_batch(a)
+    batch = {k: dict(us_per_step=v["us_per_step"], dense_us=v["dense_us"],
+                     speedup_vs_dense=v["speedup_vs_dense"], union_frac=v["union_frac"])
+             for k, v in b["batches"].items()}
+    gc.collect()
+    torch.cuda.empty_cache()
+    st = bench_stack(args)
+    tm = st["threshold_mode"]
+    stack = dict(tokens_per_s=st["value"], us_per_layer=st["us_per_layer"],
+                 dense_tokens_per_s=st["dense_tokens_per_s"],
+                 speedup_vs_dense=st["speedup_vs_dense"], graph_tokens_per_s=st["graph_tokens_per_s"],
+                 threshold_mask=dict(tokens_per_s=tm["tokens_per_s"], target_e=tm["target_e"],
+                                     speedup_vs_dense=tm["speedup_vs_dense"]),
+                 threshold_artifact=st["threshold_artifact"])
+    gc.collect()
+    torch.cuda.empty_cache()
+    return {"70b_batch": dict(steps=a.steps, ring_layers=a.ring, k=b["config"]["k"], batches=batch),
+            "stack8b": stack}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -745,6 +777,9 @@ def main():
     ap.add_argument("--ring", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="8b only: skip the 70B batch and 32-layer stack summaries appended "
+                         "to the line")
     ap.add_argument("--dump", default=None,
                     help="timeline workload: save the last call's raw trace (.npy) here")
     ap.add_argument("--batch-gemv", choices=["valu", "mfma"], default="valu",
@@ -761,6 +796,8 @@ def main():
         sys.exit(1)
     if args.workload in ("8b", "14b"):
         res = bench_single_layer(args, args.workload)
+        if args.workload == "8b" and not args.no_other_workloads:
+            res["other_workloads"] = other_workloads(args)
     elif args.workload == "70b":
         res = bench_batch(args)
     elif args.workload == "stack8b":
