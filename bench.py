@@ -734,7 +734,8 @@ def bench_copy(args):
 
 def other_workloads(args):
     """Short runs of the 70B-shaped batch step (1/2/4/8 tokens, 4-layer ring,
-    50 timed steps per point) and of the 32-layer 8B-shaped stack, summarised
+    50 timed steps per point), of the 32-layer 8B-shaped stack and of the
+    14B-shaped layer (100 timed steps, no CPU leg), summarised
     beside the 8B line so that one default run reports every workload."""
     import copy
     import gc
@@ -760,7 +761,15 @@ def other_workloads(args):
                  threshold_artifact=st["threshold_artifact"])
     gc.collect()
     torch.cuda.empty_cache()
-    return {"70b_batch": dict(steps=a.steps, ring_layers=a.ring, k=b["config"]["k"], batches=batch),
+    a = copy.copy(args)
+    a.steps, a.warmup, a.no_cpu_baseline = 100, 10, True
+    r = bench_single_layer(a, "14b")
+    l14 = dict(steps=a.steps, us_per_layer=r["us_per_layer"], k=r["config"]["k"],
+               hbm_frac=r["roofline"]["frac"], dense_us=r["dense"]["us_per_layer"],
+               speedup_vs_dense=r["speedup_vs_dense"])
+    gc.collect()
+    torch.cuda.empty_cache()
+    return {"14b": l14, "70b_batch": dict(steps=a.steps, ring_layers=a.ring, k=b["config"]["k"], batches=batch),
             "stack8b": stack}
 
 
