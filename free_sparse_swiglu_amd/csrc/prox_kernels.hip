@@ -729,9 +729,10 @@ template <int PER>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff, int k,
                                                     int *sel, unsigned *selw, unsigned *ucnt,
                                                     int *uni, int *nuni, uint8_t *umask) {
-  // digit 1 in 4 copies (waves w and w + 4 share one), so that keys of the
-  // few crowded bins queue on 4 addresses instead of 1
-  __shared__ unsigned h1[4][2048];
+  // digit 1 in 4 copies, picked by lane % 4 and interleaved (a bin's copies
+  // are 4 consecutive words, in 4 banks): the lanes of one wave whose keys
+  // fall in the same crowded bin then queue on 4 addresses instead of 1
+  __shared__ __attribute__((aligned(16))) unsigned h1[2048][4];
   __shared__ unsigned h2[2048];
   __shared__ unsigned h3[512];
   __shared__ unsigned cnt[PER * 16];
@@ -754,11 +755,8 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
     const int j = e * 1024 + tid;
     key[e] = (j < d_ff) ? __float_as_uint(z[j]) : 0u;
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    h1[c][tid] = 0u;
-    h1[c][tid + 1024] = 0u;
-  }
+  *(uint4 *)h1[tid] = make_uint4(0u, 0u, 0u, 0u);
+  *(uint4 *)h1[tid + 1024] = make_uint4(0u, 0u, 0u, 0u);
   h2[tid] = 0u; h2[tid + 1024] = 0u;
   if (tid < 512) h3[tid] = 0u;
   __syncthreads();
@@ -766,9 +764,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *sabs, int d_ff,
   // Digit 1: bits 30..20.
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    if (e * 1024 + tid < d_ff) atomicAdd(&h1[w & 3][key[e] >> 20], 1u);
+    if (e * 1024 + tid < d_ff) atomicAdd(&h1[key[e] >> 20][lane & 3], 1u);
   __syncthreads();
-  pick_bin<2048>([&](int i) { return h1[0][i] + h1[1][i] + h1[2][i] + h1[3][i]; }, (unsigned)k,
+  pick_bin<2048>([&](int i) { return h1[i][0] + h1[i][1] + h1[i][2] + h1[i][3]; }, (unsigned)k,
                  wsum, &s_bin, &s_kk);
   __syncthreads();
   const unsigned b1 = s_bin;
